@@ -1,0 +1,523 @@
+/*
+ * oracle.c -- plain, slow CPU reference of the quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The product (libqlinear
+ * and its Python binding) never calls it, and the two share no source: this
+ * file includes no project header and defines its own half-precision codec.
+ *
+ * What it computes, step by step, and where each step comes from:
+ *
+ *   W4A16 (AWQ-style weight-only int4), LMDeploy walkthrough, section 2
+ *   ("quantization is not trading precision for speed"): per-group scales
+ *   along the input dimension, an asymmetric zero point from each group's
+ *   min/max, 4-bit codes; AUQ dual-process page, sections 3.3 and 5.4: the
+ *   qweight / scales / zeros tensors and the "int4 times scale, zero point"
+ *   dequantisation.
+ *     1. lo = min(0, min w), hi = max(0, max w) over a group of G weights.
+ *     2. s = fp16 rounded toward +inf of max((hi - lo) / 15, 2^-14).
+ *     3. z = clamp(rint(-lo / s), 0, 15).
+ *     4. q = clamp(rint(w / s) + z, 0, 15).
+ *     5. 8 codes per 32-bit word, code i in bits [4i, 4i+4), along K.
+ *     6. unpack = the inverse of 5.
+ *     7. wd = (q - z) * s (exact in fp32); wd16 = its fp16 rounding.
+ *     8. y[m,n] = sum_k x[m,k] * wd16[n,k], fp64 accumulator, k ascending.
+ *   The symmetric per-tensor example of the same section (scale = max|w| /
+ *   7.5, codes clamped to [-7, 7]) is implemented as or_sym_int4.
+ *
+ *   W8A8 (SmoothQuant), LMDeploy W8A8 guide, "step 2: weight smoothing" and
+ *   "inference kernels: QRMSNorm and QLinear":
+ *     1. a_j = max_m |X[m,j]|, b_j = max_n |W[n,j]|,
+ *        s_j = a_j^0.5 / b_j^0.5 (alpha = 0.5); s_j = 1 where a_j, b_j or
+ *        gamma_j is zero.
+ *     2. gamma'_j = fp16(gamma_j / s_j); W'[n,j] = W[n,j] * s_j.
+ *     3. per output channel: w_scale = max_j |W'| / 127,
+ *        wq = clamp(rint(W' / w_scale), -127, 127).
+ *     4. per token: RMSNorm y = x * (1/sqrt(mean(x^2) + eps)) * gamma' in
+ *        fp32, x_scale = max|y| / 127, xq = clamp(rint(y / x_scale), -127, 127).
+ *        mean(x^2) is the exact mean rounded once to fp32.
+ *     5. acc = sum_j xq * wq in exact integer arithmetic.
+ *     6. y = acc * x_scale * w_scale (fp64).
+ *
+ * Rounding: rintf under the default environment (nearest, ties to even).
+ * Built with -ffp-contract=off so every fp32 operation rounds on its own.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_BAD -1
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary16, from the format's definition                           */
+/* ------------------------------------------------------------------------ */
+
+/* binary16 bits -> value.  sign | 5-bit biased exponent | 10-bit fraction. */
+float or_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+    float v;
+    if (e == 0)
+        v = ldexpf((float)f, -24);                 /* subnormal: f * 2^-24 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexpf((float)(f | 0x400), e - 25);    /* 1.f * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* value -> binary16 bits, rounding to nearest, ties to even. */
+uint16_t or_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    float a = fabsf(x);
+    if (isnan(x))
+        return 0x7e00;
+    if (a >= 65520.0f)              /* halfway above 65504 and beyond: overflow */
+        return sign | 0x7c00;
+    if (a < ldexpf(1.0f, -14)) {    /* subnormal range: quantum 2^-24 */
+        float m = rintf(ldexpf(a, 24));
+        return sign | (uint16_t)m;  /* m == 1024 encodes the smallest normal */
+    }
+    int e2;
+    frexpf(a, &e2);                 /* a = f * 2^e2, f in [0.5, 1) */
+    int ex = e2 - 1;                /* a in [2^ex, 2^(ex+1)) */
+    float m = rintf(ldexpf(a, 10 - ex));   /* significand in [1024, 2048] */
+    if (m == 2048.0f) {
+        m = 1024.0f;
+        ex += 1;
+    }
+    if (ex + 15 >= 31)
+        return sign | 0x7c00;
+    return sign | (uint16_t)(((ex + 15) << 10) | ((int)m - 1024));
+}
+
+/* smallest binary16 value >= x, for finite x >= 2^-14 */
+uint16_t or_f32_to_f16_up(float x)
+{
+    uint16_t h = or_f32_to_f16(x);
+    if (or_f16_to_f32(h) < x)
+        h = (uint16_t)(h + 1);      /* next representable value up (x > 0) */
+    return h;
+}
+
+/* element-wise forms of the three conversions above, for arrays */
+void or_f16_to_f32_n(const uint16_t* h, int64_t count, float* out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = or_f16_to_f32(h[i]);
+}
+
+void or_f32_to_f16_n(const float* x, int64_t count, int round_up, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = round_up ? or_f32_to_f16_up(x[i]) : or_f32_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* W4A16: group-wise asymmetric uint4                                        */
+/* ------------------------------------------------------------------------ */
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/*
+ * Steps 1-4.  w: float32 [n, k] row-major.  Outputs q uint8 [n, k] (codes),
+ * z uint8 [n, k/G] (zero points), s uint16 [n, k/G] (fp16 scale bits).
+ */
+int or_awq_quantize(const float* w, int64_t n, int64_t k, int G,
+                    uint8_t* q, uint8_t* z, uint16_t* s)
+{
+    if (G <= 0 || k % G)
+        return OR_BAD;
+    const int64_t ng = k / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const float* wg = w + r * k + g * G;
+            float lo = 0.0f, hi = 0.0f;
+            for (int i = 0; i < G; ++i) {
+                if (wg[i] < lo) lo = wg[i];
+                if (wg[i] > hi) hi = wg[i];
+            }
+            float step = (hi - lo) / 15.0f;
+            float floor_s = ldexpf(1.0f, -14);
+            if (step < floor_s)
+                step = floor_s;
+            uint16_t sb = or_f32_to_f16_up(step);
+            float sv = or_f16_to_f32(sb);
+            int zp = clampi((int)rintf(-lo / sv), 0, 15);
+            s[r * ng + g] = sb;
+            z[r * ng + g] = (uint8_t)zp;
+            for (int i = 0; i < G; ++i)
+                q[r * k + g * G + i] = (uint8_t)clampi((int)rintf(wg[i] / sv) + zp, 0, 15);
+        }
+    }
+    return OR_OK;
+}
+
+/* Step 5.  qweight uint32 [n, k/8]; qzeros uint32 [n, ceil((k/G)/8)], pad 0. */
+int or_awq_pack(const uint8_t* q, const uint8_t* z, int64_t n, int64_t k, int G,
+                uint32_t* qweight, uint32_t* qzeros)
+{
+    if (k % 8 || G <= 0 || k % G)
+        return OR_BAD;
+    const int64_t ng = k / G, zw = (ng + 7) / 8;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t j = 0; j < k / 8; ++j) {
+            uint32_t word = 0;
+            for (int i = 0; i < 8; ++i)
+                word |= (uint32_t)(q[r * k + 8 * j + i] & 0xF) << (4 * i);
+            qweight[r * (k / 8) + j] = word;
+        }
+        for (int64_t v = 0; v < zw; ++v) {
+            uint32_t word = 0;
+            for (int i = 0; i < 8; ++i) {
+                int64_t g = 8 * v + i;
+                if (g < ng)
+                    word |= (uint32_t)(z[r * ng + g] & 0xF) << (4 * i);
+            }
+            qzeros[r * zw + v] = word;
+        }
+    }
+    return OR_OK;
+}
+
+/* Step 6. */
+int or_awq_unpack(const uint32_t* qweight, const uint32_t* qzeros, int64_t n, int64_t k, int G,
+                  uint8_t* q, uint8_t* z)
+{
+    if (k % 8 || G <= 0 || k % G)
+        return OR_BAD;
+    const int64_t ng = k / G, zw = (ng + 7) / 8;
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < k; ++c)
+            q[r * k + c] = (uint8_t)((qweight[r * (k / 8) + c / 8] >> (4 * (c % 8))) & 0xF);
+        for (int64_t g = 0; g < ng; ++g)
+            z[r * ng + g] = (uint8_t)((qzeros[r * zw + g / 8] >> (4 * (g % 8))) & 0xF);
+    }
+    return OR_OK;
+}
+
+/* Step 7.  wd float32 [n, k] (nullable), wd16 fp16 bits [n, k] (nullable). */
+int or_awq_dequant(const uint8_t* q, const uint8_t* z, const uint16_t* s,
+                   int64_t n, int64_t k, int G, float* wd, uint16_t* wd16)
+{
+    if (G <= 0 || k % G)
+        return OR_BAD;
+    const int64_t ng = k / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < k; ++c) {
+            int64_t g = c / G;
+            float v = (float)((int)q[r * k + c] - (int)z[r * ng + g]) * or_f16_to_f32(s[r * ng + g]);
+            if (wd)
+                wd[r * k + c] = v;
+            if (wd16)
+                wd16[r * k + c] = or_f32_to_f16(v);
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Step 8.  x fp16 [m, k]; wd16 fp16 [n, k].  y float64 [m, nrows] for the
+ * output channels listed in rows (all n channels when rows is NULL).
+ */
+int or_w4a16_matmul(const uint16_t* x, int64_t m, const uint16_t* wd16, int64_t n, int64_t k,
+                    const int64_t* rows, int64_t nrows, double* y)
+{
+    if (!rows)
+        nrows = n;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < nrows; ++j) {
+        int64_t r = rows ? rows[j] : j;
+        if (r < 0 || r >= n)
+            continue;
+        for (int64_t i = 0; i < m; ++i) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < k; ++c)
+                acc += (double)or_f16_to_f32(x[i * k + c]) * (double)or_f16_to_f32(wd16[r * k + c]);
+            y[i * nrows + j] = acc;
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Steps 6-8 from the packed tensors for a subset of output channels: unpack,
+ * dequantise and contract one channel at a time.
+ */
+int or_w4a16_forward(const uint16_t* x, int64_t m, const uint32_t* qweight, const uint16_t* scales,
+                     const uint32_t* qzeros, int64_t n, int64_t k, int G,
+                     const int64_t* rows, int64_t nrows, double* y)
+{
+    if (k % 8 || G <= 0 || k % G)
+        return OR_BAD;
+    if (!rows)
+        nrows = n;
+    const int64_t ng = k / G, zw = (ng + 7) / 8;
+    int bad = 0;
+#pragma omp parallel
+    {
+        uint8_t* q = (uint8_t*)malloc((size_t)k);
+        uint8_t* z = (uint8_t*)malloc((size_t)ng);
+        uint16_t* w16 = (uint16_t*)malloc((size_t)k * 2);
+        if (!q || !z || !w16) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t j = 0; j < nrows; ++j) {
+                int64_t r = rows ? rows[j] : j;
+                if (r < 0 || r >= n)
+                    continue;
+                or_awq_unpack(qweight + r * (k / 8), qzeros + r * zw, 1, k, G, q, z);
+                or_awq_dequant(q, z, scales + r * ng, 1, k, G, NULL, w16);
+                for (int64_t i = 0; i < m; ++i) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < k; ++c)
+                        acc += (double)or_f16_to_f32(x[i * k + c]) * (double)or_f16_to_f32(w16[c]);
+                    y[i * nrows + j] = acc;
+                }
+            }
+        }
+        free(q);
+        free(z);
+        free(w16);
+    }
+    return bad ? OR_BAD : OR_OK;
+}
+
+/* Symmetric per-tensor int4 of the worked example: scale = max|w| / 7.5. */
+int or_sym_int4(const float* w, int64_t count, float* scale_out, int8_t* q)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < count; ++i)
+        if (fabsf(w[i]) > amax)
+            amax = fabsf(w[i]);
+    float scale = amax / 7.5f;
+    *scale_out = scale;
+    if (q)
+        for (int64_t i = 0; i < count; ++i)
+            q[i] = (int8_t)(scale > 0.0f ? clampi((int)rintf(w[i] / scale), -7, 7) : 0);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A8: SmoothQuant smoothing, int8 weights, QRMSNorm, integer GEMM          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Steps 1-2.  x fp16 [rows, k] (calibration activations), gamma fp16 [k],
+ * w float32 [n, k].  Outputs s float32 [k], gamma_s fp16 [k], w_s float32 [n, k].
+ */
+int or_smooth(const uint16_t* x, int64_t rows, const uint16_t* gamma, const float* w,
+              int64_t n, int64_t k, float* s, uint16_t* gamma_s, float* w_s)
+{
+    for (int64_t j = 0; j < k; ++j) {
+        float a = 0.0f, b = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            float v = fabsf(or_f16_to_f32(x[r * k + j]));
+            if (v > a) a = v;
+        }
+        for (int64_t r = 0; r < n; ++r) {
+            float v = fabsf(w[r * k + j]);
+            if (v > b) b = v;
+        }
+        float g = or_f16_to_f32(gamma[j]);
+        float sj = (a == 0.0f || b == 0.0f || g == 0.0f) ? 1.0f : sqrtf(a) / sqrtf(b);
+        s[j] = sj;
+        gamma_s[j] = or_f32_to_f16(g / sj);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t j = 0; j < k; ++j)
+            w_s[r * k + j] = w[r * k + j] * s[j];
+    return OR_OK;
+}
+
+/* Step 3.  wq int8 [n, k], w_scale float32 [n]. */
+int or_w8_quant_weight(const float* w, int64_t n, int64_t k, int8_t* wq, float* w_scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j)
+            if (fabsf(w[r * k + j]) > amax)
+                amax = fabsf(w[r * k + j]);
+        float sc = amax / 127.0f;
+        w_scale[r] = sc;
+        for (int64_t j = 0; j < k; ++j)
+            wq[r * k + j] = (int8_t)(sc > 0.0f ? clampi((int)rintf(w[r * k + j] / sc), -127, 127) : 0);
+    }
+    return OR_OK;
+}
+
+/*
+ * Exact sum of squares of fp16 values as an unsigned 128-bit integer in units
+ * of 2^-48.  An fp16 value is an integer significand times 2^(e-25); its
+ * square is significand^2 * 2^(2e-50) = (significand^2 << (2e-2)) * 2^-48.
+ */
+static unsigned __int128 sumsq_exact(const uint16_t* x, int64_t k)
+{
+    unsigned __int128 acc = 0;
+    for (int64_t j = 0; j < k; ++j) {
+        uint16_t h = x[j];
+        int e = (h >> 10) & 0x1f;
+        uint64_t sig = h & 0x3ff;
+        if (e == 0)
+            e = 1;
+        else
+            sig |= 0x400;
+        acc += (unsigned __int128)(sig * sig) << (2 * e - 2);
+    }
+    return acc;
+}
+
+static int bitlen128(unsigned __int128 v)
+{
+    int b = 0;
+    while (v) {
+        v >>= 1;
+        ++b;
+    }
+    return b;
+}
+
+/*
+ * num / den * 2^e2 rounded to the nearest fp32 (ties to even).  The result
+ * must lie in the normal fp32 range (true for the mean of squares below).
+ */
+float or_ratio_to_f32(unsigned __int128 num, uint64_t den, int e2)
+{
+    if (num == 0)
+        return 0.0f;
+    /* choose t so that q = floor(num * 2^t / den) has exactly 25 bits */
+    int t = 25 - (bitlen128(num) - bitlen128(den));
+    unsigned __int128 qv, rv;
+    for (;;) {
+        unsigned __int128 a = t >= 0 ? num << t : num;
+        unsigned __int128 b = t >= 0 ? (unsigned __int128)den : (unsigned __int128)den << (-t);
+        qv = a / b;
+        rv = a % b;
+        int bl = bitlen128(qv);
+        if (bl == 25)
+            break;
+        t += (bl < 25) ? 1 : -1;
+    }
+    uint32_t mant = (uint32_t)(qv >> 1);        /* 24 significant bits */
+    int rbit = (int)(qv & 1);
+    int sticky = rv != 0;
+    if (rbit && (sticky || (mant & 1)))
+        ++mant;                                 /* 2^24 after a carry is still exact */
+    return ldexpf((float)mant, e2 - t + 1);
+}
+
+/*
+ * Step 4 for m tokens.  x fp16 [m, k], gamma fp16 [k] (already smoothed).
+ * xq int8 [m, k], x_scale float32 [m], ms_out float32 [m] (nullable: the
+ * rounded mean of squares, exposed for the pins).
+ */
+int or_quant_rmsnorm(const uint16_t* x, int64_t m, int64_t k, const uint16_t* gamma, float eps,
+                     int8_t* xq, float* x_scale, float* ms_out)
+{
+    if (k <= 0)
+        return OR_BAD;
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc((size_t)k * sizeof(float));
+        if (!y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; ++i) {
+                const uint16_t* xr = x + i * k;
+                float ms = or_ratio_to_f32(sumsq_exact(xr, k), (uint64_t)k, -48);
+                float r = 1.0f / sqrtf(ms + eps);
+                float amax = 0.0f;
+                for (int64_t j = 0; j < k; ++j) {
+                    float t = or_f16_to_f32(xr[j]) * r;
+                    y[j] = t * or_f16_to_f32(gamma[j]);
+                    if (fabsf(y[j]) > amax)
+                        amax = fabsf(y[j]);
+                }
+                float sc = amax / 127.0f;
+                x_scale[i] = sc;
+                if (ms_out)
+                    ms_out[i] = ms;
+                for (int64_t j = 0; j < k; ++j)
+                    xq[i * k + j] = (int8_t)(sc > 0.0f ? clampi((int)rintf(y[j] / sc), -127, 127) : 0);
+            }
+        }
+        free(y);
+    }
+    return bad ? OR_BAD : OR_OK;
+}
+
+/*
+ * Step 5 on a sub-grid: acc int64 [nr, nc] for rows[] x cols[] (all when NULL).
+ */
+int or_int8_gemm(const int8_t* xq, int64_t m, const int8_t* wq, int64_t n, int64_t k,
+                 const int64_t* rows, int64_t nr, const int64_t* cols, int64_t nc, int64_t* acc)
+{
+    if (!rows)
+        nr = m;
+    if (!cols)
+        nc = n;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t a = 0; a < nr; ++a) {
+        int64_t i = rows ? rows[a] : a;
+        for (int64_t b = 0; b < nc; ++b) {
+            int64_t j = cols ? cols[b] : b;
+            int64_t s = 0;
+            if (i >= 0 && i < m && j >= 0 && j < n)
+                for (int64_t c = 0; c < k; ++c)
+                    s += (int64_t)xq[i * k + c] * (int64_t)wq[j * k + c];
+            acc[a * nc + b] = s;
+        }
+    }
+    return OR_OK;
+}
+
+/* Steps 5-6 on a sub-grid: y float64 [nr, nc]. */
+int or_w8a8_forward(const int8_t* xq, const float* x_scale, int64_t m, const int8_t* wq,
+                    const float* w_scale, int64_t n, int64_t k,
+                    const int64_t* rows, int64_t nr, const int64_t* cols, int64_t nc, double* y)
+{
+    if (!rows)
+        nr = m;
+    if (!cols)
+        nc = n;
+    int64_t* acc = (int64_t*)malloc((size_t)(nr * nc) * sizeof(int64_t));
+    if (!acc)
+        return OR_BAD;
+    or_int8_gemm(xq, m, wq, n, k, rows, nr, cols, nc, acc);
+    for (int64_t a = 0; a < nr; ++a) {
+        int64_t i = rows ? rows[a] : a;
+        for (int64_t b = 0; b < nc; ++b) {
+            int64_t j = cols ? cols[b] : b;
+            y[a * nc + b] = (double)acc[a * nc + b] * (double)x_scale[i] * (double)w_scale[j];
+        }
+    }
+    free(acc);
+    return OR_OK;
+}
+
+/* Exposed for the pins: exact sum of squares as (hi, lo) 64-bit halves. */
+void or_sumsq_exact(const uint16_t* x, int64_t k, uint64_t* hi, uint64_t* lo)
+{
+    unsigned __int128 v = sumsq_exact(x, k);
+    *hi = (uint64_t)(v >> 64);
+    *lo = (uint64_t)v;
+}
+
+/* Exposed for the pins: or_ratio_to_f32 with a 128-bit numerator in halves. */
+float or_ratio_to_f32_parts(uint64_t num_hi, uint64_t num_lo, uint64_t den, int e2)
+{
+    unsigned __int128 num = ((unsigned __int128)num_hi << 64) | num_lo;
+    return or_ratio_to_f32(num, den, e2);
+}
