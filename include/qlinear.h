@@ -1,0 +1,222 @@
+/*
+ * qlinear.h -- C ABI of libqlinear, the quantized linear layer for MI355X
+ * (gfx950 / CDNA4).
+ *
+ * Two paths of LLM inference:
+ *
+ *   W4A16 (AWQ-style weight-only int4).  LMDeploy engineering walkthrough
+ *   (zwxr.cn/news/301173), section 2: weights quantised per group along the
+ *   input dimension with their own scale, an asymmetric zero point from each
+ *   group's min/max, group sizes 32/64/128 (CLI default 128); AUQ dual-process
+ *   page (bjbfmj.com/news/39067), sections 3.3 and 5.4: the tensors qweight,
+ *   scales, zeros and the dequantisation "int4 times scale with zero point".
+ *
+ *   W8A8 (SmoothQuant).  LMDeploy W8A8 guide (m.nxbn.cn/news/126471),
+ *   "step 2: weight smoothing" (alpha = 0.5, norm weight divided by s, linear
+ *   weight multiplied by s along its input dimension) and "inference kernels:
+ *   QRMSNorm and QLinear" (RMSNorm fused with per-token dynamic int8
+ *   quantisation; per-channel int8 weights with an fp32 scale; 8-bit GEMM with
+ *   an int32 accumulator; output = acc * rms_scale * linear_scale in fp16).
+ *
+ * Conventions for every entry point
+ *   - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
+ *   - All matrices are dense row-major.  x is [m, k]; weights are [n, k]
+ *     (n output channels, k input channels: the torch Linear layout); y is
+ *     [m, n].
+ *   - "host" pointers are ordinary CPU memory; the call is synchronous.
+ *     "device" pointers are HIP device memory of the current device; the call
+ *     only enqueues work on `stream` (a hipStream_t, NULL = the null stream)
+ *     and returns without synchronising.  Execution faults surface at the
+ *     caller's next synchronisation.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     memory and keeps no state between calls, except a thread-local error
+ *     message.
+ *   - Return value: QL_OK (0) or a negative QL_ERR_* code.  On any error
+ *     nothing is launched and no output is written; ql_last_error() gives a
+ *     human-readable reason on the calling thread.
+ *   - m == 0 or n == 0 is an empty problem: QL_OK, nothing launched.
+ *     Negative sizes are QL_ERR_SHAPE.
+ *   - Device pointers must be 16-byte aligned (128-bit loads and stores), or
+ *     QL_ERR_ALIGN.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QL_OK 0
+#define QL_ERR_NULL (-1)        /* a required pointer is NULL */
+#define QL_ERR_SHAPE (-2)       /* negative size, k not a multiple of 8 or of group, ... */
+#define QL_ERR_GROUP (-3)       /* group not in {32, 64, 128} */
+#define QL_ERR_ALIGN (-4)       /* device pointer not 16-byte aligned */
+#define QL_ERR_WORKSPACE (-5)   /* workspace missing or smaller than required */
+#define QL_ERR_UNSUPPORTED (-6) /* shape or path the kernels do not cover */
+#define QL_ERR_VALUE (-7)       /* non-finite input, or a scale outside fp16 range */
+#define QL_ERR_HIP (-8)         /* a HIP runtime call or launch failed */
+
+/* W4A16 kernel selection for ql_w4a16_gemm_path */
+#define QL_PATH_AUTO 0          /* by m: decode path for m <= 32, MFMA GEMM above */
+#define QL_PATH_DECODE 1        /* split-K GEMV path, m <= 32 */
+#define QL_PATH_GEMM 2          /* LDS-tiled fp16 MFMA GEMM, any m */
+
+/* ------------------------------------------------------------------------ */
+/* W4A16                                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * ql_awq_pack (host).  Group-wise asymmetric uint4 quantisation of a float32
+ * weight w [n, k] and packing, as in the LMDeploy walkthrough, section 2
+ * (per-group min/max, asymmetric zero point) with the tensor names of the AUQ
+ * page, section 5.4.  Per row r and group g (columns [g*group, (g+1)*group)):
+ *   lo = min(0, min w), hi = max(0, max w)
+ *   s  = fp16 value of max((hi - lo) / 15, 2^-14) rounded toward +infinity
+ *   z  = clamp(rint(-lo / s), 0, 15)
+ *   q  = clamp(rint(w / s) + z, 0, 15)           (rint: nearest, ties to even)
+ * Rounding the scale up guarantees |w - (q - z) * s| <= s / 2.
+ * Outputs
+ *   qweight int32 [n, k/8]: word j of row r holds q[r, 8j + i] in bits
+ *                           [4i, 4i + 4), i = 0..7
+ *   scales  fp16  [n, k/group]
+ *   qzeros  int32 [n, ceil(k/group/8)]: zero point of group g in bits
+ *                           [4(g%8), 4(g%8) + 4) of word g/8; pad nibbles 0
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE (n < 0, k <= 0, k % group != 0),
+ * QL_ERR_GROUP, QL_ERR_VALUE (non-finite weight, or (hi - lo) / 15 above the
+ * largest fp16).
+ */
+int ql_awq_pack(const float* w, int64_t n, int64_t k, int group,
+                int32_t* qweight, uint16_t* scales, int32_t* qzeros);
+
+/*
+ * Bytes of device workspace ql_w4a16_gemm needs for this shape (0 if none).
+ * The workspace holds split-K partial sums and per-tile arrival counters.
+ */
+size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
+
+/*
+ * ql_w4a16_gemm (device).  y[m, n] = x[m, k] * dequant(W)^T with
+ *   dequant(W)[r, c] = fp16((q[r, c] - z[r, c/group]) * s[r, c/group])
+ * (one rounding of an exact product; the value ql_w4a16_dequant returns),
+ * fp16 x fp16 products accumulated in fp32, y rounded once to fp16.
+ * The dequantisation happens in registers; packed weights are streamed from
+ * HBM once per call for m <= 32.
+ *   x        fp16 [m, k]            (device)
+ *   qweight, scales, qzeros         as written by ql_awq_pack (device)
+ *   y        fp16 [m, n]            (device, written)
+ *   workspace, workspace_bytes      device scratch of at least
+ *            ql_w4a16_workspace_bytes(m, n, k, group) bytes.  Its first use
+ *            must find it zero-filled; every completed call leaves its counter
+ *            area zero again, so one zeroed buffer serves any number of calls
+ *            on one stream.  Calls that may run concurrently need separate
+ *            workspaces.  May be NULL when the size is 0.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_GROUP, QL_ERR_ALIGN,
+ * QL_ERR_WORKSPACE, QL_ERR_HIP.
+ */
+int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                  const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                  int group, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As ql_w4a16_gemm with an explicit kernel choice (QL_PATH_*), for tests and
+ * tuning.  QL_PATH_DECODE with m > 32 is QL_ERR_UNSUPPORTED. */
+int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                       const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                       int group, void* workspace, size_t workspace_bytes, void* stream,
+                       int path);
+
+/*
+ * ql_w4a16_dequant (device).  Runs the same device dequantisation routine the
+ * GEMM kernels use and writes its results out.
+ *   w16   fp16 [n, k]  dequantised weights (device, written)
+ *   q_u8  uint8 [n, k] unpacked codes (device, written; may be NULL)
+ * Errors as ql_w4a16_gemm (no workspace).
+ */
+int ql_w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                     uint16_t* w16, uint8_t* q_u8, int64_t n, int64_t k, int group,
+                     void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 (SmoothQuant)                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * ql_smooth (host).  SmoothQuant smoothing with alpha = 0.5 (LMDeploy W8A8
+ * guide, "step 2: weight smoothing").  For each input channel j:
+ *   a_j = max over rows of |x[:, j]|,  b_j = max over n of |w[:, j]|
+ *   s_j = sqrt(a_j) / sqrt(b_j)   (s_j = 1 where a_j, b_j or gamma_j is 0)
+ *   gamma_smoothed_j = fp16(gamma_j / s_j),  w_smoothed[:, j] = w[:, j] * s_j
+ *   x      fp16 [rows, k]  activations whose column maxima define a_j (host)
+ *   gamma  fp16 [k]        RMSNorm weight feeding the linear (host)
+ *   w      float32 [n, k]  linear weight (host)
+ *   s float32 [k], gamma_smoothed fp16 [k], w_smoothed float32 [n, k] (host, written)
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_VALUE (non-finite input).
+ */
+int ql_smooth(const uint16_t* x, int64_t rows, const uint16_t* gamma, const float* w,
+              int64_t n, int64_t k, float* s, uint16_t* gamma_smoothed, float* w_smoothed);
+
+/*
+ * ql_w8a8_quant_weight (host).  Per-output-channel symmetric int8 weights
+ * (LMDeploy W8A8 guide, QLinear.from_float / per_channel_quant):
+ *   w_scale[r] = max_j |w[r, j]| / 127
+ *   wq[r, j]   = clamp(rint(w[r, j] / w_scale[r]), -127, 127)  (0 for a zero row)
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_VALUE (non-finite weight).
+ */
+int ql_w8a8_quant_weight(const float* w, int64_t n, int64_t k, int8_t* wq, float* w_scale);
+
+/*
+ * ql_w8a8_quant_rmsnorm (device).  QRMSNorm: RMSNorm fused with per-token
+ * dynamic int8 quantisation (LMDeploy W8A8 guide, "inference kernels":
+ * rms_norm_dynamic_quant, per-token scale = absmax / 127).  Per token i, in
+ * fp32:
+ *   ms  = sum_j x[i,j]^2 / k, computed exactly and rounded once to fp32
+ *   r   = 1 / sqrt(ms + eps)
+ *   y_j = (x[i,j] * r) * gamma[j]
+ *   x_scale[i] = max_j |y_j| / 127
+ *   xq[i,j]    = clamp(rint(y_j / x_scale[i]), -127, 127)  (0 for x_scale 0)
+ * Divisions and the square root are correctly rounded, so results are
+ * bit-identical to any exact implementation of these definitions.
+ *   x fp16 [m, k], gamma fp16 [k] (device); xq int8 [m, k], x_scale float32 [m]
+ *   (device, written).  k <= 65536.  Inputs must be finite.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED,
+ * QL_ERR_HIP.
+ */
+int ql_w8a8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps,
+                          int8_t* xq, float* x_scale, int64_t m, int64_t k, void* stream);
+
+/*
+ * ql_w8a8_gemm (device).  QLinear forward on a quantised activation
+ * (LMDeploy W8A8 guide, matmul_kernel_dynamic_quant): int8 x int8 products
+ * accumulated exactly in int32, then y = fp16((float)acc * x_scale[i] *
+ * w_scale[j]).
+ *   xq int8 [m, k], x_scale float32 [m], wq int8 [n, k], w_scale float32 [n]
+ *   (device); y fp16 [m, n] (device, written).
+ *   k <= 131072 keeps |acc| <= 127 * 127 * k below 2^31.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED, QL_ERR_HIP.
+ */
+int ql_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                 uint16_t* y, int64_t m, int64_t n, int64_t k, void* stream);
+
+/* ql_w8a8_gemm_i32 (device).  The same int8 MFMA main loop writing the raw
+ * int32 accumulator acc [m, n] instead of the fp16 epilogue. */
+int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,
+                     int64_t m, int64_t n, int64_t k, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Static name of a status code ("QL_OK", "QL_ERR_SHAPE", ...). */
+const char* ql_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ql_last_error(void);
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int ql_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

@@ -1,0 +1,135 @@
+"""The C ABI: library loads, exports every symbol of include/qlinear.h, and
+rejects bad arguments with the documented codes before launching anything.
+
+CPU only.  Every device-side call here fails validation (or is an empty
+problem), so no kernel is ever launched; fake device pointers are never
+dereferenced.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import weight_quantized_amd as ql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+LIB = C.CDLL(ql.lib_path)
+for name, (res, args) in ql.EXPORTS.items():
+    getattr(LIB, name).restype = res
+    getattr(LIB, name).argtypes = args
+
+CODES = {}
+with open(HEADER) as f:
+    for m in re.finditer(r"#define (QL_\w+) \(?(-?\d+)\)?", f.read()):
+        CODES[m.group(1)] = int(m.group(2))
+
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+MIS = FAKE + 4                 # misaligned
+DEF = 0                        # default stream
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ql_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(LIB, n), n
+        assert n in ql.EXPORTS, f"binding lacks {n}"
+
+
+def test_status_strings_and_version():
+    for name, code in CODES.items():
+        if name.startswith("QL_ERR") or name == "QL_OK":
+            assert ql.status_string(code) == name
+    assert ql.version() >= 100
+
+
+def _last():
+    return LIB.ql_last_error().decode()
+
+
+def test_w4a16_gemm_validation():
+    g = LIB.ql_w4a16_gemm_path
+    E = CODES
+    # null weight pointers
+    assert g(FAKE, None, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_NULL"]
+    assert "null" in _last()
+    # bad group, k not a multiple of the group, negative sizes
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 16, None, 0, DEF, 0) == E["QL_ERR_GROUP"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 96, 64, None, 0, DEF, 0) == E["QL_ERR_SHAPE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_SHAPE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, -64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_SHAPE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 0, 128, None, 0, DEF, 0) == E["QL_ERR_SHAPE"]
+    # misaligned pointers
+    assert g(FAKE, MIS, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_ALIGN"]
+    assert g(MIS, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_ALIGN"]
+    # decode path with m > 32, unknown path
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 33, 64, 128, 128, None, 0, DEF, 1) == E["QL_ERR_UNSUPPORTED"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 7) == E["QL_ERR_UNSUPPORTED"]
+    # split-K shape with missing / short workspace
+    need = LIB.ql_w4a16_workspace_bytes(16, 4096, 4096, 128)
+    assert need > 0
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 4096, 4096, 128, None, 0, DEF, 0) == E["QL_ERR_WORKSPACE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 4096, 4096, 128, FAKE, need - 1, DEF, 0) == E["QL_ERR_WORKSPACE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 16, 4096, 4096, 128, MIS, need, DEF, 0) == E["QL_ERR_ALIGN"]
+    # empty problems succeed without launching; x and y may then be NULL
+    assert g(None, FAKE, FAKE, FAKE, None, 0, 64, 128, 128, None, 0, DEF, 0) == E["QL_OK"]
+    assert g(None, FAKE, FAKE, FAKE, None, 4, 0, 128, 128, None, 0, DEF, 0) == E["QL_OK"]
+    # non-empty with null activations
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 2) == E["QL_ERR_NULL"]
+
+
+def test_workspace_sizes():
+    assert LIB.ql_w4a16_workspace_bytes(0, 64, 128, 128) == 0
+    assert LIB.ql_w4a16_workspace_bytes(512, 4096, 4096, 64) == 0        # GEMM path needs none
+    a = LIB.ql_w4a16_workspace_bytes(1, 22016, 4096, 128)
+    b = LIB.ql_w4a16_workspace_bytes(16, 22016, 4096, 128)
+    assert 0 < a < b
+
+
+def test_dequant_validation():
+    d = LIB.ql_w4a16_dequant
+    E = CODES
+    assert d(None, FAKE, FAKE, FAKE, None, 64, 128, 128, DEF) == E["QL_ERR_NULL"]
+    assert d(FAKE, FAKE, FAKE, None, None, 64, 128, 128, DEF) == E["QL_ERR_NULL"]
+    assert d(FAKE, FAKE, FAKE, FAKE, MIS, 64, 128, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert d(FAKE, FAKE, FAKE, FAKE, None, 64, 100, 32, DEF) == E["QL_ERR_SHAPE"]
+    assert d(FAKE, FAKE, FAKE, FAKE, None, 0, 128, 128, DEF) == E["QL_OK"]
+
+
+def test_w8a8_validation():
+    E = CODES
+    q = LIB.ql_w8a8_quant_rmsnorm
+    assert q(FAKE, FAKE, 1e-6, FAKE, FAKE, 4, 100, DEF) == E["QL_ERR_SHAPE"]          # k % 8
+    assert q(FAKE, FAKE, 1e-6, FAKE, FAKE, 4, 65544, DEF) == E["QL_ERR_UNSUPPORTED"]
+    assert q(FAKE, FAKE, float("nan"), FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_VALUE"]
+    assert q(FAKE, None, 1e-6, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+    assert q(FAKE, FAKE, 1e-6, MIS, FAKE, 4, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert q(None, None, 1e-6, None, None, 0, 128, DEF) == E["QL_OK"]
+    gm = LIB.ql_w8a8_gemm
+    assert gm(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 100, DEF) == E["QL_ERR_SHAPE"]     # k % 16
+    assert gm(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 131088, DEF) == E["QL_ERR_UNSUPPORTED"]
+    assert gm(FAKE, None, FAKE, FAKE, FAKE, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
+    assert gm(FAKE, FAKE, MIS, FAKE, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert gm(None, None, None, None, None, 0, 64, 128, DEF) == E["QL_OK"]
+    gi = LIB.ql_w8a8_gemm_i32
+    assert gi(FAKE, FAKE, None, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
+    assert gi(FAKE, FAKE, FAKE, 4, -1, 128, DEF) == E["QL_ERR_SHAPE"]
+
+
+def test_python_binding_raises():
+    with pytest.raises(ql.QLError) as e:
+        ql.awq_pack(np.zeros((4, 100), np.float32), 32)
+    assert e.value.code == CODES["QL_ERR_SHAPE"]
+    with pytest.raises(ql.QLError) as e:
+        ql.awq_pack(np.zeros((4, 128), np.float32), 48)
+    assert e.value.code == CODES["QL_ERR_GROUP"]

@@ -1,0 +1,187 @@
+"""W4A16 HIP path against the oracle (GPU).
+
+Bar: unpacked codes and fp16 dequantised weights bit-exact; fp16 GEMM output
+max|gpu - oracle| / max|oracle| <= 2e-3 (oracle: fp64 accumulation of the
+same fp16 dequantised weights).  Every call goes through libqlinear's C ABI.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ql():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import weight_quantized_amd
+    return weight_quantized_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def pack_dev(ql, w, group):
+    qw, sc, qz = ql.awq_pack(w, group)
+    return (qw, sc, qz), (dev(qw), dev(sc), dev(qz))
+
+
+def rel_err(got, ref):
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / (den if den > 0 else 1.0))
+
+
+def sample_rows(n, seed=0, count=16):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(16, n - 16), size=min(count, max(n - 32, 0)), replace=False) if n > 32 else []
+    return np.unique(np.concatenate([np.arange(min(16, n)), np.arange(max(n - 16, 0), n), mid]).astype(np.int64))
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("n,k,group", [(64, 128, 32), (100, 1056, 32), (48, 4096, 128), (64, 4096, 64),
+                                       (33, 11008, 128)])
+def test_dequant_bit_exact(ql, n, k, group):
+    rng = np.random.default_rng(n + k + group)
+    w = workloads.weight(rng, n, k, outliers="normal0.3", outlier_frac=0.01)
+    w[0, :group] = 0.0
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    w16, codes = ql.w4a16_dequant(*d, group, with_codes=True)
+    torch.cuda.synchronize()
+    oq, oz = oracle.awq_unpack(qw, qz, group)
+    _, owd16 = oracle.awq_dequant(oq, oz, sc, group)
+    assert np.array_equal(codes.cpu().numpy(), oq)
+    assert np.array_equal(w16.cpu().numpy().view(np.uint16), owd16.view(np.uint16))
+
+
+def test_dequant_bit_exact_q_proj(ql):
+    w = workloads.config_weight("q_proj")
+    (qw, sc, qz), d = pack_dev(ql, w, 128)
+    w16 = ql.w4a16_dequant(*d, 128)
+    torch.cuda.synchronize()
+    oq, oz = oracle.awq_unpack(qw, qz, 128)
+    _, owd16 = oracle.awq_dequant(oq, oz, sc, 128)
+    assert np.array_equal(w16.cpu().numpy().view(np.uint16), owd16.view(np.uint16))
+
+
+# ------------------------------------------------------------------ GEMM, small shapes
+SMALL = [
+    # m, n, k, group
+    (1, 64, 128, 32), (2, 64, 256, 64), (3, 64, 256, 128), (1, 48, 1056, 32), (5, 200, 1024, 64),
+    (16, 128, 4096, 128), (17, 64, 512, 32), (31, 96, 2080, 32), (32, 256, 4096, 128),
+    (1, 4096, 4096, 128), (8, 1000, 11008, 128),
+]
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("m,n,k,group", SMALL)
+def test_gemm_small_parity(ql, path, m, n, k, group):
+    rng = np.random.default_rng(m * 7 + n * 3 + k + group)
+    w = workloads.weight(rng, n, k, outliers="pm0.3")
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y = ql.w4a16_gemm(dev(x), *d, group, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k,group", [(33, 64, 256, 64), (64, 128, 512, 128), (100, 300, 1056, 32),
+                                         (130, 256, 4096, 64), (257, 130, 384, 128)])
+def test_gemm_path_mid_m(ql, m, n, k, group):
+    rng = np.random.default_rng(m + n + k)
+    w = workloads.weight(rng, n, k, outliers="normal0.3")
+    x = workloads.activations(rng, m, k, outlier_channel_frac=0.01)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y = ql.w4a16_gemm(dev(x), *d, group)
+    torch.cuda.synchronize()
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group)
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_gemm_closed_forms(ql, path):
+    k, group, n = 1024, 64, 96
+    rng = np.random.default_rng(9)
+    w = workloads.weight(rng, n, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    w16 = ql.w4a16_dequant(*d, group).cpu().numpy()
+    # one-hot rows of x: y[i, :] = w16[:, col_i] exactly
+    cols = np.array([0, 1, 7, 8, 31, 32, 127, 128, 500, 1023, 640, 333, 64, 65, 900, 1000])
+    x = np.zeros((16, k), np.float16)
+    x[np.arange(16), cols] = 1.0
+    y = ql.w4a16_gemm(dev(x), *d, group, path=path).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), w16[:, cols].T.copy().view(np.uint16))
+    # every code equal to its zero point -> exactly zero
+    q, z, s = oracle.awq_quantize(w, group)
+    qw2, qz2 = oracle.awq_pack(np.repeat(z, group, axis=1), z, group)
+    x2 = workloads.activations(rng, 5, k)
+    y2 = ql.w4a16_gemm(dev(x2), dev(qw2), dev(sc), dev(qz2), group, path=path).cpu().numpy()
+    assert not y2.any()
+
+
+def test_gemm_empty(ql):
+    qw = torch.zeros((64, 16), dtype=torch.int32, device="cuda:0")
+    sc = torch.zeros((64, 1), dtype=torch.float16, device="cuda:0")
+    qz = torch.zeros((64, 1), dtype=torch.int32, device="cuda:0")
+    y = ql.w4a16_gemm(torch.zeros((0, 128), dtype=torch.float16, device="cuda:0"), qw, sc, qz, 128)
+    assert y.shape == (0, 64)
+
+
+def test_decode_deterministic_and_workspace_left_zero(ql):
+    m, n, k, group = 16, 4096, 4096, 128
+    rng = np.random.default_rng(4)
+    w = workloads.weight(rng, n, k)
+    x = dev(workloads.activations(rng, m, k))
+    _, d = pack_dev(ql, w, group)
+    need = ql.w4a16_workspace_bytes(m, n, k, group)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    y1 = ql.w4a16_gemm(x, *d, group, workspace=ws, path=1).clone()
+    y2 = ql.w4a16_gemm(x, *d, group, workspace=ws, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    counters = ws[:256].cpu().numpy()
+    assert not counters.any()
+
+
+# ------------------------------------------------------------------ full-size configurations
+def _config_case(ql, name, m, group, seed=0, rows_seed=0):
+    w = workloads.config_weight(name, seed=seed)
+    n, k = w.shape
+    x = workloads.config_activations(name, m, k, seed=seed)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y = ql.w4a16_gemm(dev(x), *d, group)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, rows_seed)
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
+    got = y.cpu().numpy()[:, rows]
+    assert np.isfinite(y.cpu().numpy()).all()
+    return rel_err(got, ref)
+
+
+def test_config_q_proj_m1(ql):
+    assert _config_case(ql, "q_proj", 1, 128) <= TOL
+
+
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 32])
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_config_llama7b_mlp_decode(ql, name, m):
+    assert _config_case(ql, name, m, 128) <= TOL
+
+
+def test_config_qkv_prefill(ql):
+    assert _config_case(ql, "qkv", 512, 64) <= TOL
+
+
+@pytest.mark.parametrize("name", ["13b_up", "13b_down"])
+@pytest.mark.parametrize("m,group", [(1, 128), (8, 128), (64, 128), (256, 128), (1024, 128),
+                                     (1, 32), (64, 32), (1024, 32)])
+def test_config_llama13b_sweep(ql, name, m, group):
+    assert _config_case(ql, name, m, group) <= TOL

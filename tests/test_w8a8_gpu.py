@@ -1,0 +1,125 @@
+"""W8A8 (SmoothQuant) HIP path against the oracle (GPU).
+
+Bar: QRMSNorm int8 codes and fp32 scales bit-exact (the mean of squares is
+exact on both sides and every other step is one correctly rounded fp32
+operation); int32 accumulators bit-exact; fp16 output within 2e-3 of the
+oracle's fp64 epilogue relative to max|oracle|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ql():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import weight_quantized_amd
+    return weight_quantized_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def rel_err(got, ref):
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got.astype(np.float64) - ref)) / (den if den > 0 else 1.0))
+
+
+@pytest.mark.parametrize("m,k", [(1, 8), (3, 4096), (17, 1000), (64, 4096), (5, 11008), (2, 65536)])
+def test_quant_rmsnorm_bit_exact(ql, m, k):
+    x, gamma, _ = workloads.smoothquant_inputs(m=m, k=k, n=1, seed=m + k)
+    xq, xs = ql.w8a8_quant_rmsnorm(dev(x), dev(gamma), 1e-6)
+    torch.cuda.synchronize()
+    oq, osc = oracle.quant_rmsnorm(x, gamma, 1e-6)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    assert np.array_equal(xq.cpu().numpy(), oq)
+
+
+def test_quant_rmsnorm_edge_rows(ql):
+    k = 512
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((8, k)).astype(np.float16)
+    x[0] = 0                                              # zero token
+    x[1] = 0
+    x[1, 100] = -2.5                                      # single nonzero
+    x[2] = np.float16(65504)                              # largest fp16 everywhere
+    x[3] = np.float16(2.0 ** -24)                         # smallest subnormal everywhere
+    x[4, ::3] = np.float16(6e-5)                          # subnormal / normal boundary
+    x[5] = np.float16(0.5)                                # constant row
+    gamma = rng.uniform(0.5, 1.5, k).astype(np.float16)
+    gamma[7] = 0
+    for eps in (1e-6, 0.0, 1e-2):
+        xq, xs = ql.w8a8_quant_rmsnorm(dev(x), dev(gamma), eps)
+        torch.cuda.synchronize()
+        oq, osc = oracle.quant_rmsnorm(x, gamma, eps)
+        assert np.array_equal(xs.cpu().numpy().view(np.uint32), osc.view(np.uint32)), eps
+        assert np.array_equal(xq.cpu().numpy(), oq), eps
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 16), (5, 64, 128), (130, 200, 4096), (64, 128, 1040), (257, 33, 512)])
+def test_gemm_i32_bit_exact_small(ql, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    acc = ql.w8a8_gemm_i32(dev(xq), dev(wq))
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.int8_gemm(xq, wq))
+
+
+def test_gemm_i32_saturating_operands(ql):
+    k = 4096
+    xq = np.full((128, k), 127, np.int8)
+    wq = np.full((128, k), 127, np.int8)
+    wq[1] = -127
+    acc = ql.w8a8_gemm_i32(dev(xq), dev(wq)).cpu().numpy()
+    assert (acc[:, 0] == 16129 * k).all() and (acc[:, 1] == -16129 * k).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 64, 128), (130, 200, 4096), (2048, 512, 4096)])
+def test_gemm_fp16_parity_small(ql, m, n, k):
+    rng = np.random.default_rng(m * n)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    xs = rng.uniform(1e-3, 1e-1, m).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    y = ql.w8a8_gemm(dev(xq), dev(xs), dev(wq), dev(ws))
+    torch.cuda.synchronize()
+    ref = oracle.w8a8_forward(xq, xs, wq, ws)
+    assert rel_err(y.cpu().numpy(), ref) <= TOL
+
+
+def test_config_smoothquant_pipeline(ql):
+    """Full W8A8 workload: host smoothing and int8 weights, GPU QRMSNorm and
+    int8 GEMM, against the oracle's own pipeline on sampled outputs."""
+    x, gamma, w = workloads.smoothquant_inputs()
+    s, gs, wsm = ql.smooth(x, gamma, w)
+    wq, wsc = ql.w8a8_quant_weight(wsm)
+    # oracle pipeline, independent of the library's host steps
+    os_, ogs, owsm = oracle.smooth(x, gamma, w)
+    owq, owsc = oracle.w8_quant_weight(owsm)
+    oxq, oxs = oracle.quant_rmsnorm(x, ogs, 1e-6)
+
+    xq, xs = ql.w8a8_quant_rmsnorm(dev(x), dev(gs), 1e-6)
+    wq_d, wsc_d = dev(wq), dev(wsc)
+    acc = ql.w8a8_gemm_i32(xq, wq_d)
+    y = ql.w8a8_gemm(xq, xs, wq_d, wsc_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq.cpu().numpy(), oxq)
+    assert np.array_equal(xs.cpu().numpy(), oxs)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(2040, 2048), rng.choice(2048, 24, replace=False)]))
+    cols = np.unique(np.concatenate([np.arange(8), np.arange(11000, 11008), rng.choice(11008, 40, replace=False)]))
+    oacc = oracle.int8_gemm(oxq, owq, rows=rows, cols=cols)
+    assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), oacc)
+    oy = oracle.w8a8_forward(oxq, oxs, owq, owsc, rows=rows, cols=cols)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got[np.ix_(rows, cols)], oy) <= TOL

@@ -1,0 +1,259 @@
+"""Python binding of libqlinear, the MI355X quantized linear layer.
+
+Argument marshalling only: every step runs in libqlinear (HIP kernels for
+gfx950 and the host quantisers).  Device tensors are torch tensors on the
+current HIP device; PyTorch supplies memory and the current stream.  Host
+functions take and return NumPy arrays.
+
+The library must have been built (``python -m weight_quantized_amd.build``);
+importing the package without it raises ImportError -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+__all__ = [
+    "QLError", "lib_path", "awq_pack", "smooth", "w8a8_quant_weight",
+    "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant", "w8a8_quant_rmsnorm",
+    "w8a8_gemm", "w8a8_gemm_i32", "status_string", "version",
+    "PATH_AUTO", "PATH_DECODE", "PATH_GEMM", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libqlinear.so")
+
+PATH_AUTO, PATH_DECODE, PATH_GEMM = 0, 1, 2
+
+_p, _i64, _sz, _i = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
+
+# name -> (restype, argtypes); mirrors include/qlinear.h
+EXPORTS = {
+    "ql_awq_pack": (_i, [_p, _i64, _i64, _i, _p, _p, _p]),
+    "ql_w4a16_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
+    "ql_w4a16_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p]),
+    "ql_w4a16_gemm_path": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p, _i]),
+    "ql_w4a16_dequant": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i, _p]),
+    "ql_smooth": (_i, [_p, _i64, _p, _p, _i64, _i64, _p, _p, _p]),
+    "ql_w8a8_quant_weight": (_i, [_p, _i64, _i64, _p, _p]),
+    "ql_w8a8_quant_rmsnorm": (_i, [_p, _p, C.c_float, _p, _p, _i64, _i64, _p]),
+    "ql_w8a8_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "ql_w8a8_gemm_i32": (_i, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "ql_status_string": (C.c_char_p, [_i]),
+    "ql_last_error": (C.c_char_p, []),
+    "ql_version": (_i, []),
+}
+
+if not os.path.exists(lib_path):
+    raise ImportError(f"libqlinear.so not built at {lib_path}; run `python -m weight_quantized_amd.build`")
+
+_lib = C.CDLL(lib_path)
+for _name, (_res, _args) in EXPORTS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class QLError(RuntimeError):
+    """A libqlinear call returned a QL_ERR_* status."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{status_string(code)} ({code}): {msg}")
+        self.code = code
+
+
+def status_string(code: int) -> str:
+    return _lib.ql_status_string(code).decode()
+
+
+def version() -> int:
+    return _lib.ql_version()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise QLError(rc, _lib.ql_last_error().decode())
+
+
+def _np(a, dtype):
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _f16_bits(a):
+    a = np.asarray(a)
+    if a.dtype == np.float16:
+        return np.ascontiguousarray(a).view(np.uint16)
+    if a.dtype == np.uint16:
+        return np.ascontiguousarray(a)
+    raise TypeError(f"expected float16, got {a.dtype}")
+
+
+# ---------------------------------------------------------------- host
+def awq_pack(w, group: int):
+    """float32 w [n, k] -> (qweight int32 [n, k/8], scales float16 [n, k/group],
+    qzeros int32 [n, ceil(k/group/8)])."""
+    w = _np(w, np.float32)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D")
+    n, k = w.shape
+    g = max(int(group), 1)
+    qw = np.empty((n, k // 8), np.int32)
+    sc = np.empty((n, k // g), np.uint16)
+    qz = np.empty((n, (k // g + 7) // 8), np.int32)
+    _check(_lib.ql_awq_pack(w.ctypes.data, n, k, int(group), qw.ctypes.data, sc.ctypes.data, qz.ctypes.data))
+    return qw, sc.view(np.float16), qz
+
+
+def smooth(x, gamma, w):
+    """SmoothQuant smoothing (alpha = 0.5): (s float32 [k], gamma' float16 [k], W' float32 [n, k])."""
+    x = _f16_bits(x)
+    gm = _f16_bits(gamma)
+    w = _np(w, np.float32)
+    rows, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k or gm.shape != (k,):
+        raise ValueError("shape mismatch")
+    s = np.empty(k, np.float32)
+    gs = np.empty(k, np.uint16)
+    ws = np.empty((n, k), np.float32)
+    _check(_lib.ql_smooth(x.ctypes.data, rows, gm.ctypes.data, w.ctypes.data, n, k,
+                          s.ctypes.data, gs.ctypes.data, ws.ctypes.data))
+    return s, gs.view(np.float16), ws
+
+
+def w8a8_quant_weight(w):
+    """Per-channel symmetric int8: (wq int8 [n, k], w_scale float32 [n])."""
+    w = _np(w, np.float32)
+    n, k = w.shape
+    wq = np.empty((n, k), np.int8)
+    sc = np.empty(n, np.float32)
+    _check(_lib.ql_w8a8_quant_weight(w.ctypes.data, n, k, wq.ctypes.data, sc.ctypes.data))
+    return wq, sc
+
+
+# ---------------------------------------------------------------- device
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def w4a16_workspace_bytes(m: int, n: int, k: int, group: int) -> int:
+    return int(_lib.ql_w4a16_workspace_bytes(m, n, k, group))
+
+
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    """A zero-filled workspace per device, grown on demand.  The kernels leave
+    its counter area zero after every call, so it is reused as is."""
+    torch = _torch()
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def w4a16_gemm(x, qweight, scales, qzeros, group: int, out=None, workspace=None, path: int = PATH_AUTO):
+    """y fp16 [m, n] = x fp16 [m, k] @ dequant(W)^T."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float16, "scales")
+    qzeros = _dev(qzeros, torch.int32, "qzeros")
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k:
+        raise ValueError("qweight does not match x's k")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    out = _dev(out, torch.float16, "out")
+    need = w4a16_workspace_bytes(m, n, k, group) if path != PATH_GEMM else 0
+    if workspace is None:
+        workspace = _workspace(x.device, need) if need else None
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.ql_w4a16_gemm_path(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                                   out.data_ptr(), m, n, k, int(group), wptr, wbytes, _stream(x), int(path)))
+    return out
+
+
+def w4a16_dequant(qweight, scales, qzeros, group: int, with_codes: bool = False):
+    """Dequantised fp16 weights [n, k] (and uint8 codes [n, k] if with_codes)."""
+    torch = _torch()
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float16, "scales")
+    qzeros = _dev(qzeros, torch.int32, "qzeros")
+    n, k = qweight.shape[0], qweight.shape[1] * 8
+    w16 = torch.empty((n, k), dtype=torch.float16, device=qweight.device)
+    q8 = torch.empty((n, k), dtype=torch.uint8, device=qweight.device) if with_codes else None
+    _check(_lib.ql_w4a16_dequant(qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), w16.data_ptr(),
+                                 q8.data_ptr() if q8 is not None else None, n, k, int(group), _stream(qweight)))
+    return (w16, q8) if with_codes else w16
+
+
+def w8a8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
+    """QRMSNorm: (xq int8 [m, k], x_scale float32 [m])."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    gamma = _dev(gamma, torch.float16, "gamma")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_w8a8_quant_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), xq.data_ptr(),
+                                      x_scale.data_ptr(), m, k, _stream(x)))
+    return xq, x_scale
+
+
+def w8a8_gemm(xq, x_scale, wq, w_scale, out=None):
+    """y fp16 [m, n] = fp16((xq @ wq^T) * x_scale[:, None] * w_scale[None, :])."""
+    torch = _torch()
+    xq = _dev(xq, torch.int8, "xq")
+    wq = _dev(wq, torch.int8, "wq")
+    x_scale = _dev(x_scale, torch.float32, "x_scale")
+    w_scale = _dev(w_scale, torch.float32, "w_scale")
+    m, k = xq.shape
+    n = wq.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
+    _check(_lib.ql_w8a8_gemm(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
+                             out.data_ptr(), m, n, k, _stream(xq)))
+    return out
+
+
+def w8a8_gemm_i32(xq, wq, out=None):
+    """Raw int32 accumulator [m, n] = xq @ wq^T."""
+    torch = _torch()
+    xq = _dev(xq, torch.int8, "xq")
+    wq = _dev(wq, torch.int8, "wq")
+    m, k = xq.shape
+    n = wq.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    _check(_lib.ql_w8a8_gemm_i32(xq.data_ptr(), wq.data_ptr(), out.data_ptr(), m, n, k, _stream(xq)))
+    return out

@@ -1,0 +1,74 @@
+// Device dequantisation of packed uint4 weights (gfx950).  One routine is
+// shared by the dequant export and both W4A16 GEMM paths, so the bit-exact
+// check of the export covers the values the GEMMs contract.
+//
+// A 32-bit word holds codes q0..q7 (code i in bits [4i, 4i+4), consecutive
+// input channels).  Masking two nibbles that sit 16 bits apart and OR-ing in
+// 0x6400 (fp16 1024.0, whose mantissa ulp is 1) gives the fp16 pair
+// (1024 + qi, 1024 + q(i+4)) in one VALU instruction.  Subtracting
+// (1024 + z) is exact in fp16 and leaves the small integer q - z; one fp16
+// multiply by the group scale s then rounds the exact product (q - z) * s
+// once, to nearest even.  This is bit-identical to computing (q - z) * s
+// exactly and rounding it to fp16 afterwards.
+//
+// Output element order within the 8 lanes of a word: (0,4) (1,5) (2,6) (3,7).
+// Contractions take the activation chunk in the same order (permute_x8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t u2h(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+__device__ __forceinline__ uint32_t h2u(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// (1024 + z) in both halves, z = zero point of the group.
+__device__ __forceinline__ h2_t zero_bias(uint32_t z) { return u2h((0x6400u | z) * 0x10001u); }
+// the fp16 scale in both halves
+__device__ __forceinline__ h2_t scale2(uint32_t s16) { return u2h(s16 * 0x10001u); }
+
+// Eight codes of one word -> eight fp16 weights in the order (0,4)(1,5)(2,6)(3,7).
+__device__ __forceinline__ void dequant_word(uint32_t w, h2_t zb, h2_t s2, h2_t out[4])
+{
+    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
+    out[0] = (u2h((w & kMask) | kMagic) - zb) * s2;
+    out[1] = (u2h(((w >> 4) & kMask) | kMagic) - zb) * s2;
+    out[2] = (u2h(((w >> 8) & kMask) | kMagic) - zb) * s2;
+    out[3] = (u2h(((w >> 12) & kMask) | kMagic) - zb) * s2;
+}
+
+// dequant_word packed as one 8-half MFMA operand
+__device__ __forceinline__ h8_t dequant_word8(uint32_t w, h2_t zb, h2_t s2)
+{
+    h2_t o[4];
+    dequant_word(w, zb, s2, o);
+    h8_t r;
+    r[0] = o[0][0]; r[1] = o[0][1]; r[2] = o[1][0]; r[3] = o[1][1];
+    r[4] = o[2][0]; r[5] = o[2][1]; r[6] = o[3][0]; r[7] = o[3][1];
+    return r;
+}
+
+// Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
+// (0,4)(1,5)(2,6)(3,7) that matches dequant_word.
+__device__ __forceinline__ uint4 permute_x8(uint4 v)
+{
+    uint4 p;
+    p.x = (v.x & 0xFFFFu) | (v.z << 16);
+    p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    p.z = (v.y & 0xFFFFu) | (v.w << 16);
+    p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return p;
+}
+
+// Zero point of group g of one row: nibble g%8 of word g/8.
+__device__ __forceinline__ uint32_t zero_of(const uint32_t* qz_row, int g)
+{
+    return (qz_row[g >> 3] >> (4 * (g & 7))) & 0xFu;
+}
+
+}  // namespace ql
