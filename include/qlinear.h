@@ -108,11 +108,13 @@ size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
  *   qweight, scales, qzeros         as written by ql_awq_pack (device)
  *   y        fp16 [m, n]            (device, written)
  *   workspace, workspace_bytes      device scratch of at least
- *            ql_w4a16_workspace_bytes(m, n, k, group) bytes.  Its first use
- *            must find it zero-filled; every completed call leaves its counter
- *            area zero again, so one zeroed buffer serves any number of calls
- *            on one stream.  Calls that may run concurrently need separate
- *            workspaces.  May be NULL when the size is 0.
+ *            ql_w4a16_workspace_bytes(m, n, k, group) bytes: a fixed 32 KiB
+ *            region of split-K arrival counters followed by fp32 partial sums.
+ *            Its first use must find the counter region zero-filled; every
+ *            completed call leaves it zero again, so one zeroed buffer serves
+ *            any number of calls of any shape on one stream.  Calls that may
+ *            run concurrently need separate workspaces.  May be NULL when the
+ *            size is 0.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_GROUP, QL_ERR_ALIGN,
  * QL_ERR_WORKSPACE, QL_ERR_HIP.
  */

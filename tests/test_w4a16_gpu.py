@@ -147,8 +147,30 @@ def test_decode_deterministic_and_workspace_left_zero(ql):
     y2 = ql.w4a16_gemm(x, *d, group, workspace=ws, path=1)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    counters = ws[:256].cpu().numpy()
+    counters = ws[:32768].cpu().numpy()
     assert not counters.any()
+
+
+def test_decode_shared_workspace_across_shapes(ql):
+    """One workspace serves calls of different shapes in turn (split-K counters
+    and partial sums of one call never alias another call's)."""
+    group = 128
+    rng = np.random.default_rng(6)
+    cases = [(16, 4096, 4096), (1, 22016, 4096), (8, 1000, 11008), (16, 22016, 4096), (32, 4096, 11008)]
+    need = max(ql.w4a16_workspace_bytes(m, n, k, group) for m, n, k in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    for m, n, k in cases + cases[::-1]:
+        w = workloads.weight(rng, n, k)
+        x = workloads.activations(rng, m, k)
+        (qw, sc, qz), d = pack_dev(ql, w, group)
+        y = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=1)
+        torch.cuda.synchronize()
+        rows = sample_rows(n, 1)
+        ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
+        got = y.cpu().numpy()
+        assert np.isfinite(got).all()
+        assert rel_err(got[:, rows], ref) <= TOL, (m, n, k)
+    assert not ws[:32768].cpu().numpy().any()
 
 
 # ------------------------------------------------------------------ full-size configurations

@@ -49,6 +49,10 @@ EXPORTS = {
 if not os.path.exists(lib_path):
     raise ImportError(f"libqlinear.so not built at {lib_path}; run `python -m weight_quantized_amd.build`")
 
+# torch first: its HIP runtime (libamdhip64.so.7) is then already loaded and the
+# library binds to that one instance instead of mapping a second runtime.
+import torch  # noqa: E402,F401
+
 _lib = C.CDLL(lib_path)
 for _name, (_res, _args) in EXPORTS.items():
     _fn = getattr(_lib, _name)

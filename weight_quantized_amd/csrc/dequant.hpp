@@ -32,14 +32,24 @@ __device__ __forceinline__ h2_t zero_bias(uint32_t z) { return u2h((0x6400u | z)
 // the fp16 scale in both halves
 __device__ __forceinline__ h2_t scale2(uint32_t s16) { return u2h(s16 * 0x10001u); }
 
+// (w & mask) | magic in one VALU instruction.  The compiler otherwise splits
+// it into an AND and an OR.  VOP3 may read one scalar register: the mask sits
+// in an SGPR, the magic constant in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+
 // Eight codes of one word -> eight fp16 weights in the order (0,4)(1,5)(2,6)(3,7).
 __device__ __forceinline__ void dequant_word(uint32_t w, h2_t zb, h2_t s2, h2_t out[4])
 {
     constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
-    out[0] = (u2h((w & kMask) | kMagic) - zb) * s2;
-    out[1] = (u2h(((w >> 4) & kMask) | kMagic) - zb) * s2;
-    out[2] = (u2h(((w >> 8) & kMask) | kMagic) - zb) * s2;
-    out[3] = (u2h(((w >> 12) & kMask) | kMagic) - zb) * s2;
+    out[0] = (u2h(and_or(w, kMask, kMagic)) - zb) * s2;
+    out[1] = (u2h(and_or(w >> 4, kMask, kMagic)) - zb) * s2;
+    out[2] = (u2h(and_or(w >> 8, kMask, kMagic)) - zb) * s2;
+    out[3] = (u2h(and_or(w >> 12, kMask, kMagic)) - zb) * s2;
 }
 
 // dequant_word packed as one 8-half MFMA operand
@@ -47,10 +57,7 @@ __device__ __forceinline__ h8_t dequant_word8(uint32_t w, h2_t zb, h2_t s2)
 {
     h2_t o[4];
     dequant_word(w, zb, s2, o);
-    h8_t r;
-    r[0] = o[0][0]; r[1] = o[0][1]; r[2] = o[1][0]; r[3] = o[1][1];
-    r[4] = o[2][0]; r[5] = o[2][1]; r[6] = o[3][0]; r[7] = o[3][1];
-    return r;
+    return __builtin_bit_cast(h8_t, make_uint4(h2u(o[0]), h2u(o[1]), h2u(o[2]), h2u(o[3])));
 }
 
 // Eight consecutive fp16 activations (as four 32-bit pairs) -> the order

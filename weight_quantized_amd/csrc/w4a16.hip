@@ -73,93 +73,172 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 // ---------------------------------------------------------------------------
 // decode: m <= MT (16 or 32)
 //
-// Workgroup = NT waves; wave w owns 16 output channels; the workgroup covers a
-// K slice of NB blocks of 256.  In a block, lane l (row l%16, quarter
-// q = l/16) loads two 16-byte pieces of its row: words [4q, 4q+4) and
-// [16+4q, 16+4q+4), so 4 lanes read 64 contiguous bytes per row per load.
-// Word j of piece i feeds MFMA 4i+j; the matching activations are chunk
-// 16i + 4q + j of the block, staged once per workgroup in LDS in the
-// dequantiser's element order.  All NB blocks are requested before any is
-// consumed.  Slices are combined in fixed order by the last workgroup to
-// finish a column block (deterministic split-K).
+// Workgroup = T waves; wave t owns 16 output channels, so a workgroup covers
+// 16T channels and one K slice of KS (a multiple of 256).  The slice's
+// activations (rows < m) are staged once in LDS, in the dequantiser's element
+// order, and shared by the T waves.  Each wave then streams its 16 rows of the
+// slice in blocks of 256 k through a P-deep register ring: as soon as block b
+// is consumed its slot is refilled with block b + P, so every wave keeps about
+// P x 2 KB of weights in flight.
+//
+// In a block, lane l (row l%16, quarter q = l/16) loads two 16-byte pieces of
+// its row: words [4q, 4q+4) and [16+4q, 16+4q+4), so 4 lanes read 64
+// contiguous bytes of a row per load.  Word j of piece i is the B operand of
+// one MFMA directly; weights never pass through LDS.
+//
+// Weights, scales and zero points are read with buffer loads: a scalar
+// resource per tensor and a 32-bit per-lane offset, so the per-block address
+// arithmetic is one add or an immediate offset.  A read past a resource's end
+// returns zero.  Lanes past N read row N-1 and their outputs are discarded;
+// pieces past the slice end read finite words of the same tensor that meet
+// zero activations (the staged slice is zero past K).  MFMA rows past m read
+// a real activation row and are never stored.
+//
+// Split-K (S > 1 slices): each slice writes its fp32 partial tile with
+// agent-scope stores, waits for them to complete, then bumps a per-column-block
+// arrival counter; the last arrival reads the partials back with agent-scope
+// loads and sums them in slice order (deterministic).  No cache-wide fence is
+// needed because every cross-workgroup value travels through agent-scope
+// accesses.
 // ---------------------------------------------------------------------------
-constexpr int kDecodeNT = 4;
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 
-template <int MT, int NT, int NB>
-__global__ __launch_bounds__(64 * NT) void w4a16_decode_kernel(
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+template <int MT, int T, int P>
+__global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int M, int N, int K, int G)
+    uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
 {
-    constexpr int KS = NB * 256;        // k per slice
-    constexpr int CH = KS / 8;          // 8-element chunks per slice
-    constexpr int RS = CH + 1;          // LDS row stride in uint4 (16-byte pad)
-    __shared__ uint4 xs[MT * RS];
+    // LDS: activations [min(M, MT)][RS] uint4, then per (row, group) of the
+    // slice one word holding (fp16 scale | zero point << 16)
+    extern __shared__ uint4 xs[];
     __shared__ int s_last;
 
     const int S = gridDim.y;
     const int k0 = blockIdx.y * KS;
     const int kend = min(K, k0 + KS);
     const int nch = (kend - k0) >> 3;
-
-    // activations of this slice -> LDS (rows < M only; chunks past K are zero)
-    for (int idx = threadIdx.x; idx < M * CH; idx += 64 * NT) {
-        const int m = idx / CH, c = idx - m * CH;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nch)
-            v = ql::permute_x8(*reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + 8 * c));
-        xs[m * RS + c] = v;
-    }
+    const int nb = (kend - k0 + 255) >> 8;
+    const int nbp = (nb + P - 1) / P * P;         // blocks streamed, padded to the ring
+    const int RS = ((KS >> 8) + P - 1) / P * P * 32 + 1;   // padded slice + 16-byte pad
+    const int mrows = M < MT ? M : MT;
+    const int gs = KS >> lg;                      // groups per slice
+    uint32_t* sz = reinterpret_cast<uint32_t*>(xs + mrows * RS);   // [16T][gs]
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
-    const int n = (blockIdx.x * NT + wave) * 16 + r16;
+    const int n0 = blockIdx.x * T * 16;
+    const int n = n0 + wave * 16 + r16;
     const bool nok = n < N;
-    const int KW = K >> 3, NG = K / G, ZW = (NG + 7) >> 3;
-    const uint32_t* qrow = qw + (int64_t)(nok ? n : 0) * KW;
-    const uint16_t* srow = sc + (int64_t)(nok ? n : 0) * NG;
-    const uint32_t* zrow = qz + (int64_t)(nok ? n : 0) * ZW;
+    const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
+    const uint32_t nr = (uint32_t)(nok ? n : N - 1);
 
-    uint4 wv[NB][2];
-    uint32_t sv[NB][2], zv[NB][2];
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
+    const uint32_t ow = nr * (uint32_t)KW * 4u + (uint32_t)(k0 + 32 * q) / 2u;   // block 0, piece 0
+    auto load_block = [&](int b, uint4& w0, uint4& w1) {
+        const uint32_t bw = ow + (uint32_t)b * 128u;
+        w0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)bw, 0, 0));
+        w1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(bw + 64u), 0, 0));
+    };
+
+    // 1. the first P weight blocks (unconditional: blocks past the slice
+    // re-read block nb-1, so every wait in the stream has a static count)
+    uint4 ring[P][2];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int kk = k0 + b * 256 + i * 128 + 32 * q;
-            const bool ok = nok && kk < kend;
-            wv[b][i] = ok ? *reinterpret_cast<const uint4*>(qrow + (kk >> 3)) : make_uint4(0u, 0u, 0u, 0u);
-            const int g = kk / G;
-            sv[b][i] = ok ? srow[g] : 0u;
-            zv[b][i] = ok ? ql::zero_of(zrow, g) : 0u;
+    for (int p = 0; p < P; ++p) {
+        load_block(p < nb ? p : nb - 1, ring[p][0], ring[p][1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 2. scales and zero points of this workgroup's rows and slice -> LDS
+    {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, (uint32_t)N * (uint32_t)NG * 2u);
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
+        const int g0 = k0 >> lg;
+        for (int e = threadIdx.x; e < 16 * T * gs; e += 64 * T) {
+            const int rr = e / gs, gg = e - rr * gs;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t g = (uint32_t)(g0 + gg);
+            const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)((row * (uint32_t)NG + g) * 2u), 0, 0);
+            const uint32_t zw = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)((row * (uint32_t)ZW + (g >> 3)) * 4u), 0, 0);
+            sz[e] = sv | (((zw >> (4 * (g & 7))) & 0xFu) << 16);
         }
+    }
+
+    // 3. activations of the slice -> LDS (zero past K and in the ring padding)
+    {
+        const int cpr = nbp * 32;
+        const int total = mrows * cpr;
+        for (int idx = threadIdx.x; idx < total; idx += 64 * T) {
+            const int m = idx / cpr, c = idx - m * cpr;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (c < nch)
+                v = ql::permute_x8(*reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + 8 * c));
+            xs[m * RS + c] = v;
+        }
+    }
     __syncthreads();
 
-    f4_t acc[MT / 16];
+    // 4. stream the slice: consume block b, refill its slot with block b + P
+    f4_t acc[4][MT / 16];
 #pragma unroll
-    for (int t = 0; t < MT / 16; ++t)
-        acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < MT / 16; ++t)
+            acc[i][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+    int arow[MT / 16];
+#pragma unroll
+    for (int t = 0; t < MT / 16; ++t) {
+        const int m = t * 16 + r16;
+        arow[t] = (m < mrows ? m : mrows - 1) * RS + 4 * q;
+    }
+    const uint32_t* szrow = sz + (wave * 16 + r16) * gs;
+    const int glane = (32 * q) >> lg;             // this lane's group offset within a block
+    const int gmax = gs - 1;
 
+    for (int b0 = 0; b0 < nbp; b0 += P) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int p = 0; p < P; ++p) {
+            const int b = b0 + p;
+            // groups of the two pieces (padding blocks clamp to the last group;
+            // their activations are zero)
+            const int ga = min(((256 * b) >> lg) + glane, gmax);
+            const int gb = min(((256 * b + 128) >> lg) + glane, gmax);
+            const uint32_t ea = szrow[ga], eb = szrow[gb];
+            const h2_t zb[2] = {ql::zero_bias(ea >> 16), ql::zero_bias(eb >> 16)};
+            const h2_t s2[2] = {ql::scale2(ea & 0xFFFFu), ql::scale2(eb & 0xFFFFu)};
+            const uint32_t words[8] = {ring[p][0].x, ring[p][0].y, ring[p][0].z, ring[p][0].w,
+                                       ring[p][1].x, ring[p][1].y, ring[p][1].z, ring[p][1].w};
+            h8_t bw[8];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const h2_t zb = ql::zero_bias(zv[b][i]), s2 = ql::scale2(sv[b][i]);
-            const uint32_t words[4] = {wv[b][i].x, wv[b][i].y, wv[b][i].z, wv[b][i].w};
+            for (int j = 0; j < 8; ++j)
+                bw[j] = ql::dequant_word8(words[j], zb[j >> 2], s2[j >> 2]);
+            // Refill in place and in order.  Without the scheduling barriers the
+            // compiler sinks and regroups the refills, so waiting for one block
+            // means waiting for the whole ring.
+            const int nxt = b + P < nb ? b + P : nb - 1;
+            __builtin_amdgcn_sched_barrier(0);
+            load_block(nxt, ring[p][0], ring[p][1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const h8_t bw = ql::dequant_word8(words[j], zb, s2);
-                const int c = b * 32 + i * 16 + 4 * q + j;
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
                 for (int t = 0; t < MT / 16; ++t) {
-                    const int m = t * 16 + r16;
-                    h8_t a = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-                    if (m < M)
-                        a = __builtin_bit_cast(h8_t, xs[m * RS + c]);
-                    acc[t] = mfma16x16x32(a, bw, acc[t]);
+                    const int c = b * 32 + (j >> 2) * 16 + (j & 3);
+                    const h8_t af = __builtin_bit_cast(h8_t, xs[arow[t] + c]);
+                    acc[j & 3][t] = mfma16x16x32(af, bw[j], acc[j & 3][t]);
                 }
-            }
         }
+    }
+    f4_t res[MT / 16];
+#pragma unroll
+    for (int t = 0; t < MT / 16; ++t)
+        res[t] = (acc[0][t] + acc[1][t]) + (acc[2][t] + acc[3][t]);
 
     if (S == 1) {
 #pragma unroll
@@ -168,38 +247,38 @@ __global__ __launch_bounds__(64 * NT) void w4a16_decode_kernel(
             for (int r = 0; r < 4; ++r) {
                 const int m = t * 16 + 4 * q + r;
                 if (m < M && nok)
-                    y[(int64_t)m * N + n] = f32_to_f16_bits(acc[t][r]);
+                    y[(int64_t)m * N + n] = f32_to_f16_bits(res[t][r]);
             }
         return;
     }
 
-    // split-K: publish this slice's partial sums, the last arrival reduces
+    // 5. split-K: publish this slice's partial sums (agent scope), then arrive
 #pragma unroll
     for (int t = 0; t < MT / 16; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = t * 16 + 4 * q + r;
             if (m < M && nok)
-                part[((int64_t)blockIdx.y * M + m) * N + n] = acc[t][r];
+                __hip_atomic_store(&part[((int64_t)blockIdx.y * M + m) * N + n], res[t][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-    __threadfence();
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
+    __syncthreads();                    // ... and so have every other thread's
     if (threadIdx.x == 0) {
         const uint32_t prev =
-            __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(S - 1));
     }
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
-    const int nb0 = blockIdx.x * NT * 16;
-    for (int idx = threadIdx.x; idx < M * NT * 16; idx += 64 * NT) {
-        const int m = idx / (NT * 16), nn = nb0 + idx - m * (NT * 16);
+    for (int idx = threadIdx.x; idx < M * T * 16; idx += 64 * T) {
+        const int m = idx / (T * 16), nn = n0 + idx - m * (T * 16);
         if (nn < N) {
             float s = 0.f;
             for (int sl = 0; sl < S; ++sl)
-                s += __builtin_nontemporal_load(&part[((int64_t)sl * M + m) * N + nn]);
+                s += __hip_atomic_load(&part[((int64_t)sl * M + m) * N + nn], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             y[(int64_t)m * N + nn] = f32_to_f16_bits(s);
         }
     }
@@ -311,21 +390,54 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 struct DecodePlan {
     int mt;     // 16 or 32
-    int nb;     // 256-blocks per slice
+    int t;      // waves (16-channel tiles) per workgroup
+    int p;      // blocks in flight per wave
+    int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
-    size_t counter_bytes, part_offset, part_bytes;
+    size_t lds; // dynamic LDS bytes
+    size_t part_offset, part_bytes;
 };
 
-DecodePlan decode_plan(int64_t m, int64_t n, int64_t k)
+// The workspace starts with a fixed counter region that only ever holds
+// arrival counters (zero between calls); partial sums follow it.  A fixed
+// region keeps calls of different shapes from reading each other's partial
+// sums as counters when they share one workspace.
+constexpr size_t kCounterBytes = 32768;
+constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
+constexpr size_t kDecodeLdsBudget = 64 * 1024;   // staged activations + scales per workgroup
+constexpr int kDecodeWaveTarget = 2048;          // >= 8 streaming waves per CU
+
+// Tile choice.  Activations of one slice are staged per workgroup, so the
+// slice length is capped by m * ks * 2 <= 64 KiB; within that cap the slice is
+// as long as possible (fewer partial sums), but K is split further when the
+// column tiles alone give fewer than ~8 streaming waves per CU.
+DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
 {
     DecodePlan p{};
     p.mt = m <= 16 ? 16 : 32;
-    p.nb = p.mt == 16 ? 4 : 2;
-    p.slices = (int)((k + p.nb * 256 - 1) / (p.nb * 256));
-    p.nblk = (int)((n + kDecodeNT * 16 - 1) / (kDecodeNT * 16));
-    p.counter_bytes = (size_t)p.nblk * sizeof(uint32_t);
-    p.part_offset = (p.counter_bytes + 255) & ~(size_t)255;
+    p.t = 4;
+    p.nblk = (int)((n + p.t * 16 - 1) / (p.t * 16));
+    const int64_t rows = std::min<int64_t>(m, p.mt);
+    const int64_t kblocks = (k + 255) / 256;
+    const int64_t waves = (int64_t)p.nblk * p.t;
+    int64_t slices = waves >= kDecodeWaveTarget ? 1 : (kDecodeWaveTarget + waves - 1) / waves;
+    slices = std::min<int64_t>(slices, kblocks);
+    for (;; ++slices) {
+        const int64_t sblocks = (kblocks + slices - 1) / slices;
+        const int pd = sblocks % 4 == 0 ? 4 : 2;
+        const int64_t nbp = (sblocks + pd - 1) / pd * pd;
+        const int64_t gs = sblocks * 256 / group;
+        const size_t lds = (size_t)rows * (size_t)(nbp * 32 + 1) * 16 + (size_t)(16 * p.t * gs) * 4;
+        if (lds <= kDecodeLdsBudget || sblocks == 1) {
+            p.p = pd;
+            p.ks = (int)(sblocks * 256);
+            p.lds = lds;
+            break;
+        }
+    }
+    p.slices = (int)((k + p.ks - 1) / p.ks);
+    p.part_offset = kCounterBytes;
     p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)m * (size_t)n * sizeof(float) : 0;
     return p;
 }
@@ -341,8 +453,9 @@ int check_common(const void* qweight, const void* scales, const void* qzeros, in
         QL_FAIL(QL_ERR_GROUP, "%s: group %d not in {32, 64, 128}", who, group);
     if (n < 0 || k <= 0 || k % group)
         QL_FAIL(QL_ERR_SHAPE, "%s: n=%lld k=%lld group=%d", who, (long long)n, (long long)k, group);
-    if (n > (1LL << 30) || k > (1LL << 30) || n * (k / 8) > (1LL << 40))
-        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld k=%lld too large", who, (long long)n, (long long)k);
+    if (n > (1LL << 30) || k > (1LL << 30) || n * (k / 2) >= (1LL << 31))
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld k=%lld: packed weights must stay below 2 GiB", who, (long long)n,
+                (long long)k);
     if (!ql::aligned16(qweight) || !ql::aligned16(scales) || !ql::aligned16(qzeros))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
     return QL_OK;
@@ -356,14 +469,30 @@ int launch_status(const char* who)
     return QL_OK;
 }
 
-template <int MT, int NB>
-void launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
-                   const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int g, hipStream_t st)
+template <int MT, int T, int P>
+void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
+                     const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<MT, kDecodeNT, NB>), dim3(p.nblk, p.slices), dim3(64 * kDecodeNT), 0,
-                       st, x, qw, sc, qz, y, part, cnt, m, n, k, g);
+    hipLaunchKernelGGL((w4a16_decode_kernel<MT, T, P>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds, st, x, qw,
+                       sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+}
+
+// Exact dispatch on the plan; returns false for a combination that is not
+// instantiated.
+bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
+                   const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
+{
+#define QL_DECODE_CASE(MT_, T_, P_)                                                    \
+    if (p.mt == MT_ && p.t == T_ && p.p == P_) {                                       \
+        launch_decode_t<MT_, T_, P_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);        \
+        return true;                                                                   \
+    }
+    QL_DECODE_CASE(16, 4, 2) QL_DECODE_CASE(16, 4, 4)
+    QL_DECODE_CASE(32, 4, 2) QL_DECODE_CASE(32, 4, 4)
+#undef QL_DECODE_CASE
+    return false;
 }
 
 }  // namespace
@@ -373,7 +502,7 @@ extern "C" size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int 
     (void)group;
     if (m <= 0 || n <= 0 || k <= 0 || m > 32)
         return 0;
-    return decode_workspace(decode_plan(m, n, k));
+    return decode_workspace(decode_plan(m, n, k, group));
 }
 
 extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
@@ -407,17 +536,19 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     const int mi = (int)m, ni = (int)n, ki = (int)k;
 
     if (path == QL_PATH_DECODE) {
-        DecodePlan p = decode_plan(m, n, k);
+        DecodePlan p = decode_plan(m, n, k, group);
+        if (p.slices > 1 && p.nblk > kMaxDecodeBlocks)
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld exceeds the decode path's %d column blocks", who, (long long)n,
+                    kMaxDecodeBlocks);
         const size_t need = decode_workspace(p);
         if (need > 0 && (!workspace || workspace_bytes < need))
             QL_FAIL(QL_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
                     workspace ? workspace_bytes : (size_t)0);
         if (need > 0 && !ql::aligned16(workspace))
             QL_FAIL(QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
-        if (p.mt == 16)
-            launch_decode<16, 4>(p, xw, qw, scales, qz, y, workspace, mi, ni, ki, group, st);
-        else
-            launch_decode<32, 2>(p, xw, qw, scales, qz, y, workspace, mi, ni, ki, group, st);
+        const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
+        if (!launch_decode(p, xw, qw, scales, qz, y, workspace, mi, ni, ki, lg, st))
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d t=%d p=%d", who, p.mt, p.t, p.p);
         return launch_status(who);
     }
     dim3 grid((unsigned)((n + kGemmBN - 1) / kGemmBN), (unsigned)((m + kGemmBM - 1) / kGemmBM));

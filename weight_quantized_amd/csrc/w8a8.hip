@@ -92,6 +92,34 @@ __device__ float mean_from_exact(U128 v, uint32_t k)
     return ldexpf((float)mant, drop + d - 48);
 }
 
+// Correctly rounded square root of a non-negative finite float.  The hardware
+// estimate is within an ulp or so; it is then moved to the float whose
+// rounding interval contains sqrt(x).  The boundary between two neighbouring
+// floats c < c' is their midpoint m, which has at most 25 significant bits, so
+// m*m is exact in fp64 and "sqrt(x) < m" is decided exactly by "x < m*m".
+// (sqrt(x) never equals such a midpoint for a float x.)
+__device__ float sqrt_rn(float x)
+{
+    if (!(x > 0.0f))
+        return x == 0.0f ? x : __builtin_nanf("");
+    float c = sqrtf(x);
+    const double xd = (double)x;
+#pragma unroll 1
+    for (int it = 0; it < 4; ++it) {
+        const float lo = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c) - 1u);
+        const float hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c) + 1u);
+        const double mlo = 0.5 * ((double)c + (double)lo);
+        const double mhi = 0.5 * ((double)c + (double)hi);
+        if (xd < mlo * mlo)
+            c = lo;
+        else if (xd > mhi * mhi)
+            c = hi;
+        else
+            break;
+    }
+    return c;
+}
+
 template <int NT>
 __device__ __forceinline__ U128 block_sum128(U128 v, U128* sh)
 {
@@ -158,7 +186,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     }
     const U128 tot = block_sum128<kNormThreads>(acc, s_sum);
     const float ms = mean_from_exact(tot, (uint32_t)K);
-    const float r = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(ms, eps)));
+    const float r = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
 
     float amax = 0.0f;
     for (int c = threadIdx.x; c < nch; c += kNormThreads) {
