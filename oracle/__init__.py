@@ -51,6 +51,7 @@ def _load():
         "or_w8a8_forward": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
         "or_sumsq_exact": (None, [_p, _i64, _p, _p]),
         "or_ratio_to_f32_parts": (C.c_float, [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int]),
+        "or_num_threads": (C.c_int, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -275,6 +276,11 @@ def w8a8_forward(xq, x_scale, wq, w_scale, rows=None, cols=None):
     _check(lib.or_w8a8_forward(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(r), nr, _ptr(c), nc,
                                _ptr(y)), "w8a8_forward")
     return y
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().or_num_threads())
 
 
 def sumsq_exact(x_row):

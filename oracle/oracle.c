@@ -43,6 +43,7 @@
  * Built with -ffp-contract=off so every fp32 operation rounds on its own.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -506,6 +507,9 @@ int or_w8a8_forward(const int8_t* xq, const float* x_scale, int64_t m, const int
     free(acc);
     return OR_OK;
 }
+
+/* Threads the OpenMP loops of this file use. */
+int or_num_threads(void) { return omp_get_max_threads(); }
 
 /* Exposed for the pins: exact sum of squares as (hi, lo) 64-bit halves. */
 void or_sumsq_exact(const uint16_t* x, int64_t k, uint64_t* hi, uint64_t* lo)

@@ -173,6 +173,40 @@ def test_decode_shared_workspace_across_shapes(ql):
     assert not ws[:32768].cpu().numpy().any()
 
 
+def test_decode_graph_replays_match_eager(ql):
+    """Split-K decode launches captured in a HIP graph: every replay, with eager
+    work and synchronisation in between, reproduces the eager result exactly
+    (the arrival counters reset themselves; no memset nodes are involved)."""
+    group = 128
+    rng = np.random.default_rng(8)
+    cases = [(1, 4096, 4096), (16, 4096, 11008)]
+    need = max(ql.w4a16_workspace_bytes(m, n, k, group) for m, n, k in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    data = []
+    for m, n, k in cases:
+        w = workloads.weight(rng, n, k)
+        _, d = pack_dev(ql, w, group)
+        x = dev(workloads.activations(rng, m, k))
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda:0")
+        data.append((x, d, y))
+    eager = [ql.w4a16_gemm(x, *d, group, workspace=ws, path=1).clone() for x, d, _ in data]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, d, y in data:
+            ql.w4a16_gemm(x, *d, group, out=y, workspace=ws, path=1)
+    for rep in range(4):
+        for _, _, y in data:
+            y.fill_(float("nan"))
+        ql.w4a16_gemm(data[0][0], *data[0][1], group, workspace=ws, path=1)   # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, (_, _, y) in zip(eager, data):
+            assert torch.equal(e, y), rep
+    assert not ws[:32768].cpu().numpy().any()
+
+
 # ------------------------------------------------------------------ full-size configurations
 def _config_case(ql, name, m, group, seed=0, rows_seed=0):
     w = workloads.config_weight(name, seed=seed)
