@@ -64,7 +64,13 @@ def test_quant_rmsnorm_edge_rows(ql):
         assert np.array_equal(xq.cpu().numpy(), oq), eps
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 64, 16), (5, 64, 128), (130, 200, 4096), (64, 128, 1040), (257, 33, 512)])
+# Shapes reach: one k-tile and fewer k-tiles than pipeline stages (64, 192),
+# a k-tile count that is not a multiple of the stage count (448 = 7 tiles),
+# exactly one full 256x128 tile, ragged m and n, n % 4 != 0 (element stores),
+# and k % 64 != 0 (the register-staged kernel: 16, 1040).
+@pytest.mark.parametrize("m,n,k", [(1, 64, 16), (5, 64, 128), (130, 200, 4096), (64, 128, 1040), (257, 33, 512),
+                                   (256, 128, 64), (300, 260, 192), (64, 128, 448), (512, 256, 640),
+                                   (511, 130, 4096)])
 def test_gemm_i32_bit_exact_small(ql, m, n, k):
     rng = np.random.default_rng(m + n + k)
     xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
@@ -123,3 +129,21 @@ def test_config_smoothquant_pipeline(ql):
     got = y.cpu().numpy()
     assert np.isfinite(got).all()
     assert rel_err(got[np.ix_(rows, cols)], oy) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 128, 4096), (300, 260, 1040), (2048, 512, 4096)])
+def test_gemm_fp16_epilogue_rounding(ql, m, n, k):
+    """The fp16 epilogue rounds (float)acc * x_scale to fp32, that times
+    w_scale to fp32, then once to fp16 (round to nearest even); checked bit
+    for bit from the oracle's exact int32 accumulator."""
+    rng = np.random.default_rng(7 * m + n)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    xs = rng.uniform(1e-3, 1e-1, m).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    y = ql.w8a8_gemm(dev(xq), dev(xs), dev(wq), dev(ws))
+    torch.cuda.synchronize()
+    acc = oracle.int8_gemm(xq, wq).astype(np.float32)
+    want = ((acc * xs[:, None]).astype(np.float32) * ws[None, :]).astype(np.float32).astype(np.float16)
+    got = y.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))

@@ -287,100 +287,164 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GEMM: block tile 128 (m) x 128 (n), 4 waves as 2 x 2, wave tile 64 x 64.
-// K advances in super-steps of 128.  The activation tile goes through LDS in
-// the dequantiser's element order; each wave streams its own 64 weight rows
-// straight into registers (one 16-byte piece per lane and 16-row tile per
-// super-step) and dequantises them there.
+// GEMM (m > 32): block tile BM x BN, K advanced in tiles of 64, 4 waves as
+// 2 x 2 (wave tile BM/2 x BN/2), MFMA f32 16x16x32 f16.
+//
+// Per k-tile the activations (BM rows x 64 k, 128 contiguous bytes per row)
+// and the packed weights (BN rows x 8 words) are fetched into registers while
+// the previous tile is multiplied.  The weights are dequantised by the shared
+// routine as they are written to LDS, once per workgroup, so every wave reads
+// both operands as fp16 fragments in the dequantiser's element order.  LDS is
+// double-buffered, rows padded to 144 bytes against bank conflicts.  Tiles are
+// ordered per XCD as in the int8 GEMM.
 // ---------------------------------------------------------------------------
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 128;
+constexpr int kGBK = 64;                  // k per tile
+constexpr int kGRow = kGBK * 2 + 16;      // padded LDS row (bytes)
+constexpr int kXcds = 8;
 
+__device__ __forceinline__ int xcd_tile(int wg, int ntiles)
+{
+    const int per = (ntiles + kXcds - 1) / kXcds;
+    return (wg % kXcds) * per + wg / kXcds;
+}
+
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restrict__ x,
                                                          const uint32_t* __restrict__ qw,
                                                          const uint16_t* __restrict__ sc,
                                                          const uint32_t* __restrict__ qz,
-                                                         uint16_t* __restrict__ y, int M, int N, int K, int G)
+                                                         uint16_t* __restrict__ y, int M, int N, int K, int lg)
 {
-    constexpr int CH = kGemmBK / 8;      // 16 chunks per row per super-step
-    constexpr int RS = CH + 1;           // padded LDS row stride (uint4)
-    __shared__ uint4 as[kGemmBM * RS];
+    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int FI = TM / 16, FJ = TN / 16;
+    constexpr int ACH = BM * (kGBK / 8) / 256;         // activation 16-byte chunks per thread per tile
+    constexpr int BCH = (BN * 2 + 255) / 256;          // packed 16-byte pieces per thread (2 per row)
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * kGRow];
+    uint8_t* const As = lds;
+    uint8_t* const Bs = lds + 2 * BM * kGRow;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    const int tile = xcd_tile(blockIdx.x, tm * tn);
+    if (tile >= tm * tn)
+        return;
+    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int q = lane >> 4, r16 = lane & 15;
-    const int m0 = blockIdx.y * kGemmBM, n0 = blockIdx.x * kGemmBN;
-    const int KW = K >> 3, NG = K / G, ZW = (NG + 7) >> 3;
+    const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
 
-    int nrow[4];
-    bool nok[4];
+    uint4 ra[ACH], rb[BCH];
+    uint32_t rs[BCH], rz[BCH];
+    auto fetch = [&](int kb) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int n = n0 + wn * 64 + t * 16 + r16;
-        nok[t] = n < N;
-        nrow[t] = nok[t] ? n : 0;
-    }
-
-    f4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb = 0; kb < K; kb += kGemmBK) {
-        const int nch = min(CH, (K - kb) >> 3);
-        // weights of this super-step (issued first: the longest latency)
-        uint4 wv[4];
-        uint32_t sv[4], zv[4];
-        const int kk = kb + 32 * q;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool ok = nok[t] && kk < K;
-            wv[t] = ok ? *reinterpret_cast<const uint4*>(qw + (int64_t)nrow[t] * KW + (kk >> 3))
-                       : make_uint4(0u, 0u, 0u, 0u);
-            const int g = kk / G;
-            sv[t] = ok ? sc[(int64_t)nrow[t] * NG + g] : 0u;
-            zv[t] = ok ? ql::zero_of(qz + (int64_t)nrow[t] * ZW, g) : 0u;
+        for (int u = 0; u < ACH; ++u) {
+            const int c = tid + u * 256;
+            const int row = c >> 3, col = (c & 7) * 8;
+            const int m = m0 + row, k = kb + col;
+            const bool ok = m < M && k < K;
+            ra[u] = *reinterpret_cast<const uint4*>(x + (int64_t)(ok ? m : 0) * K + (ok ? k : 0));
+            if (!ok)
+                ra[u] = make_uint4(0u, 0u, 0u, 0u);
         }
-        // activation tile -> LDS
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kGemmBM * CH; idx += 256) {
-            const int r = idx / CH, c = idx - r * CH;
-            const int m = m0 + r;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M && c < nch)
-                v = ql::permute_x8(*reinterpret_cast<const uint4*>(x + (int64_t)m * K + kb + 8 * c));
-            as[r * RS + c] = v;
-        }
-        __syncthreads();
-
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const h2_t zb = ql::zero_bias(zv[t]), s2 = ql::scale2(sv[t]);
-            const uint32_t words[4] = {wv[t].x, wv[t].y, wv[t].z, wv[t].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const h8_t bw = ql::dequant_word8(words[j], zb, s2);
-                const int c = 4 * q + j;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const h8_t a = __builtin_bit_cast(h8_t, as[(wm * 64 + i * 16 + r16) * RS + c]);
-                    acc[i][t] = mfma16x16x32(a, bw, acc[i][t]);
-                }
+        for (int u = 0; u < BCH; ++u) {
+            const int c = tid + u * 256;
+            const int row = c >> 1, k = kb + (c & 1) * 32;
+            const int n = n0 + row;
+            const bool ok = row < BN && n < N && k < K;
+            const int nn = ok ? n : 0, kk = ok ? k : 0;
+            rb[u] = *reinterpret_cast<const uint4*>(qw + (int64_t)nn * KW + (kk >> 3));
+            const int g = kk >> lg;
+            rs[u] = sc[(int64_t)nn * NG + g];
+            rz[u] = qz[(int64_t)nn * ZW + (g >> 3)] >> (4 * (g & 7));
+            if (!ok) {
+                rb[u] = make_uint4(0u, 0u, 0u, 0u);
+                rs[u] = 0u;
+                rz[u] = 0u;
             }
         }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) {
+            const int c = tid + u * 256;
+            *reinterpret_cast<uint4*>(As + buf * BM * kGRow + (c >> 3) * kGRow + (c & 7) * 16) =
+                ql::permute_x8(ra[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < BCH; ++u) {
+            const int c = tid + u * 256;
+            const int row = c >> 1;
+            if (row < BN) {
+                const h2_t zb = ql::zero_bias(rz[u] & 0xFu), s2 = ql::scale2(rs[u]);
+                const uint32_t words[4] = {rb[u].x, rb[u].y, rb[u].z, rb[u].w};
+                uint8_t* dst = Bs + buf * BN * kGRow + row * kGRow + (c & 1) * 64;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<h8_t*>(dst + j * 16) = ql::dequant_word8(words[j], zb, s2);
+            }
+        }
+    };
+
+    f4_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (K + kGBK - 1) / kGBK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk)
+            fetch((kt + 1) * kGBK);
+        const uint8_t* a_base = As + buf * BM * kGRow + (wm * TM + r16) * kGRow + q * 16;
+        const uint8_t* b_base = Bs + buf * BN * kGRow + (wn * TN + r16) * kGRow + q * 16;
+#pragma unroll
+        for (int s2 = 0; s2 < kGBK / 32; ++s2) {
+            h8_t af[FI], bf[FJ];
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+                af[i] = *reinterpret_cast<const h8_t*>(a_base + i * 16 * kGRow + s2 * 64);
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                bf[j] = *reinterpret_cast<const h8_t*>(b_base + j * 16 * kGRow + s2 * 64);
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+                    acc[i][j] = mfma16x16x32(bf[j], af[i], acc[i][j]);
+        }
+        if (kt + 1 < nk)
+            stash(buf ^ 1);
+        __syncthreads();
     }
 
+    // The weight fragment is the MFMA's A operand, so fragment (i, j) is the
+    // transposed product: lane (q, r16) holds y[m][n .. n+3], four consecutive
+    // outputs of one row.
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int n = n0 + wn * 64 + t * 16 + r16;
+        for (int j = 0; j < FJ; ++j) {
+            const int m = m0 + wm * TM + i * 16 + r16;
+            const int n = n0 + wn * TN + j * 16 + 4 * q;
+            if (vec) {
+                uint2 h;
+                h.x = f32_to_f16_bits(acc[i][j][0]) | ((uint32_t)f32_to_f16_bits(acc[i][j][1]) << 16);
+                h.y = f32_to_f16_bits(acc[i][j][2]) | ((uint32_t)f32_to_f16_bits(acc[i][j][3]) << 16);
+                *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = h;
+            } else if (m < M) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * q + r;
-                if (m < M && n < N)
-                    y[(int64_t)m * N + n] = f32_to_f16_bits(acc[i][t][r]);
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        y[(int64_t)m * N + n + r] = f32_to_f16_bits(acc[i][j][r]);
             }
         }
 }
@@ -551,8 +615,13 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
             QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d t=%d p=%d", who, p.mt, p.t, p.p);
         return launch_status(who);
     }
-    dim3 grid((unsigned)((n + kGemmBN - 1) / kGemmBN), (unsigned)((m + kGemmBM - 1) / kGemmBM));
-    hipLaunchKernelGGL(w4a16_gemm_kernel, grid, dim3(256), 0, st, xw, qw, scales, qz, y, mi, ni, ki, group);
+    const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
+    // 128 x 192 tiles: M=512, N=12288 gives exactly one tile per CU
+    constexpr int BM = 128, BN = 192;
+    const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN>), dim3((unsigned)grid), dim3(256), 0, st, xw, qw, scales, qz, y,
+                       mi, ni, ki, lg);
     return launch_status(who);
 }
 

@@ -9,6 +9,8 @@
 //                           linear_scale)
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <algorithm>
 #include <cstdint>
 
@@ -229,96 +231,386 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
 }
 
 // ---------------------------------------------------------------------------
-// int8 GEMM: block tile 128 x 128, BK = 128, 4 waves as 2 x 2 (64 x 64 each),
-// MFMA i32 16x16x64 i8.  Lane l supplies A[l%16][16(l/16) .. +15] and
-// B[16(l/16) .. +15][l%16] (row l%16 of wq) and receives D[4(l/16)+r][l%16].
+// int8 GEMM.  Block tile BM x BN, K advanced in tiles of 128 bytes, 4 waves as
+// 2 x 2 (wave tile BM/2 x BN/2), MFMA i32 16x16x64 i8.  Lane l supplies
+// A[l%16][16(l/16) .. +15] and B[16(l/16) .. +15][l%16] (row l%16 of wq) and
+// receives D[4(l/16)+r][l%16].
+//
+// Both operands are K-major, so a k-tile of either is BM (BN) rows of 128
+// contiguous bytes: every global load fetches whole 128-byte lines.  Tiles are
+// double-buffered in LDS; the next k-tile is fetched into registers while the
+// current one is multiplied, then written to the other buffer.  LDS rows are
+// padded to 144 bytes so the 16 rows of an MFMA fragment read fall in
+// distinct banks.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2); the tile order below gives every XCD a contiguous run of tiles that
+// sweeps N for one M block, so that block of A stays in that XCD's L2.
 // ---------------------------------------------------------------------------
-constexpr int kQBM = 128, kQBN = 128, kQBK = 128;
+constexpr int kQBK = 128;                 // k bytes per tile
+constexpr int kQRow = kQBK + 16;          // padded LDS row (bytes)
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ i4_t mfma_i8(i4_t a, i4_t b, i4_t c)
 {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-template <bool kRaw>
+// tile index of workgroup `wg` so that each XCD gets a contiguous run of tiles
+__device__ __forceinline__ int xcd_tile(int wg, int ntiles)
+{
+    const int per = (ntiles + kXcds - 1) / kXcds;
+    const int t = (wg % kXcds) * per + wg / kXcds;
+    return t;
+}
+
+// Epilogue of both int8 GEMM kernels.  The MFMA takes the weight fragment as
+// its A operand and the activation fragment as B, so fragment (i, j) holds the
+// transposed product: lane (q, r16) has y[m][n .. n+3] with m = mrow + 16 i,
+// n = ncol + 16 j, mrow = tile row of r16, ncol = tile column 4 q, i.e. four
+// consecutive outputs of one row (one 8-byte fp16 or 16-byte int32 store).
+// Every scale is loaded first at a clamped index so the loads are in flight
+// together.  `vec`: the whole tile is in bounds and rows are 4-aligned.
+template <int FI, int FJ, bool kRaw>
+__device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const float* __restrict__ xs,
+                                           const float* __restrict__ ws, void* __restrict__ out, int M, int N,
+                                           int mrow, int ncol, bool vec)
+{
+    float xsv[FI], wsv[FJ][4];
+    if (!kRaw) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+            xsv[i] = xs[min(mrow + 16 * i, M - 1)];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                wsv[j][r] = ws[min(ncol + 16 * j + r, N - 1)];
+    }
+    // y = fp16(fp32(fp32(acc * x_scale) * w_scale)): each product rounded to
+    // fp32, then one rounding to fp16 (the empty asm keeps the conversion
+    // from being fused with the product into a single rounding)
+    auto to_h = [&](int i, int j, int r) -> uint32_t {
+        float v = __fmul_rn(__fmul_rn((float)acc[i][j][r], xsv[i]), wsv[j][r]);
+        asm volatile("" : "+v"(v));
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    };
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const int64_t o = (int64_t)(mrow + 16 * i) * N + ncol + 16 * j;
+                if (kRaw) {
+                    *reinterpret_cast<i4_t*>(static_cast<int32_t*>(out) + o) = acc[i][j];
+                } else {
+                    uint2 h;
+                    h.x = to_h(i, j, 0) | (to_h(i, j, 1) << 16);
+                    h.y = to_h(i, j, 2) | (to_h(i, j, 3) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = h;
+                }
+            }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+        const int m = mrow + 16 * i;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int n = ncol + 16 * j + r;
+                if (n >= N)
+                    continue;
+                if (kRaw)
+                    static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][r];
+                else
+                    static_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)to_h(i, j, r);
+            }
+    }
+}
+
+template <int BM, int BN, bool kRaw>
 __global__ __launch_bounds__(256) void w8a8_gemm_kernel(const int8_t* __restrict__ xq,
                                                         const float* __restrict__ xs,
                                                         const int8_t* __restrict__ wq,
                                                         const float* __restrict__ ws, void* __restrict__ out,
                                                         int M, int N, int K)
 {
-    constexpr int CH = kQBK / 16;        // 16-byte chunks per row per step
-    constexpr int RS = CH + 1;           // padded row stride (uint4)
-    __shared__ uint4 at[kQBM * RS];
-    __shared__ uint4 bt[kQBN * RS];
+    constexpr int TM = BM / 2, TN = BN / 2;           // wave tile
+    constexpr int FI = TM / 16, FJ = TN / 16;          // MFMA tiles per wave
+    constexpr int ACH = BM * (kQBK / 16) / 256;        // A 16-byte chunks per thread per tile
+    constexpr int BCH = BN * (kQBK / 16) / 256;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * kQRow];
+    uint8_t* const As = lds;
+    uint8_t* const Bs = lds + 2 * BM * kQRow;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    const int tile = xcd_tile(blockIdx.x, tm * tn);
+    if (tile >= tm * tn)
+        return;
+    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int q = lane >> 4, r16 = lane & 15;
-    const int m0 = blockIdx.y * kQBM, n0 = blockIdx.x * kQBN;
 
-    i4_t acc[4][4];
+    // global -> register staging of one k-tile
+    uint4 ra[ACH], rb[BCH];
+    auto fetch = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < ACH; ++u) {
+            const int c = tid + u * 256;
+            const int row = c >> 3, col = (c & 7) * 16;
+            const int m = m0 + row, k = kb + col;
+            const bool ok = m < M && k < K;
+            ra[u] = *reinterpret_cast<const uint4*>(xq + (int64_t)(ok ? m : 0) * K + (ok ? k : 0));
+            if (!ok)
+                ra[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int u = 0; u < BCH; ++u) {
+            const int c = tid + u * 256;
+            const int row = c >> 3, col = (c & 7) * 16;
+            const int n = n0 + row, k = kb + col;
+            const bool ok = n < N && k < K;
+            rb[u] = *reinterpret_cast<const uint4*>(wq + (int64_t)(ok ? n : 0) * K + (ok ? k : 0));
+            if (!ok)
+                rb[u] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < ACH; ++u) {
+            const int c = tid + u * 256;
+            *reinterpret_cast<uint4*>(As + buf * BM * kQRow + (c >> 3) * kQRow + (c & 7) * 16) = ra[u];
+        }
+#pragma unroll
+        for (int u = 0; u < BCH; ++u) {
+            const int c = tid + u * 256;
+            *reinterpret_cast<uint4*>(Bs + buf * BN * kQRow + (c >> 3) * kQRow + (c & 7) * 16) = rb[u];
+        }
+    };
+
+    i4_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
             acc[i][j] = i4_t{0, 0, 0, 0};
 
-    for (int kb = 0; kb < K; kb += kQBK) {
-        const int nch = min(CH, (K - kb) >> 4);
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < kQBM * CH; idx += 256) {
-            const int r = idx / CH, c = idx - r * CH;
-            const int m = m0 + r, n = n0 + r;
-            uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M && c < nch)
-                va = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + kb + 16 * c);
-            if (n < N && c < nch)
-                vb = *reinterpret_cast<const uint4*>(wq + (int64_t)n * K + kb + 16 * c);
-            at[r * RS + c] = va;
-            bt[r * RS + c] = vb;
-        }
-        __syncthreads();
+    const int nk = (K + kQBK - 1) / kQBK;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk)
+            fetch((kt + 1) * kQBK);
+        const uint8_t* a_base = As + buf * BM * kQRow + (wm * TM + r16) * kQRow + q * 16;
+        const uint8_t* b_base = Bs + buf * BN * kQRow + (wn * TN + r16) * kQRow + q * 16;
 #pragma unroll
         for (int s = 0; s < kQBK / 64; ++s) {
-            const int c = 4 * s + q;
-            i4_t af[4], bf[4];
+            i4_t af[FI], bf[FJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = __builtin_bit_cast(i4_t, at[(wm * 64 + i * 16 + r16) * RS + c]);
+            for (int i = 0; i < FI; ++i)
+                af[i] = *reinterpret_cast<const i4_t*>(a_base + i * 16 * kQRow + s * 64);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = __builtin_bit_cast(i4_t, bt[(wn * 64 + j * 16 + r16) * RS + c]);
+            for (int j = 0; j < FJ; ++j)
+                bf[j] = *reinterpret_cast<const i4_t*>(b_base + j * 16 * kQRow + s * 64);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = mfma_i8(af[i], bf[j], acc[i][j]);
+                for (int j = 0; j < FJ; ++j)
+                    acc[i][j] = mfma_i8(bf[j], af[i], acc[i][j]);
         }
+        if (kt + 1 < nk)
+            stash(buf ^ 1);
+        __syncthreads();
     }
 
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + r16;
-        if (n >= N)
-            continue;
-        const float wsn = kRaw ? 0.0f : ws[n];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + i * 16 + 4 * q + r;
-                if (m >= M)
-                    continue;
-                if (kRaw) {
-                    static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][r];
-                } else {
-                    const float v = __fmul_rn(__fmul_rn((float)acc[i][j][r], xs[m]), wsn);
-                    static_cast<uint16_t*>(out)[(int64_t)m * N + n] = __builtin_bit_cast(uint16_t, (_Float16)v);
-                }
-            }
-    }
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
+    store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
 }
+
+constexpr int kQBM = 256, kQBN = 128;
+
+// ---------------------------------------------------------------------------
+// int8 GEMM, pipelined (K % 64 == 0).  Same tiles and MFMA as above, but the
+// operands go straight from global memory into a ring of LDS stages with the
+// gfx950 direct global->LDS load (16 bytes per lane; a wave's 64 lanes fill
+// 1 KB of LDS contiguously).  STAGES-1 k-tiles are in flight while one is
+// multiplied, without holding them in registers.
+//
+// The loads and the stage handshake are written in inline assembly: the
+// compiler does not track which LDS stage a direct load fills and would wait
+// for every outstanding load before any LDS read, serialising the ring.  Here
+// each wave waits (vmcnt) only for its own loads of the stage about to be read,
+// then a barrier makes every wave's part of that stage visible.
+//
+// LDS rows are 64 bytes (4 chunks of 16).  Logical chunk c of tile row r sits
+// at chunk c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16 rows of an
+// MFMA fragment read land in 16 distinct bank groups.
+// ---------------------------------------------------------------------------
+constexpr int kPBK = 64;                                   // k bytes per stage
+constexpr int kPStages = 6;
+constexpr int kPStageBytes = (kQBM + kQBN) * kPBK;         // 24 KiB
+constexpr int kPDmaPerWave = (kQBM + kQBN) * kPBK / 1024 / 4;   // 1 KiB loads per wave per stage
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// one direct load: each lane's 16 bytes at `src` -> LDS `lds_base` + 16 * lane
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
+{
+    asm volatile("global_load_lds_dwordx4 %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
+}
+
+// wait until at most N of this wave's vector-memory operations are pending,
+// then synchronise the workgroup; a compiler barrier for memory accesses
+template <int N>
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <bool kRaw>
+__global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
+                                                             const float* __restrict__ xs,
+                                                             const int8_t* __restrict__ wq,
+                                                             const float* __restrict__ ws, void* __restrict__ out,
+                                                             int M, int N, int K)
+{
+    constexpr int BM = kQBM, BN = kQBN;
+    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int FI = TM / 16, FJ = TN / 16;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // kPStages * kPStageBytes
+
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    const int tile = xcd_tile(blockIdx.x, tm * tn);
+    if (tile >= tm * tn)
+        return;
+    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int q = lane >> 4, r16 = lane & 15;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
+
+    // This wave's direct loads: the stage is (BM + BN) rows of 64 bytes, i.e.
+    // 24 blocks of 16 rows (1 KiB each); wave w fills blocks w, w+4, ..., w+20.
+    // Lane l of a block writes physical chunk l&3 of row l>>2 and so reads
+    // logical chunk (l&3) ^ swz(row).  Rows past M or N re-read the last row.
+    const uint8_t* src[kPDmaPerWave];
+    uint32_t dst[kPDmaPerWave];
+#pragma unroll
+    for (int u = 0; u < kPDmaPerWave; ++u) {
+        const int blk = wave + 4 * u;                  // 0..23
+        const int row = blk * 16 + (lane >> 2);        // stage row 0..383
+        const int c = (lane & 3) ^ swz(row);
+        if (row < BM) {
+            const int m = min(m0 + row, M - 1);
+            src[u] = reinterpret_cast<const uint8_t*>(xq) + (int64_t)m * K + 16 * c;
+        } else {
+            const int n = min(n0 + row - BM, N - 1);
+            src[u] = reinterpret_cast<const uint8_t*>(wq) + (int64_t)n * K + 16 * c;
+        }
+        dst[u] = (uint32_t)(blk * 1024);
+    }
+    auto issue = [&](int kt, int slot) {
+#pragma unroll
+        for (int u = 0; u < kPDmaPerWave; ++u)
+            dma16(src[u] + (int64_t)kt * kPBK,
+                  (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * kPStageBytes + dst[u]));
+    };
+
+    i4_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            acc[i][j] = i4_t{0, 0, 0, 0};
+
+    const int nk = K / kPBK;
+    // prologue: stages 0 .. STAGES-2 in flight (past the end, reload the last tile)
+#pragma unroll
+    for (int s = 0; s < kPStages - 1; ++s)
+        issue(s < nk ? s : nk - 1, s);
+
+    // fragment addresses within a stage (row-relative, swizzled chunk)
+    const int arow0 = wm * TM + r16, brow0 = BM + wn * TN + r16;
+    for (int kt0 = 0; kt0 < nk; kt0 += kPStages) {
+#pragma unroll
+        for (int s = 0; s < kPStages; ++s) {
+            const int kt = kt0 + s;
+            if (kt < nk) {
+                // stage s holds tile kt; (STAGES-2) younger stages stay in flight
+                stage_barrier<kPDmaPerWave * (kPStages - 2)>();
+                // refill the slot read in the previous iteration with tile kt + STAGES - 1
+                const int nt = kt + kPStages - 1;
+                issue(nt < nk ? nt : nk - 1, (s + kPStages - 1) % kPStages);
+                const uint8_t* base = pl + s * kPStageBytes;
+                i4_t af[FI], bf[FJ];
+#pragma unroll
+                for (int i = 0; i < FI; ++i) {
+                    const int r = arow0 + 16 * i;
+                    af[i] = *reinterpret_cast<const i4_t*>(base + r * kPBK + 16 * (q ^ swz(r)));
+                }
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) {
+                    const int r = brow0 + 16 * j;
+                    bf[j] = *reinterpret_cast<const i4_t*>(base + r * kPBK + 16 * (q ^ swz(r)));
+                }
+#pragma unroll
+                for (int i = 0; i < FI; ++i)
+#pragma unroll
+                    for (int j = 0; j < FJ; ++j)
+                        acc[i][j] = mfma_i8(bf[j], af[i], acc[i][j]);
+            }
+        }
+    }
+    stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
+
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
+    store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
+}
+
+// The pipelined kernel needs kPStages * kPStageBytes of LDS per workgroup
+// (gfx950 allows 160 KiB); queried once per device.
+bool pipe_lds_fits()
+{
+    static std::atomic<int> known[64];   // 0 unknown, 1 fits, 2 does not
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return false;
+    int v = known[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int lds = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            lds = 0;
+        v = lds >= kPStages * kPStageBytes ? 1 : 2;
+        known[dev].store(v, std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
+template <bool kRaw>
+void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, void* out, int64_t m,
+                      int64_t n, int64_t k, hipStream_t st)
+{
+    const int64_t tiles = ((n + kQBN - 1) / kQBN) * ((m + kQBM - 1) / kQBM);
+    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;   // whole rounds over the XCDs
+    if (k % kPBK == 0 && pipe_lds_fits())
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<kRaw>), dim3((unsigned)grid), dim3(256),
+                           (size_t)kPStages * kPStageBytes, st, xq, xs, wq, ws, out, (int)m, (int)n, (int)k);
+    else
+        hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3((unsigned)grid), dim3(256), 0, st, xq, xs, wq,
+                           ws, out, (int)m, (int)n, (int)k);
+}
+
 
 int launch_status(const char* who)
 {
@@ -382,9 +674,7 @@ extern "C" int ql_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
     if (!ql::aligned16(x_scale) || !ql::aligned16(w_scale))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
-    dim3 grid((unsigned)((n + kQBN - 1) / kQBN), (unsigned)((m + kQBM - 1) / kQBM));
-    hipLaunchKernelGGL(w8a8_gemm_kernel<false>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), xq, x_scale,
-                       wq, w_scale, (void*)y, (int)m, (int)n, (int)k);
+    launch_w8a8_gemm<false>(xq, x_scale, wq, w_scale, (void*)y, m, n, k, static_cast<hipStream_t>(stream));
     return launch_status(who);
 }
 
@@ -397,8 +687,6 @@ extern "C" int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc
         return rc;
     if (m == 0 || n == 0)
         return QL_OK;
-    dim3 grid((unsigned)((n + kQBN - 1) / kQBN), (unsigned)((m + kQBM - 1) / kQBM));
-    hipLaunchKernelGGL(w8a8_gemm_kernel<true>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), xq, nullptr,
-                       wq, nullptr, (void*)acc, (int)m, (int)n, (int)k);
+    launch_w8a8_gemm<true>(xq, nullptr, wq, nullptr, (void*)acc, m, n, k, static_cast<hipStream_t>(stream));
     return launch_status(who);
 }
