@@ -439,28 +439,37 @@ __global__ __launch_bounds__(256) void w8a8_gemm_kernel(const int8_t* __restrict
 constexpr int kQBM = 256, kQBN = 128;
 
 // ---------------------------------------------------------------------------
-// int8 GEMM, pipelined (K % 64 == 0).  Same tiles and MFMA as above, but the
-// operands go straight from global memory into a ring of LDS stages with the
-// gfx950 direct global->LDS load (16 bytes per lane; a wave's 64 lanes fill
-// 1 KB of LDS contiguously).  STAGES-1 k-tiles are in flight while one is
-// multiplied, without holding them in registers.
+// int8 GEMM, pipelined (K % BK == 0).  The same 2x2-wave MFMA tiling as above,
+// but the operands go straight from global memory into a ring of S LDS stages
+// with the gfx950 direct global->LDS load (16 bytes per lane; a wave's 64
+// lanes fill 1 KiB of LDS contiguously), so up to S-1 k-tiles are in flight
+// without holding them in registers.
 //
-// The loads and the stage handshake are written in inline assembly: the
-// compiler does not track which LDS stage a direct load fills and would wait
-// for every outstanding load before any LDS read, serialising the ring.  Here
-// each wave waits (vmcnt) only for its own loads of the stage about to be read,
-// then a barrier makes every wave's part of that stage visible.
+// The loads and the stage handshake are inline assembly: the compiler does not
+// track which LDS stage a direct load fills and would wait for every
+// outstanding load before any LDS read, serialising the ring.  Here each wave
+// waits (vmcnt) only for its own loads of the stage it needs next, then a
+// barrier makes every wave's part of that stage visible.
 //
-// LDS rows are 64 bytes (4 chunks of 16).  Logical chunk c of tile row r sits
-// at chunk c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16 rows of an
-// MFMA fragment read land in 16 distinct bank groups.
+// MFMA fragments are double-buffered in registers per 64-byte k-step: the LDS
+// reads of step t+1 are in flight while step t is multiplied.  The barrier of
+// a stage sits before its first step is read, after every wave has read the
+// whole previous stage, whose slot is then refilled.
+//
+// LDS rows are BK bytes (BK/16 chunks of 16).  Logical chunk c of tile row r
+// sits at physical chunk c ^ f(r), chosen so that the 16 rows of a fragment
+// read fall in 16 distinct groups of four banks (64 banks of 4 bytes):
+//   BK = 64:  f(r) = ((r >> 1) ^ (r >> 3)) & 3   (rows r, r+4, r+8, r+12 share banks)
+//   BK = 128: f(r) = (r >> 1) & 7                 (rows of equal parity share banks)
 // ---------------------------------------------------------------------------
-constexpr int kPBK = 64;                                   // k bytes per stage
-constexpr int kPStages = 6;
-constexpr int kPStageBytes = (kQBM + kQBN) * kPBK;         // 24 KiB
-constexpr int kPDmaPerWave = (kQBM + kQBN) * kPBK / 1024 / 4;   // 1 KiB loads per wave per stage
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+template <int BK>
+__device__ __forceinline__ int swz(int r)
+{
+    if constexpr (BK == 64)
+        return ((r >> 1) ^ (r >> 3)) & 3;
+    else
+        return (r >> 1) & 7;
+}
 
 // one direct load: each lane's 16 bytes at `src` -> LDS `lds_base` + 16 * lane
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
@@ -473,26 +482,44 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
 template <int N>
 __device__ __forceinline__ void stage_barrier()
 {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <bool kRaw>
+template <int BM_, int BN_, int BK_, int S_, bool kMapN_>
+struct PipeCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
+    static constexpr bool kMapN = kMapN_;   // tile order: m fastest (true) or n fastest
+    static constexpr int KS = BK / 64;       // MFMA k-steps per stage
+    static constexpr int CH = BK / 16;       // 16-byte chunks per LDS row
+    static constexpr int RPB = 1024 / BK;    // rows filled by one 1 KiB wave load
+    static constexpr int kStageBytes = (BM + BN) * BK;
+    static constexpr int kLds = S * kStageBytes;
+    static constexpr int D = (BM + BN) / RPB / 4;   // direct loads per wave per stage
+    static_assert(BK == 64 || BK == 128, "k-tile of 64 or 128 bytes");
+    static_assert((BM + BN) % (4 * RPB) == 0 && BM % RPB == 0, "whole 1 KiB blocks, X/W split on a block");
+    static_assert((S * KS) % 2 == 0, "register buffer index taken from the unrolled step");
+    static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
+};
+
+template <class C, bool kRaw>
 __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
                                                              const float* __restrict__ ws, void* __restrict__ out,
                                                              int M, int N, int K)
 {
-    constexpr int BM = kQBM, BN = kQBN;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, KS = C::KS, D = C::D;
     constexpr int TM = BM / 2, TN = BN / 2;
     constexpr int FI = TM / 16, FJ = TN / 16;
-    extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // kPStages * kPStageBytes
+    extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // S * kStageBytes
 
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     const int tile = xcd_tile(blockIdx.x, tm * tn);
     if (tile >= tm * tn)
         return;
-    const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+    const int m0 = (C::kMapN ? tile % tm : tile / tn) * BM;
+    const int n0 = (C::kMapN ? tile / tm : tile % tn) * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -500,17 +527,17 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     const int q = lane >> 4, r16 = lane & 15;
     const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
 
-    // This wave's direct loads: the stage is (BM + BN) rows of 64 bytes, i.e.
-    // 24 blocks of 16 rows (1 KiB each); wave w fills blocks w, w+4, ..., w+20.
-    // Lane l of a block writes physical chunk l&3 of row l>>2 and so reads
-    // logical chunk (l&3) ^ swz(row).  Rows past M or N re-read the last row.
-    const uint8_t* src[kPDmaPerWave];
-    uint32_t dst[kPDmaPerWave];
+    // This wave's direct loads: the stage is (BM + BN) rows of BK bytes in
+    // blocks of RPB rows (1 KiB); wave w fills blocks w, w+4, ...  Lane l of a
+    // block writes physical chunk l % CH of row l / CH, i.e. it reads logical
+    // chunk (l % CH) ^ f(row).  Rows past M or N re-read the last row.
+    const uint8_t* src[D];
+    uint32_t dst[D];
 #pragma unroll
-    for (int u = 0; u < kPDmaPerWave; ++u) {
-        const int blk = wave + 4 * u;                  // 0..23
-        const int row = blk * 16 + (lane >> 2);        // stage row 0..383
-        const int c = (lane & 3) ^ swz(row);
+    for (int u = 0; u < D; ++u) {
+        const int blk = wave + 4 * u;
+        const int row = blk * C::RPB + lane / C::CH;
+        const int c = (lane % C::CH) ^ swz<BK>(row);
         if (row < BM) {
             const int m = min(m0 + row, M - 1);
             src[u] = reinterpret_cast<const uint8_t*>(xq) + (int64_t)m * K + 16 * c;
@@ -522,9 +549,9 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     }
     auto issue = [&](int kt, int slot) {
 #pragma unroll
-        for (int u = 0; u < kPDmaPerWave; ++u)
-            dma16(src[u] + (int64_t)kt * kPBK,
-                  (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * kPStageBytes + dst[u]));
+        for (int u = 0; u < D; ++u)
+            dma16(src[u] + (int64_t)kt * BK,
+                  (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * C::kStageBytes + dst[u]));
     };
 
     i4_t acc[FI][FJ];
@@ -534,41 +561,55 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
         for (int j = 0; j < FJ; ++j)
             acc[i][j] = i4_t{0, 0, 0, 0};
 
-    const int nk = K / kPBK;
-    // prologue: stages 0 .. STAGES-2 in flight (past the end, reload the last tile)
-#pragma unroll
-    for (int s = 0; s < kPStages - 1; ++s)
-        issue(s < nk ? s : nk - 1, s);
-
-    // fragment addresses within a stage (row-relative, swizzled chunk)
+    // fragments of k-step j of a stage, row-relative with the swizzled chunk
     const int arow0 = wm * TM + r16, brow0 = BM + wn * TN + r16;
-    for (int kt0 = 0; kt0 < nk; kt0 += kPStages) {
+    i4_t fa[2][FI], fb[2][FJ];
+    auto read_frags = [&](int slot, int j, i4_t (&af)[FI], i4_t (&bf)[FJ]) {
+        const uint8_t* base = pl + slot * C::kStageBytes;
+        const int c = 4 * j + q;
 #pragma unroll
-        for (int s = 0; s < kPStages; ++s) {
+        for (int i = 0; i < FI; ++i) {
+            const int r = arow0 + 16 * i;
+            af[i] = *reinterpret_cast<const i4_t*>(base + r * BK + 16 * (c ^ swz<BK>(r)));
+        }
+#pragma unroll
+        for (int jj = 0; jj < FJ; ++jj) {
+            const int r = brow0 + 16 * jj;
+            bf[jj] = *reinterpret_cast<const i4_t*>(base + r * BK + 16 * (c ^ swz<BK>(r)));
+        }
+    };
+
+    const int nk = K / BK;
+    // prologue: every slot in flight (tiles past the end reload the last one)
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        issue(s < nk ? s : nk - 1, s);
+    stage_barrier<D * (S - 1)>();   // tile 0 landed
+    read_frags(0, 0, fa[0], fb[0]);
+
+    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
             const int kt = kt0 + s;
             if (kt < nk) {
-                // stage s holds tile kt; (STAGES-2) younger stages stay in flight
-                stage_barrier<kPDmaPerWave * (kPStages - 2)>();
-                // refill the slot read in the previous iteration with tile kt + STAGES - 1
-                const int nt = kt + kPStages - 1;
-                issue(nt < nk ? nt : nk - 1, (s + kPStages - 1) % kPStages);
-                const uint8_t* base = pl + s * kPStageBytes;
-                i4_t af[FI], bf[FJ];
 #pragma unroll
-                for (int i = 0; i < FI; ++i) {
-                    const int r = arow0 + 16 * i;
-                    af[i] = *reinterpret_cast<const i4_t*>(base + r * kPBK + 16 * (q ^ swz(r)));
+                for (int j = 0; j < KS; ++j) {
+                    const int cur = (s * KS + j) & 1;
+                    if (j + 1 < KS) {
+                        read_frags(s, j + 1, fa[cur ^ 1], fb[cur ^ 1]);
+                    } else if (kt + 1 < nk) {
+                        // tile kt+1 landed (S-2 younger tiles may be pending) and
+                        // every wave has read tile kt: refill its slot
+                        stage_barrier<D * (S - 2)>();
+                        issue(kt + S < nk ? kt + S : nk - 1, s);
+                        read_frags((s + 1) % S, 0, fa[cur ^ 1], fb[cur ^ 1]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < FI; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < FJ; ++jj)
+                            acc[i][jj] = mfma_i8(fb[cur][jj], fa[cur][i], acc[i][jj]);
                 }
-#pragma unroll
-                for (int j = 0; j < FJ; ++j) {
-                    const int r = brow0 + 16 * j;
-                    bf[j] = *reinterpret_cast<const i4_t*>(base + r * kPBK + 16 * (q ^ swz(r)));
-                }
-#pragma unroll
-                for (int i = 0; i < FI; ++i)
-#pragma unroll
-                    for (int j = 0; j < FJ; ++j)
-                        acc[i][j] = mfma_i8(bf[j], af[i], acc[i][j]);
             }
         }
     }
@@ -578,37 +619,42 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
 }
 
-// The pipelined kernel needs kPStages * kPStageBytes of LDS per workgroup
-// (gfx950 allows 160 KiB); queried once per device.
-bool pipe_lds_fits()
+// Whether the device grants `bytes` of LDS to one workgroup (gfx950: 160 KiB);
+// queried once per device.
+bool lds_fits(int bytes)
 {
-    static std::atomic<int> known[64];   // 0 unknown, 1 fits, 2 does not
+    static std::atomic<int> cap[64];   // LDS bytes per workgroup + 1; 0 = not yet queried
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return false;
-    int v = known[dev].load(std::memory_order_relaxed);
+    int v = cap[dev].load(std::memory_order_relaxed);
     if (v == 0) {
         int lds = 0;
         if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             lds = 0;
-        v = lds >= kPStages * kPStageBytes ? 1 : 2;
-        known[dev].store(v, std::memory_order_relaxed);
+        v = lds + 1;
+        cap[dev].store(v, std::memory_order_relaxed);
     }
-    return v == 1;
+    return bytes <= v - 1;
 }
+
+using Pipe = PipeCfg<kQBM, kQBN, 128, 3, true>;
 
 template <bool kRaw>
 void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, void* out, int64_t m,
                       int64_t n, int64_t k, hipStream_t st)
 {
-    const int64_t tiles = ((n + kQBN - 1) / kQBN) * ((m + kQBM - 1) / kQBM);
-    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;   // whole rounds over the XCDs
-    if (k % kPBK == 0 && pipe_lds_fits())
-        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<kRaw>), dim3((unsigned)grid), dim3(256),
-                           (size_t)kPStages * kPStageBytes, st, xq, xs, wq, ws, out, (int)m, (int)n, (int)k);
+    // grid: whole rounds over the XCDs
+    auto grid_for = [&](int bm, int bn) {
+        const int64_t tiles = ((n + bn - 1) / bn) * ((m + bm - 1) / bm);
+        return (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
+    };
+    if (k % Pipe::BK == 0 && lds_fits(Pipe::kLds))
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(256),
+                           (size_t)Pipe::kLds, st, xq, xs, wq, ws, out, (int)m, (int)n, (int)k);
     else
-        hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3((unsigned)grid), dim3(256), 0, st, xq, xs, wq,
-                           ws, out, (int)m, (int)n, (int)k);
+        hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3(grid_for(kQBM, kQBN)), dim3(256), 0, st, xq, xs,
+                           wq, ws, out, (int)m, (int)n, (int)k);
 }
 
 
