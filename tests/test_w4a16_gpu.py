@@ -93,8 +93,15 @@ def test_gemm_small_parity(ql, path, m, n, k, group):
     assert rel_err(got, ref) <= TOL
 
 
+# GEMM path shapes: k % 128 != 0 (1056, 384 with G = 128 and three blocks)
+# and an odd number of 128-blocks with G = 128 (1152) take the register-staged
+# kernel; the rest the LDS-ring kernel, including an odd block count (1152
+# with G = 32, 64), one exactly full 128 x 192 tile, and ragged m and n with
+# n % 4 != 0.
 @pytest.mark.parametrize("m,n,k,group", [(33, 64, 256, 64), (64, 128, 512, 128), (100, 300, 1056, 32),
-                                         (130, 256, 4096, 64), (257, 130, 384, 128)])
+                                         (130, 256, 4096, 64), (257, 130, 384, 128), (70, 200, 1152, 32),
+                                         (70, 200, 1152, 64), (70, 200, 1152, 128), (128, 192, 512, 64),
+                                         (129, 194, 768, 32)])
 def test_gemm_path_mid_m(ql, m, n, k, group):
     rng = np.random.default_rng(m + n + k)
     w = workloads.weight(rng, n, k, outliers="normal0.3")

@@ -62,6 +62,26 @@ __device__ __forceinline__ h8_t dequant_word8(uint32_t w, h2_t zb, h2_t s2)
 
 // Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
 // (0,4)(1,5)(2,6)(3,7) that matches dequant_word.
+// Same values as dequant_word8 in natural element order (0,1)(2,3)(4,5)(6,7):
+// with w4 = w >> 4, v_perm_b32 places byte i of w (low nibble n_2i) in byte 0
+// and byte i of w4 (low nibble n_2i+1) in byte 2, then the same mask-and-bias
+// and the same two packed operations as above.  Two more instructions per word
+// than dequant_word8, but the activations need no reordering.
+__device__ __forceinline__ h8_t dequant_word8_natural(uint32_t w, h2_t zb, h2_t s2)
+{
+    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
+    const uint32_t w4 = w >> 4;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // selector bytes: [i of w, zero, i of w4, zero]; w4 is bytes 4..7 of the pair
+        const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
+        const uint32_t p = __builtin_amdgcn_perm(w4, w, sel);
+        o[i] = h2u((u2h(and_or(p, kMask, kMagic)) - zb) * s2);
+    }
+    return __builtin_bit_cast(h8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
 __device__ __forceinline__ uint4 permute_x8(uint4 v)
 {
     uint4 p;

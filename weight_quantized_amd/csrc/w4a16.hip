@@ -14,6 +14,7 @@
 #include <cstdint>
 
 #include "dequant.hpp"
+#include "lds_dma.hpp"
 #include "ql_common.hpp"
 
 using ql::f4_t;
@@ -50,16 +51,24 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
         const int n = (int)(i / KW), j = (int)(i - (int64_t)n * KW);
         const int g = (8 * j) / G;
         const uint32_t w = qw[i];
-        h2_t o[4];
-        ql::dequant_word(w, ql::zero_bias(ql::zero_of(qz + (int64_t)n * ZW, g)),
-                         ql::scale2(sc[(int64_t)n * NG + g]), o);
-        // back to natural order: (0,4)(1,5)(2,6)(3,7) -> 0..7
-        const uint32_t a = ql::h2u(o[0]), b = ql::h2u(o[1]), c = ql::h2u(o[2]), d = ql::h2u(o[3]);
+        const h2_t zb = ql::zero_bias(ql::zero_of(qz + (int64_t)n * ZW, g));
+        const h2_t s2 = ql::scale2(sc[(int64_t)n * NG + g]);
+        // Both in-register routines give the same natural-order values; even
+        // words take the natural-order one (GEMM), odd words the (0,4)(1,5)
+        // (2,6)(3,7) one (decode) put back in order, so the exported weights
+        // check both.
         uint4 u;
-        u.x = (a & 0xFFFFu) | (b << 16);
-        u.y = (c & 0xFFFFu) | (d << 16);
-        u.z = (a >> 16) | (b & 0xFFFF0000u);
-        u.w = (c >> 16) | (d & 0xFFFF0000u);
+        if ((j & 1) == 0) {
+            u = __builtin_bit_cast(uint4, ql::dequant_word8_natural(w, zb, s2));
+        } else {
+            h2_t o[4];
+            ql::dequant_word(w, zb, s2, o);
+            const uint32_t a = ql::h2u(o[0]), b = ql::h2u(o[1]), c = ql::h2u(o[2]), d = ql::h2u(o[3]);
+            u.x = (a & 0xFFFFu) | (b << 16);
+            u.y = (c & 0xFFFFu) | (d << 16);
+            u.z = (a >> 16) | (b & 0xFFFF0000u);
+            u.w = (c >> 16) | (d & 0xFFFF0000u);
+        }
         *reinterpret_cast<uint4*>(w16 + i * 8) = u;
         if (q8) {
             uint2 cq;
@@ -450,6 +459,314 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// GEMM, pipelined (K % 128 == 0): block tile BM x BN, 4 waves, MFMA
+// f32 16x16x32 f16 with the weight fragment as the A operand (the accumulator
+// is the transposed tile, so each lane ends with four consecutive outputs of
+// one row).
+//
+// K advances in blocks of 128.  Everything a block needs -- activations (BM
+// rows x 256 bytes), packed weights (BN rows x 64 bytes), each weight row's
+// zero-point word and scales -- is streamed by direct global->LDS loads into
+// a ring of S stages, so the main loop issues no other global loads and each
+// wave's outstanding-load count is known exactly.  The weights stay packed in
+// LDS and are dequantised in registers right before the MFMA by the shared
+// routine.
+//
+// k order inside a block: at MFMA step s (0..3) the lane of quarter q covers
+// k = 32q + 8s + [0..7], i.e. word 4q + s of its weight row.  One 16-byte LDS
+// read per weight fragment and block gives the lane its words for all four
+// steps, and the lane's k range sits in one quantisation group for G = 32, 64
+// and 128 alike: one scale and one zero point per fragment and block.  The
+// weights are dequantised in natural element order, so the activation chunk
+// 4q + s read from LDS is the MFMA operand as it stands.
+//
+// Waves are laid out WM x WN over the tile.  With 1 x 4 each wave owns BN/4
+// weight columns over all BM rows, so every weight word is dequantised by
+// exactly one wave and each dequantised fragment feeds BM/16 MFMAs.
+//
+// Per stage and weight row the ring holds the zero-point word of the block's
+// groups and two scale dwords: groups 4kb..4kb+3 (G = 32), 2kb, 2kb+1
+// (G = 64, second dword unused), or the aligned pair holding group kb
+// (G = 128, second dword unused; this needs an even number of blocks so the
+// pair never runs past the end of the scales).
+//
+// Tiles go to XCDs in groups of GM m-tiles (m fastest within a group), so the
+// 32 workgroups an XCD runs at once share a few activation and weight panels.
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int S_, int GM_>
+struct W4PipeCfg {
+    static constexpr int BM = BM_, BN = BN_, S = S_, GM = GM_;
+    static constexpr int WM = WM_, WN = 4 / WM_;       // waves along m and n
+    static constexpr int kArow = 256;                  // activation LDS row: 128 fp16
+    static constexpr int kBrow = 64;                   // weight LDS row: 16 packed words
+    static constexpr int kAbytes = BM * kArow, kBbytes = BN * kBrow;
+    static constexpr int kZoff = kAbytes + kBbytes;    // zero-point words [BN]
+    static constexpr int kSoff = kZoff + BN * 4;       // scale dwords [2][BN]
+    static constexpr int kStageBytes = kSoff + BN * 8;
+    static constexpr int kLds = S * kStageBytes;
+    static constexpr int DA = kAbytes / 4096, DB = kBbytes / 4096;   // 1 KiB loads per wave per stage
+    static constexpr int kDwRows = BN / 64;             // 4-byte loads (64 rows each) per table
+    static constexpr int DW = (4 * kDwRows + 3) / 4;   // per wave: zero words, scale dwords 0 and 1
+    static constexpr int D = DA + DB + DW;
+    static_assert(kAbytes % 4096 == 0 && kBbytes % 4096 == 0, "whole 1 KiB loads for every wave");
+    static_assert(WM * WN == 4 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0 && BN % 64 == 0,
+                  "4 waves of 16-row fragments, 64-row tables");
+    static_assert(kStageBytes % 256 == 0, "stages keep the 256-byte row bank alignment");
+};
+
+// Scheduling hint for one MFMA step: its LDS reads first, then each MFMA
+// followed by up to V vector-ALU instructions (the next step's
+// dequantisation), so the matrix pipe and the vector ALU overlap within the
+// one wave a SIMD runs.
+template <int NDS, int NMFMA, int V>
+__device__ __forceinline__ void interleave()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);   // LDS reads
+#pragma unroll
+    for (int k = 0; k < NMFMA; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // vector ALU
+    }
+}
+
+// 4-byte direct load: each lane's dword at `src` -> LDS `lds_base` + 4 * lane
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base)
+{
+    asm volatile("global_load_lds_dword %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
+}
+
+template <class C>
+__global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __restrict__ x,
+                                                              const uint32_t* __restrict__ qw,
+                                                              const uint16_t* __restrict__ sc,
+                                                              const uint32_t* __restrict__ qz,
+                                                              uint16_t* __restrict__ y, int M, int N, int K, int lg)
+{
+    constexpr int BM = C::BM, BN = C::BN, S = C::S, D = C::D, DA = C::DA, DB = C::DB, DW = C::DW;
+    constexpr int TM = BM / C::WM, TN = BN / C::WN;
+    constexpr int FI = TM / 16, FJ = TN / 16;
+    constexpr int U = S % 2 == 0 ? S : 2 * S;          // unrolled blocks: slot and register parity static
+    static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
+    extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // S * kStageBytes
+
+    const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+    const int tile = xcd_tile(blockIdx.x, tm * tn);
+    if (tile >= tm * tn)
+        return;
+    const int gsz = C::GM * tn;                        // tiles per group of GM m-tiles
+    const int grp = tile / gsz, first = grp * C::GM;
+    const int gm = min(tm - first, C::GM);
+    const int m0 = (first + (tile - grp * gsz) % gm) * BM;
+    const int n0 = ((tile - grp * gsz) / gm) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int q = lane >> 4, r16 = lane & 15;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
+    const int NG = K >> lg, ZW = (NG + 7) >> 3;
+    const int gsh = lg - 4;                            // block kb's first group is kb << (7 - lg)
+
+    // Ring loads of this wave.  Activations: 1 KiB = 4 rows of 256 bytes,
+    // lane l writes physical chunk l % 16 of row l / 16.  Weights: 1 KiB =
+    // 16 rows of 64 bytes, lane l writes physical chunk l % 4 of row l / 4.
+    // Tables: 64 rows of 4 bytes per load; load t (of 4 * BN/64, spread over
+    // the waves) is zero words (t / kDwRows == 0), scale dword 0 (1), scale
+    // dword 1 (2, G = 32 only, else a repeat of dword 0) or a repeat of the
+    // zero words (3).  Rows past M or N re-read the last row (never stored).
+    const uint8_t* src[D];
+    uint32_t dst[D];
+    int step[D];                                       // bytes per block (tables: see issue)
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        if (u < DA) {
+            const int blk = wave + 4 * u;
+            const int row = blk * 4 + (lane >> 4);
+            const int c = (lane & 15) ^ ql::swz256(row);
+            const int m = min(m0 + row, M - 1);
+            src[u] = reinterpret_cast<const uint8_t*>(x) + (int64_t)m * K * 2 + 16 * c;
+            dst[u] = (uint32_t)(blk * 1024);
+            step[u] = 256;
+        } else if (u < DA + DB) {
+            const int blk = wave + 4 * (u - DA);
+            const int row = blk * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ ql::swz64(row);
+            const int n = min(n0 + row, N - 1);
+            src[u] = reinterpret_cast<const uint8_t*>(qw) + (int64_t)n * (K / 2) + 16 * c;
+            dst[u] = (uint32_t)(C::kAbytes + blk * 1024);
+            step[u] = 64;
+        } else {
+            const int t = wave + 4 * (u - DA - DB);
+            const int kind = t / C::kDwRows, part = t % C::kDwRows;
+            const int row = 64 * part + lane;
+            const int n = min(n0 + row, N - 1);
+            if (kind == 1 || kind == 2) {
+                const int extra = (kind == 2 && lg == 5) ? 4 : 0;
+                src[u] = reinterpret_cast<const uint8_t*>(sc) + (int64_t)n * NG * 2 + extra;
+                dst[u] = (uint32_t)(C::kSoff + (kind == 2 ? 4 * BN : 0) + 4 * 64 * part);
+                step[u] = -1;                          // scale dwords
+            } else {
+                src[u] = reinterpret_cast<const uint8_t*>(qz) + (int64_t)n * ZW * 4;
+                dst[u] = (uint32_t)(C::kZoff + 4 * 64 * part);
+                step[u] = -2;                          // zero words
+            }
+        }
+    }
+    auto issue = [&](int kb, int slot) {
+        const uint32_t sbase = lds0 + slot * C::kStageBytes;
+        // scale byte offset of block kb: first group * 2, aligned down to 4
+        const int soff = ((kb << (7 - lg)) * 2) & ~3;
+        const int zoff = 4 * (kb >> gsh);
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            if (u < DA + DB) {
+                ql::dma16(src[u] + (int64_t)kb * step[u], (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
+            } else {
+                // 64 rows x 4 bytes, lane l -> row 64 * part + l
+                const bool is_scale = step[u] == -1;
+                const uint8_t* p = src[u] + (is_scale ? soff : zoff);
+                dma4(p, (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
+            }
+        }
+    };
+
+
+    // LDS fragment reads: activations of step st (FI fragments), the packed
+    // weight words of a block (FJ fragments), and the block's zero-point word
+    // and scale for each weight fragment
+    auto read_a = [&](int slot, int st, uint4 (&fa)[FI]) {
+        const uint8_t* base = pl + slot * C::kStageBytes;
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            const int r = wm * TM + 16 * i + r16;
+            fa[i] = *reinterpret_cast<const uint4*>(base + r * C::kArow + 16 * ((4 * q + st) ^ ql::swz256(r)));
+        }
+    };
+    auto read_b = [&](int slot, int kb, uint4 (&fb)[FJ], uint32_t (&zr)[FJ], uint32_t (&sr)[FJ]) {
+        const uint8_t* base = pl + slot * C::kStageBytes;
+        // scale of this lane's group: table and half within the dword
+        const int tbl = lg == 5 ? (q >> 1) : 0;
+        const int half = lg == 7 ? (kb & 1) : (lg == 6 ? (q >> 1) : (q & 1));
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int r = wn * TN + 16 * j + r16;
+            fb[j] = *reinterpret_cast<const uint4*>(base + C::kAbytes + r * C::kBrow + 16 * (q ^ ql::swz64(r)));
+            zr[j] = *reinterpret_cast<const uint32_t*>(base + C::kZoff + 4 * r);
+            sr[j] = *reinterpret_cast<const uint16_t*>(base + C::kSoff + tbl * 4 * BN + 4 * r + 2 * half);
+        }
+    };
+
+    f4_t acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    uint4 fa[2][FI], fb[2][FJ];
+    uint32_t zr[2][FJ], sr[2][FJ];
+    h2_t zb[2][FJ], s2[2][FJ];
+    h8_t bw[2][FJ];
+    const int nk = K / 128;
+    auto word = [](const uint4& w4, int st) { return st == 0 ? w4.x : st == 1 ? w4.y : st == 2 ? w4.z : w4.w; };
+    // zero bias and scale of block kb from its table words
+    auto set_zs = [&](int kb, int p) {
+        const int zsh = 4 * (((kb * 128 + 32 * q) >> lg) & 7);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            zb[p][j] = ql::zero_bias((zr[p][j] >> zsh) & 0xFu);
+            s2[p][j] = ql::scale2(sr[p][j]);
+        }
+    };
+    auto dequant = [&](int p, int st, h8_t (&out)[FJ]) {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+            out[j] = ql::dequant_word8_natural(word(fb[p][j], st), zb[p][j], s2[p][j]);
+    };
+    auto mfmas = [&](int cur, int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[i][j] = mfma16x16x32(bw[cur][j], __builtin_bit_cast(h8_t, fa[cur][i]), acc[i][j]);
+    };
+
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        issue(s < nk ? s : nk - 1, s);
+    ql::stage_barrier<D * (S - 1)>();   // block 0 landed
+    read_a(0, 0, fa[0]);
+    read_b(0, 0, fb[0], zr[0], sr[0]);
+    set_zs(0, 0);
+    dequant(0, 0, bw[0]);
+
+    // One block.  fa[st & 1] / bw[st & 1] hold step st's operands, prepared
+    // during step st-1.  Step 3 waits for the next block (S-2 younger blocks
+    // may still be in flight), refills this block's slot and reads the next
+    // block's weights, tables and first activation fragments, whose
+    // dequantisation fills the second half of step 3.  Every load is issued
+    // unconditionally (block indices clamped to the last block), so every wave
+    // has exactly D * (S-2) loads younger than the block it waits for.
+    auto block = [&](int kb, int u) {
+        const int slot = u % S, par = u & 1;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int cur = st & 1;
+            if (st < 3) {
+                read_a(slot, st + 1, fa[cur ^ 1]);
+                dequant(par, st + 1, bw[cur ^ 1]);
+                mfmas(cur, 0, FI);
+                interleave<FI, FI * FJ, 3>();
+            } else {
+                ql::stage_barrier<D * (S - 2)>();
+                issue(min(kb + S, nk - 1), slot);
+                read_b((u + 1) % S, kb + 1, fb[par ^ 1], zr[par ^ 1], sr[par ^ 1]);
+                read_a((u + 1) % S, 0, fa[cur ^ 1]);
+                mfmas(cur, 0, FI / 2);
+                set_zs(kb + 1, par ^ 1);
+                dequant(par ^ 1, 0, bw[cur ^ 1]);
+                mfmas(cur, FI / 2, FI);
+                interleave<FI + 3 * FJ, FI * FJ, 3>();
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int kb0 = 0;
+    for (; kb0 + U <= nk; kb0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            block(kb0 + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+        if (kb0 + u < nk)
+            block(kb0 + u, u);
+    ql::stage_barrier<0>();   // drain the trailing reloads before the workgroup exits
+
+    // lane (q, r16) holds y[m][n .. n+3] of fragment (i, j)
+    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            const int m = m0 + wm * TM + i * 16 + r16;
+            const int n = n0 + wn * TN + j * 16 + 4 * q;
+            if (vec) {
+                uint2 h;
+                h.x = f32_to_f16_bits(acc[i][j][0]) | ((uint32_t)f32_to_f16_bits(acc[i][j][1]) << 16);
+                h.y = f32_to_f16_bits(acc[i][j][2]) | ((uint32_t)f32_to_f16_bits(acc[i][j][3]) << 16);
+                *reinterpret_cast<uint2*>(y + (int64_t)m * N + n) = h;
+            } else if (m < M) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N)
+                        y[(int64_t)m * N + n + r] = f32_to_f16_bits(acc[i][j][r]);
+            }
+        }
+}
+
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct DecodePlan {
@@ -618,10 +935,16 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
     // 128 x 192 tiles: M=512, N=12288 gives exactly one tile per CU
     constexpr int BM = 128, BN = 192;
+    using Pipe = W4PipeCfg<BM, BN, 1, 3, 4>;
     const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-    const int64_t grid = (tiles + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN>), dim3((unsigned)grid), dim3(256), 0, st, xw, qw, scales, qz, y,
-                       mi, ni, ki, lg);
+    const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);   // whole rounds over the XCDs
+    // G = 128 reads scale pairs, which needs an even number of 128-blocks
+    if (k % 128 == 0 && (group != 128 || (k / 128) % 2 == 0) && ql::lds_fits(Pipe::kLds))
+        hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe>), dim3(grid), dim3(256), (size_t)Pipe::kLds, st, xw, qw,
+                           scales, qz, y, mi, ni, ki, lg);
+    else
+        hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN>), dim3(grid), dim3(256), 0, st, xw, qw, scales, qz, y, mi, ni,
+                           ki, lg);
     return launch_status(who);
 }
 

@@ -9,11 +9,11 @@
 //                           linear_scale)
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 
 #include <algorithm>
 #include <cstdint>
 
+#include "lds_dma.hpp"
 #include "ql_common.hpp"
 
 namespace {
@@ -457,33 +457,13 @@ constexpr int kQBM = 256, kQBN = 128;
 // whole previous stage, whose slot is then refilled.
 //
 // LDS rows are BK bytes (BK/16 chunks of 16).  Logical chunk c of tile row r
-// sits at physical chunk c ^ f(r), chosen so that the 16 rows of a fragment
-// read fall in 16 distinct groups of four banks (64 banks of 4 bytes):
-//   BK = 64:  f(r) = ((r >> 1) ^ (r >> 3)) & 3   (rows r, r+4, r+8, r+12 share banks)
-//   BK = 128: f(r) = (r >> 1) & 7                 (rows of equal parity share banks)
+// sits at physical chunk c ^ f(r), f = the shared 64- or 128-byte-row swizzle,
+// which keeps the fragment reads free of bank conflicts.
 // ---------------------------------------------------------------------------
 template <int BK>
 __device__ __forceinline__ int swz(int r)
 {
-    if constexpr (BK == 64)
-        return ((r >> 1) ^ (r >> 3)) & 3;
-    else
-        return (r >> 1) & 7;
-}
-
-// one direct load: each lane's 16 bytes at `src` -> LDS `lds_base` + 16 * lane
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
-{
-    asm volatile("global_load_lds_dwordx4 %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
-}
-
-// wait until at most N of this wave's vector-memory operations are pending,
-// then synchronise the workgroup; a compiler barrier for memory accesses
-template <int N>
-__device__ __forceinline__ void stage_barrier()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+    return BK == 64 ? ql::swz64(r) : ql::swz128(r);
 }
 
 template <int BM_, int BN_, int BK_, int S_, bool kMapN_>
@@ -550,7 +530,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     auto issue = [&](int kt, int slot) {
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            dma16(src[u] + (int64_t)kt * BK,
+            ql::dma16(src[u] + (int64_t)kt * BK,
                   (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * C::kStageBytes + dst[u]));
     };
 
@@ -584,7 +564,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
 #pragma unroll
     for (int s = 0; s < S; ++s)
         issue(s < nk ? s : nk - 1, s);
-    stage_barrier<D * (S - 1)>();   // tile 0 landed
+    ql::stage_barrier<D * (S - 1)>();   // tile 0 landed
     read_frags(0, 0, fa[0], fb[0]);
 
     for (int kt0 = 0; kt0 < nk; kt0 += S) {
@@ -600,7 +580,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
                     } else if (kt + 1 < nk) {
                         // tile kt+1 landed (S-2 younger tiles may be pending) and
                         // every wave has read tile kt: refill its slot
-                        stage_barrier<D * (S - 2)>();
+                        ql::stage_barrier<D * (S - 2)>();
                         issue(kt + S < nk ? kt + S : nk - 1, s);
                         read_frags((s + 1) % S, 0, fa[cur ^ 1], fb[cur ^ 1]);
                     }
@@ -613,29 +593,10 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
             }
         }
     }
-    stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
+    ql::stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
 
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
     store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
-}
-
-// Whether the device grants `bytes` of LDS to one workgroup (gfx950: 160 KiB);
-// queried once per device.
-bool lds_fits(int bytes)
-{
-    static std::atomic<int> cap[64];   // LDS bytes per workgroup + 1; 0 = not yet queried
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return false;
-    int v = cap[dev].load(std::memory_order_relaxed);
-    if (v == 0) {
-        int lds = 0;
-        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-            lds = 0;
-        v = lds + 1;
-        cap[dev].store(v, std::memory_order_relaxed);
-    }
-    return bytes <= v - 1;
 }
 
 using Pipe = PipeCfg<kQBM, kQBN, 128, 3, true>;
@@ -649,7 +610,7 @@ void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const
         const int64_t tiles = ((n + bn - 1) / bn) * ((m + bm - 1) / bm);
         return (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
     };
-    if (k % Pipe::BK == 0 && lds_fits(Pipe::kLds))
+    if (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds))
         hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(256),
                            (size_t)Pipe::kLds, st, xq, xs, wq, ws, out, (int)m, (int)n, (int)k);
     else
