@@ -41,6 +41,7 @@ DECODE_M = (1, 4, 8, 16, 32)
 GROUP = 128
 METRIC = "W4A16/W8A8 GEMM: HBM GB/s (M<=16), TFLOP/s (M>=512), % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+COPY_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
 
 
 def w4a16_bytes(m, n, k, g):
@@ -66,6 +67,14 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="output channels per launch for the oracle sample (0 = auto)")
+    ap.add_argument("--profile-launch", metavar="SHAPE,M",
+                    help="run one workload for counter collection and exit: gate_up,M or down,M (decode, cold "
+                         "weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM); then a plain "
+                         f"{COPY_BYTES >> 20} MiB device copy of known size that calibrates the byte counters")
+    ap.add_argument("--profile-reps", type=int, default=12)
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of a --profile-launch run "
+                         "into the traffic record bench.py reads, and print a summary")
     return ap.parse_args()
 
 
@@ -94,9 +103,15 @@ def time_graph(torch, g, reps):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.profile_launch:
+        profile_launch(args)
+        return
 
     import torch
 
@@ -290,6 +305,134 @@ def cpu_baseline(host, shapes, launches, rows_opt, log):
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"one step (10 launches), min({rows_per_opt}, N) evenly spaced output channels per launch, "
                       f"{total_s:.1f} s of oracle time"}
+
+
+def profile_launch(args):
+    """One workload, launched `--profile-reps` times eagerly, for rocprofv3
+    counter runs; decode launches rotate `--copies` weight copies so each reads
+    cold weights.  Then a plain device copy (torch neg on COPY_BYTES of fp16:
+    COPY_BYTES read, COPY_BYTES written) whose counter values calibrate them."""
+    import torch
+
+    import weight_quantized_amd as ql
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shape, m = args.profile_launch.split(",")
+    m = int(m)
+    if shape in ("gate_up", "down"):
+        n, k, g = {"gate_up": workloads.C2_GATEUP, "down": workloads.C2_DOWN}[shape]
+        w = workloads.config_weight(shape)
+        qw, sc, qz = ql.awq_pack(w, g)
+        del w
+        base = [torch.from_numpy(a).to(dev) for a in (qw, sc, qz)]
+        sets = [base] + [[t.clone() for t in base] for _ in range(args.copies - 1)]
+        x = torch.from_numpy(workloads.config_activations(shape, m, k)).to(dev)
+        y = torch.empty((m, n), dtype=torch.float16, device=dev)
+        ws = torch.zeros(max(ql.w4a16_workspace_bytes(m, n, k, g), 1), dtype=torch.uint8, device=dev)
+        for i in range(args.profile_reps):
+            d = sets[i % args.copies]
+            ql.w4a16_gemm(x, d[0], d[1], d[2], g, out=y, workspace=ws)
+        desc = {"shape": f"{shape}_m{m}", "bytes_per_launch": w4a16_bytes(m, n, k, g)}
+    elif shape == "qkv":
+        n, k, g = workloads.C3
+        w = workloads.config_weight("qkv")
+        qw, sc, qz = ql.awq_pack(w, g)
+        del w
+        d = [torch.from_numpy(a).to(dev) for a in (qw, sc, qz)]
+        x = torch.from_numpy(workloads.config_activations("qkv", m, k)).to(dev)
+        y = torch.empty((m, n), dtype=torch.float16, device=dev)
+        for _ in range(args.profile_reps):
+            ql.w4a16_gemm(x, *d, g, out=y)
+        desc = {"shape": f"qkv_m{m}", "flops_per_launch": 2 * m * n * k}
+    elif shape == "w8a8":
+        xh, gamma, wf = workloads.smoothquant_inputs(m=m)
+        s_, gs, wsm = ql.smooth(xh, gamma, wf)
+        wq, wsc = ql.w8a8_quant_weight(wsm)
+        del wf, wsm
+        xd, gd = torch.from_numpy(xh).to(dev), torch.from_numpy(gs).to(dev)
+        wqd, wsd = torch.from_numpy(wq).to(dev), torch.from_numpy(wsc).to(dev)
+        xq = torch.empty(xh.shape, dtype=torch.int8, device=dev)
+        xsc = torch.empty((m,), dtype=torch.float32, device=dev)
+        yy = torch.empty((m, wq.shape[0]), dtype=torch.float16, device=dev)
+        for _ in range(args.profile_reps):
+            ql.w8a8_quant_rmsnorm(xd, gd, 1e-6, xq=xq, x_scale=xsc)
+            ql.w8a8_gemm(xq, xsc, wqd, wsd, out=yy)
+        desc = {"shape": f"w8a8_m{m}", "ops_per_launch": 2 * m * wq.shape[0] * xh.shape[1]}
+    else:
+        raise SystemExit(f"unknown workload {shape!r}")
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.profile_reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    desc.update({"reps": args.profile_reps, "copy_bytes": COPY_BYTES, "source_hash": kernel_source_hash()})
+    print(json.dumps(desc), flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            out[key] = out.get(key, 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """HBM bytes per launch of the profiled decode kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the same counter's reading on
+    the calibration copy of known size.  Writes TRAFFIC_FILE and prints a
+    markdown summary."""
+    fetch, write = _counter_rows(fetch_csv), _counter_rows(write_csv)
+
+    def pick(rows, sub):
+        return sorted(v for (_, name), v in rows.items() if sub in name)
+
+    def median(v):
+        return float(np.median(v)) if v else float("nan")
+
+    dec_f, dec_w = pick(fetch, "w4a16_decode_kernel"), pick(write, "w4a16_decode_kernel")
+    cp_f, cp_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")
+    if not (dec_f and dec_w and cp_f and cp_w):
+        raise SystemExit("counter files lack the decode kernel or the calibration copy")
+    kib = COPY_BYTES / 1024.0
+    f_fac, w_fac = kib / median(cp_f), kib / median(cp_w)
+    fetch_b = median(dec_f) * 1024.0 * f_fac
+    write_b = median(dec_w) * 1024.0 * w_fac
+    # the launch this describes is the one `bench.py --profile-launch` ran: its stdout (a JSON line) is
+    # expected as profile_launch.json next to the counter directories
+    meta_path = os.path.join(os.path.dirname(os.path.abspath(fetch_csv)), "..", "profile_launch.json")
+    meta = {}
+    for cand in (meta_path, os.path.join(os.path.dirname(os.path.abspath(fetch_csv)), "profile_launch.json")):
+        if os.path.exists(cand):
+            with open(cand) as f:
+                lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+            if lines:
+                meta = json.loads(lines[-1])
+            break
+    rec = {"source_hash": meta.get("source_hash", kernel_source_hash()), "shape": meta.get("shape"),
+           "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "algorithmic_bytes": meta.get("bytes_per_launch"),
+           "fetch_kib_raw": median(dec_f), "write_kib_raw": median(dec_w),
+           "copy_fetch_kib_raw": median(cp_f), "copy_write_kib_raw": median(cp_w),
+           "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4), "dispatches": len(dec_f)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    alg = rec["algorithmic_bytes"]
+    print(f"| launch | {rec['shape']} |\n|---|---|")
+    print(f"| decode FETCH_SIZE (KiB, median of {len(dec_f)}) | {median(dec_f):.0f} |")
+    print(f"| decode WRITE_SIZE (KiB) | {median(dec_w):.0f} |")
+    print(f"| copy of {COPY_BYTES >> 20} MiB: FETCH / WRITE (KiB) | {median(cp_f):.0f} / {median(cp_w):.0f} |")
+    print(f"| scale factors (known bytes / counter) | {f_fac:.4f} / {w_fac:.4f} |")
+    print(f"| decode HBM bytes per launch (fetch + write) | {fetch_b + write_b:,.0f} |")
+    if alg:
+        print(f"| algorithmic bytes per launch | {alg:,} (traffic / algorithmic = {(fetch_b + write_b) / alg:.3f}) |")
 
 
 if __name__ == "__main__":

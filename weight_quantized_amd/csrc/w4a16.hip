@@ -261,14 +261,19 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
         return;
     }
 
-    // 5. split-K: publish this slice's partial sums (agent scope), then arrive
+    // 5. split-K: publish this slice's partial tile -- [M][16T] fp32, row-major,
+    //    at part[(slice * nblk + column block) * M * 16T] -- with agent-scope
+    //    stores, wait for them, then arrive
+    constexpr int TW = 16 * T;                    // tile width (columns)
+    const int nblk = gridDim.x;
+    float* tile = part + ((int64_t)blockIdx.y * nblk + blockIdx.x) * (int64_t)M * TW;
 #pragma unroll
     for (int t = 0; t < MT / 16; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = t * 16 + 4 * q + r;
-            if (m < M && nok)
-                __hip_atomic_store(&part[((int64_t)blockIdx.y * M + m) * N + n], res[t][r], __ATOMIC_RELAXED,
+            if (m < M)
+                __hip_atomic_store(&tile[m * TW + wave * 16 + r16], res[t][r], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
@@ -281,14 +286,46 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
     __syncthreads();
     if (!s_last)
         return;
-    for (int idx = threadIdx.x; idx < M * T * 16; idx += 64 * T) {
-        const int m = idx / (T * 16), nn = n0 + idx - m * (T * 16);
-        if (nn < N) {
-            float s = 0.f;
-            for (int sl = 0; sl < S; ++sl)
-                s += __hip_atomic_load(&part[((int64_t)sl * M + m) * N + nn], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            y[(int64_t)m * N + nn] = f32_to_f16_bits(s);
+    // The last arrival sums the S tiles in slice order.  Each thread owns four
+    // consecutive columns of one row; the slices' 16-byte pieces are read with
+    // agent-scope buffer loads, eight slices in flight at a time.
+    {
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(part, (uint32_t)((int64_t)S * nblk * M * TW * (int64_t)sizeof(float)));
+        constexpr int kSc1 = 16;                  // cache policy: agent scope (bypasses this CU's L1)
+        const uint32_t tile_bytes = (uint32_t)(M * TW * sizeof(float));
+        const uint32_t col_bytes = (uint32_t)blockIdx.x * tile_bytes;
+        const uint32_t slice_bytes = (uint32_t)nblk * tile_bytes;
+        for (int v = threadIdx.x; v < M * (TW / 4); v += 64 * T) {
+            const uint32_t off = col_bytes + (uint32_t)v * 16u;
+            f4_t sum = f4_t{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < S; s0 += 8) {
+                f4_t pv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sl = min(s0 + u, S - 1);
+                    pv[u] = __builtin_bit_cast(
+                        f4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (int)(off + (uint32_t)sl * slice_bytes), 0,
+                                                                    kSc1));
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (s0 + u < S)
+                        sum += pv[u];
+            }
+            const int m = v / (TW / 4), nn = n0 + (v % (TW / 4)) * 4;
+            uint16_t* yr = y + (int64_t)m * N;
+            if (nn + 3 < N && (N & 3) == 0) {
+                uint2 h;
+                h.x = f32_to_f16_bits(sum[0]) | ((uint32_t)f32_to_f16_bits(sum[1]) << 16);
+                h.y = f32_to_f16_bits(sum[2]) | ((uint32_t)f32_to_f16_bits(sum[3]) << 16);
+                *reinterpret_cast<uint2*>(yr + nn) = h;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (nn + e < N)
+                        yr[nn + e] = f32_to_f16_bits(sum[e]);
+            }
         }
     }
     if (threadIdx.x == 0)
@@ -786,11 +823,11 @@ struct DecodePlan {
 // sums as counters when they share one workspace.
 constexpr size_t kCounterBytes = 32768;
 constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
-constexpr size_t kDecodeLdsBudget = 64 * 1024;   // staged activations + scales per workgroup
+constexpr size_t kDecodeLdsBudget = 80 * 1024;   // staged activations + scales per workgroup (two per CU)
 constexpr int kDecodeWaveTarget = 2048;          // >= 8 streaming waves per CU
 
 // Tile choice.  Activations of one slice are staged per workgroup, so the
-// slice length is capped by m * ks * 2 <= 64 KiB; within that cap the slice is
+// slice length is capped by the LDS budget (two workgroups per CU); within that cap the slice is
 // as long as possible (fewer partial sums), but K is split further when the
 // column tiles alone give fewer than ~8 streaming waves per CU.
 DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
@@ -806,7 +843,7 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     slices = std::min<int64_t>(slices, kblocks);
     for (;; ++slices) {
         const int64_t sblocks = (kblocks + slices - 1) / slices;
-        const int pd = sblocks % 4 == 0 ? 4 : 2;
+        const int pd = 2;   // measured at least as fast as a ring of 4 on every MLP decode shape
         const int64_t nbp = (sblocks + pd - 1) / pd * pd;
         const int64_t gs = sblocks * 256 / group;
         const size_t lds = (size_t)rows * (size_t)(nbp * 32 + 1) * 16 + (size_t)(16 * p.t * gs) * 4;
@@ -819,7 +856,9 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     }
     p.slices = (int)((k + p.ks - 1) / p.ks);
     p.part_offset = kCounterBytes;
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)m * (size_t)n * sizeof(float) : 0;
+    // partial tiles [slices][nblk][m][16 t] fp32
+    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)(16 * p.t) * sizeof(float)
+                                : 0;
     return p;
 }
 
@@ -921,6 +960,9 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
         if (p.slices > 1 && p.nblk > kMaxDecodeBlocks)
             QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld exceeds the decode path's %d column blocks", who, (long long)n,
                     kMaxDecodeBlocks);
+        if (p.part_bytes >= ((size_t)1 << 32))
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: m=%lld n=%lld k=%lld needs %zu bytes of partial sums (limit 4 GiB)", who,
+                    (long long)m, (long long)n, (long long)k, p.part_bytes);
         const size_t need = decode_workspace(p);
         if (need > 0 && (!workspace || workspace_bytes < need))
             QL_FAIL(QL_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
