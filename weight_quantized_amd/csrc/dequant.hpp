@@ -62,6 +62,32 @@ __device__ __forceinline__ h8_t dequant_word8(uint32_t w, h2_t zb, h2_t s2)
 
 // Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
 // (0,4)(1,5)(2,6)(3,7) that matches dequant_word.
+// dequant_word8 over the eight words of a 256-k decode block (words 0-3 in
+// group a, 4-7 in group b), written stage by stage -- all extractions, then
+// all zero subtractions, then all scale products -- so the 32 independent
+// chains interleave instead of running back to back through one register.
+__device__ __forceinline__ void dequant_block8(const uint32_t (&w)[8], const h2_t (&zb)[2], const h2_t (&s2)[2],
+                                               h8_t (&out)[8])
+{
+    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
+    uint32_t e[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            e[j][i] = and_or(w[j] >> (4 * i), kMask, kMagic);
+    h2_t d[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d[j][i] = u2h(e[j][i]) - zb[j >> 2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        out[j] = __builtin_bit_cast(h8_t, make_uint4(h2u(d[j][0] * s2[j >> 2]), h2u(d[j][1] * s2[j >> 2]),
+                                                     h2u(d[j][2] * s2[j >> 2]), h2u(d[j][3] * s2[j >> 2])));
+}
+
 // Same values as dequant_word8 in natural element order (0,1)(2,3)(4,5)(6,7):
 // with w4 = w >> 4, v_perm_b32 places byte i of w (low nibble n_2i) in byte 0
 // and byte i of w4 (low nibble n_2i+1) in byte 2, then the same mask-and-bias

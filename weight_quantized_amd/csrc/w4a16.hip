@@ -164,31 +164,56 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 2. scales and zero points of this workgroup's rows and slice -> LDS
+    // 2. scales and zero points of this workgroup's rows and slice -> LDS.
+    //    Each thread issues four entries' loads (clamped, always in bounds)
+    //    before using any, so the staging costs one memory latency, not four.
     {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, (uint32_t)N * (uint32_t)NG * 2u);
         const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
         const int g0 = k0 >> lg;
-        for (int e = threadIdx.x; e < 16 * T * gs; e += 64 * T) {
-            const int rr = e / gs, gg = e - rr * gs;
-            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
-            const uint32_t g = (uint32_t)(g0 + gg);
-            const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)((row * (uint32_t)NG + g) * 2u), 0, 0);
-            const uint32_t zw = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)((row * (uint32_t)ZW + (g >> 3)) * 4u), 0, 0);
-            sz[e] = sv | (((zw >> (4 * (g & 7))) & 0xFu) << 16);
+        const int total = 16 * T * gs;
+        for (int e0 = 0; e0 < total; e0 += 4 * 64 * T) {
+            uint32_t sv[4], zw[4], gv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = min(e0 + u * 64 * T + (int)threadIdx.x, total - 1);
+                const int rr = e / gs, gg = e - rr * gs;
+                const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+                const uint32_t g = (uint32_t)(g0 + gg);
+                gv[u] = g;
+                sv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)((row * (uint32_t)NG + g) * 2u), 0, 0);
+                zw[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)((row * (uint32_t)ZW + (g >> 3)) * 4u), 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * 64 * T + (int)threadIdx.x;
+                if (e < total)
+                    sz[e] = sv[u] | (((zw[u] >> (4 * (gv[u] & 7))) & 0xFu) << 16);
+            }
         }
     }
 
-    // 3. activations of the slice -> LDS (zero past K and in the ring padding)
+    // 3. activations of the slice -> LDS (zero past K and in the ring padding),
+    //    eight 16-byte loads in flight per thread before any is stored
     {
         const int cpr = nbp * 32;
         const int total = mrows * cpr;
-        for (int idx = threadIdx.x; idx < total; idx += 64 * T) {
-            const int m = idx / cpr, c = idx - m * cpr;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (c < nch)
-                v = ql::permute_x8(*reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + 8 * c));
-            xs[m * RS + c] = v;
+        for (int i0 = 0; i0 < total; i0 += 8 * 64 * T) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = i0 + u * 64 * T + (int)threadIdx.x;
+                const int m = min(idx / cpr, mrows - 1), c = min(idx % cpr, nch - 1);
+                v[u] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + 8 * c);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = i0 + u * 64 * T + (int)threadIdx.x;
+                if (idx < total) {
+                    const int m = idx / cpr, c = idx % cpr;
+                    xs[m * RS + c] = c < nch ? ql::permute_x8(v[u]) : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
         }
     }
     __syncthreads();
@@ -221,12 +246,10 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
             const uint32_t ea = szrow[ga], eb = szrow[gb];
             const h2_t zb[2] = {ql::zero_bias(ea >> 16), ql::zero_bias(eb >> 16)};
             const h2_t s2[2] = {ql::scale2(ea & 0xFFFFu), ql::scale2(eb & 0xFFFFu)};
-            const uint32_t words[8] = {ring[p][0].x, ring[p][0].y, ring[p][0].z, ring[p][0].w,
-                                       ring[p][1].x, ring[p][1].y, ring[p][1].z, ring[p][1].w};
+            const uint4 w0 = ring[p][0], w1 = ring[p][1];
+            const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
             h8_t bw[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                bw[j] = ql::dequant_word8(words[j], zb[j >> 2], s2[j >> 2]);
+            ql::dequant_block8(words, zb, s2, bw);
             // Refill in place and in order.  Without the scheduling barriers the
             // compiler sinks and regroups the refills, so waiting for one block
             // means waiting for the whole ring.
@@ -813,7 +836,7 @@ struct DecodePlan {
     int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
-    size_t lds; // dynamic LDS bytes
+    size_t lds_bytes;   // dynamic LDS bytes
     size_t part_offset, part_bytes;
 };
 
@@ -843,14 +866,14 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     slices = std::min<int64_t>(slices, kblocks);
     for (;; ++slices) {
         const int64_t sblocks = (kblocks + slices - 1) / slices;
-        const int pd = 2;   // measured at least as fast as a ring of 4 on every MLP decode shape
+        const int pd = 2;   // a ring of 2 measured at least as fast as 4 on every MLP decode shape
         const int64_t nbp = (sblocks + pd - 1) / pd * pd;
         const int64_t gs = sblocks * 256 / group;
         const size_t lds = (size_t)rows * (size_t)(nbp * 32 + 1) * 16 + (size_t)(16 * p.t * gs) * 4;
         if (lds <= kDecodeLdsBudget || sblocks == 1) {
             p.p = pd;
             p.ks = (int)(sblocks * 256);
-            p.lds = lds;
+            p.lds_bytes = lds;
             break;
         }
     }
@@ -895,7 +918,7 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<MT, T, P>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds, st, x, qw,
+    hipLaunchKernelGGL((w4a16_decode_kernel<MT, T, P>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes, st, x, qw,
                        sc, qz, y, part, cnt, m, n, k, lg, p.ks);
 }
 
@@ -909,8 +932,7 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
         launch_decode_t<MT_, T_, P_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);        \
         return true;                                                                   \
     }
-    QL_DECODE_CASE(16, 4, 2) QL_DECODE_CASE(16, 4, 4)
-    QL_DECODE_CASE(32, 4, 2) QL_DECODE_CASE(32, 4, 4)
+    QL_DECODE_CASE(16, 4, 2) QL_DECODE_CASE(32, 4, 2)
 #undef QL_DECODE_CASE
     return false;
 }
