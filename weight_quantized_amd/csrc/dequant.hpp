@@ -108,6 +108,35 @@ __device__ __forceinline__ h8_t dequant_word8_natural(uint32_t w, h2_t zb, h2_t 
     return __builtin_bit_cast(h8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
+// dequant_word8_natural over N words (each with its own zero bias and
+// scale), written stage by stage so the independent chains interleave.
+template <int N>
+__device__ __forceinline__ void dequant_words_natural(const uint32_t (&w)[N], const h2_t (&zb)[N],
+                                                      const h2_t (&s2)[N], h8_t (&out)[N])
+{
+    constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x64006400u;
+    uint32_t e[N][4];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const uint32_t w4 = w[j] >> 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
+            e[j][i] = and_or(__builtin_amdgcn_perm(w4, w[j], sel), kMask, kMagic);
+        }
+    }
+    h2_t d[N][4];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            d[j][i] = u2h(e[j][i]) - zb[j];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        out[j] = __builtin_bit_cast(h8_t, make_uint4(h2u(d[j][0] * s2[j]), h2u(d[j][1] * s2[j]),
+                                                     h2u(d[j][2] * s2[j]), h2u(d[j][3] * s2[j])));
+}
+
 __device__ __forceinline__ uint4 permute_x8(uint4 v)
 {
     uint4 p;

@@ -602,7 +602,7 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
                                                               const uint32_t* __restrict__ qz,
                                                               uint16_t* __restrict__ y, int M, int N, int K, int lg)
 {
-    constexpr int BM = C::BM, BN = C::BN, S = C::S, D = C::D, DA = C::DA, DB = C::DB, DW = C::DW;
+    constexpr int BM = C::BM, BN = C::BN, S = C::S, D = C::D, DA = C::DA, DB = C::DB;
     constexpr int TM = BM / C::WM, TN = BN / C::WN;
     constexpr int FI = TM / 16, FJ = TN / 16;
     constexpr int U = S % 2 == 0 ? S : 2 * S;          // unrolled blocks: slot and register parity static
@@ -739,9 +739,11 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
         }
     };
     auto dequant = [&](int p, int st, h8_t (&out)[FJ]) {
+        uint32_t w[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
-            out[j] = ql::dequant_word8_natural(word(fb[p][j], st), zb[p][j], s2[p][j]);
+            w[j] = word(fb[p][j], st);
+        ql::dequant_words_natural<FJ>(w, zb[p], s2[p], out);
     };
     auto mfmas = [&](int cur, int i0, int i1) {
 #pragma unroll

@@ -23,13 +23,16 @@ typedef int i4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // QRMSNorm
 //
-// The mean of squares is computed exactly: an fp16 value is an integer
-// significand times 2^(e-25), so its square is an integer multiple of 2^-48
-// below 2^80.  Each thread sums its squares in a 128-bit integer; integer
-// addition is associative, so the workgroup total does not depend on the
-// reduction order.  The total is divided by k and rounded once to fp32.
-// Every later step (sqrt, divisions, products) is a single correctly rounded
-// fp32 operation, so the codes are independent of the launch configuration.
+// The mean of squares is the exact mean rounded once to fp32.  Fast path: the
+// squares of fp16 values are exact in fp64 and are summed in fp64; with the
+// sum's error bound, the fp32 rounding of the mean is certain unless it lies
+// within 2^-36 of a rounding boundary.  Exact path (then): an fp16 value is an
+// integer significand times 2^(e-25), so its square is an integer multiple of
+// 2^-48 below 2^80; each thread sums its squares in a 128-bit integer
+// (associative, so independent of the reduction order) and the total is
+// divided by k and rounded once.  Every later step (sqrt, divisions, products)
+// is a single correctly rounded fp32 operation, so the codes do not depend on
+// the launch configuration.
 // ---------------------------------------------------------------------------
 struct U128 {
     uint64_t lo, hi;
@@ -159,46 +162,151 @@ __device__ __forceinline__ float block_max(float v, float* sh)
     return t;
 }
 
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* sh)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0)
+        sh[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w)
+        t += sh[w];
+    return t;
+}
+
+// Fast path of the mean of squares.  `tot` is the sum of K exact fp64
+// squares (non-negative) accumulated with K + log2(NT) roundings at most, so
+// |tot - exact| <= 2^-37 exact for K <= 65536; dividing by K adds one more
+// rounding.  If no fp32 rounding boundary (the midpoint to either neighbour of
+// the candidate, exact in fp64) lies within 2^-36 of tot / K, the candidate is
+// the correctly rounded exact mean; otherwise the caller takes the exact path.
+__device__ __forceinline__ bool mean_fast(double tot, int K, float* out)
+{
+    const double m = tot / (double)K;
+    if (m == 0.0) {
+        *out = 0.0f;
+        return true;
+    }
+    const float f = (float)m;
+    const uint32_t fb = __builtin_bit_cast(uint32_t, f);
+    const double lo = 0.5 * ((double)f + (double)__builtin_bit_cast(float, fb - 1u));
+    const double hi = 0.5 * ((double)f + (double)__builtin_bit_cast(float, fb + 1u));
+    const double d = m * 0x1p-36;
+    *out = f;
+    return m - d > lo && m + d < hi;
+}
+
 __device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
 
 constexpr int kNormThreads = 256;
 
 // One workgroup per token; chunks of 8 fp16 (16 bytes) strided over threads.
+// CPT > 0: each thread holds its CPT chunks of x and gamma in registers --
+// every load of the token is issued before the first is used, and the norm,
+// absmax and quantisation passes read registers.  CPT == 0: chunks are
+// re-read from memory in each pass (any k).  Chunks past k are zero: they add
+// nothing to the sum of squares or the absmax and are not stored.
+template <int CPT>
 __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint16_t* __restrict__ x,
                                                                      const uint16_t* __restrict__ gamma, float eps,
                                                                      int8_t* __restrict__ xq,
                                                                      float* __restrict__ x_scale, int K)
 {
     __shared__ U128 s_sum[kNormThreads / 64];
+    __shared__ double s_sumd[kNormThreads / 64];
     __shared__ float s_max[kNormThreads / 64];
     const int row = blockIdx.x;
     const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)row * K);
     const uint4* gr = reinterpret_cast<const uint4*>(gamma);
     const int nch = K >> 3;
+    constexpr int R = CPT > 0 ? CPT : 1;
+    uint4 xv[R], gv[R];
+    auto chunk = [&](int i, int c, uint4& v, uint4& g) {   // chunk c (loop slot i)
+        if constexpr (CPT > 0) {
+            v = xv[i];
+            g = gv[i];
+        } else {
+            v = xr[c];
+            g = gr[c];
+        }
+    };
+    if constexpr (CPT > 0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = (int)threadIdx.x + i * kNormThreads;
+            const int cc = c < nch ? c : nch - 1;
+            xv[i] = xr[cc];
+            gv[i] = gr[cc];
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            if ((int)threadIdx.x + i * kNormThreads >= nch)
+                xv[i] = gv[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int npass = CPT > 0 ? CPT : (nch - (int)threadIdx.x + kNormThreads - 1) / kNormThreads;
 
-    U128 acc{0, 0};
-    for (int c = threadIdx.x; c < nch; c += kNormThreads) {
-        const uint4 v = xr[c];
+    // mean of squares: fp64 sum of the exact squares, or, when its fp32
+    // rounding is not certain, the exact 128-bit integer sum (the decision is
+    // taken on the workgroup total, so the whole workgroup branches together)
+    double accd = 0.0;
+#pragma unroll R
+    for (int i = 0; i < npass; ++i) {
+        uint4 v, g;
+        chunk(i, (int)threadIdx.x + i * kNormThreads, v, g);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            add_square(acc, w[i] & 0xFFFFu);
-            add_square(acc, w[i] >> 16);
+        for (int e = 0; e < 4; ++e) {
+            const double a = (double)h2f(w[e] & 0xFFFFu), b = (double)h2f(w[e] >> 16);
+            accd = __builtin_fma(a, a, accd);
+            accd = __builtin_fma(b, b, accd);
         }
     }
-    const U128 tot = block_sum128<kNormThreads>(acc, s_sum);
-    const float ms = mean_from_exact(tot, (uint32_t)K);
+    float ms;
+    if (!mean_fast(block_sum_f64<kNormThreads>(accd, s_sumd), K, &ms)) {
+        U128 acc{0, 0};
+#pragma unroll R
+        for (int i = 0; i < npass; ++i) {
+            uint4 v, g;
+            chunk(i, (int)threadIdx.x + i * kNormThreads, v, g);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                add_square(acc, w[e] & 0xFFFFu);
+                add_square(acc, w[e] >> 16);
+            }
+        }
+        ms = mean_from_exact(block_sum128<kNormThreads>(acc, s_sum), (uint32_t)K);
+    }
     const float r = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
 
-    float amax = 0.0f;
-    for (int c = threadIdx.x; c < nch; c += kNormThreads) {
-        const uint4 v = xr[c], g = gr[c];
+    // y = fp32(fp32(x * r) * gamma); kept per element when the chunks are in
+    // registers, recomputed per pass otherwise
+    float yk[R][8];
+    auto y_of = [&](const uint4& v, const uint4& g, float (&yo)[8]) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float y0 = __fmul_rn(__fmul_rn(h2f(w[i] & 0xFFFFu), r), h2f(gw[i] & 0xFFFFu));
-            const float y1 = __fmul_rn(__fmul_rn(h2f(w[i] >> 16), r), h2f(gw[i] >> 16));
-            amax = fmaxf(amax, fmaxf(fabsf(y0), fabsf(y1)));
+        for (int e = 0; e < 4; ++e) {
+            yo[2 * e] = __fmul_rn(__fmul_rn(h2f(w[e] & 0xFFFFu), r), h2f(gw[e] & 0xFFFFu));
+            yo[2 * e + 1] = __fmul_rn(__fmul_rn(h2f(w[e] >> 16), r), h2f(gw[e] >> 16));
+        }
+    };
+    float amax = 0.0f;
+#pragma unroll R
+    for (int i = 0; i < npass; ++i) {
+        uint4 v, g;
+        chunk(i, (int)threadIdx.x + i * kNormThreads, v, g);
+        float yo[8];
+        y_of(v, g, yo);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            amax = fmaxf(amax, fabsf(yo[e]));
+            if constexpr (CPT > 0)
+                yk[i][e] = yo[e];
         }
     }
     amax = block_max<kNormThreads>(amax, s_max);
@@ -206,27 +314,42 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     if (threadIdx.x == 0)
         x_scale[row] = scale;
 
+    // Code of y: rint(fp32(y / scale)), clamped to +-127.  q0 = y * RN(1/scale)
+    // is within 1.5 ulp of fp32(y / scale) (both < 128 in magnitude, an ulp is
+    // at most 2^-17), so the two round to the same integer unless q0 lies
+    // within 2^-15 of a half-integer; only those take the exact division.
+    const float rcp = scale > 0.0f ? __fdiv_rn(1.0f, scale) : 0.0f;
+    auto code = [&](float yv) -> uint32_t {
+        if (!(scale > 0.0f))
+            return 0u;
+        const float q0 = yv * rcp;
+        float qr = rintf(q0);
+        const float half = floorf(q0) + 0.5f;
+        if (__builtin_expect(fabsf(q0 - half) <= 0x1p-15f, 0))
+            qr = rintf(__fdiv_rn(yv, scale));
+        const int qv = (int)fminf(fmaxf(qr, -127.0f), 127.0f);
+        return (uint32_t)qv & 0xFFu;
+    };
     uint2* qr = reinterpret_cast<uint2*>(xq + (int64_t)row * K);
-    for (int c = threadIdx.x; c < nch; c += kNormThreads) {
-        const uint4 v = xr[c], g = gr[c];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll R
+    for (int i = 0; i < npass; ++i) {
+        const int c = (int)threadIdx.x + i * kNormThreads;
+        float yo[8];
+        if constexpr (CPT > 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                yo[e] = yk[i][e];
+        } else {
+            uint4 v, g;
+            chunk(i, c, v, g);
+            y_of(v, g, yo);
+        }
         uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const uint32_t xb = hh ? (w[i] >> 16) : (w[i] & 0xFFFFu);
-                const uint32_t gb = hh ? (gw[i] >> 16) : (gw[i] & 0xFFFFu);
-                const float yv = __fmul_rn(__fmul_rn(h2f(xb), r), h2f(gb));
-                int qv = 0;
-                if (scale > 0.0f)
-                    qv = (int)rintf(__fdiv_rn(yv, scale));
-                qv = qv < -127 ? -127 : (qv > 127 ? 127 : qv);
-                const int e = 2 * i + hh;
-                packed[e >> 2] |= ((uint32_t)qv & 0xFFu) << (8 * (e & 3));
-            }
-        }
-        qr[c] = make_uint2(packed[0], packed[1]);
+        for (int e = 0; e < 8; ++e)
+            packed[e >> 2] |= code(yo[e]) << (8 * (e & 3));
+        if (c < nch)
+            qr[c] = make_uint2(packed[0], packed[1]);
     }
 }
 
@@ -663,8 +786,19 @@ extern "C" int ql_w8a8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, f
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
     if (!ql::aligned16(x) || !ql::aligned16(gamma) || !ql::aligned16(xq) || !ql::aligned16(x_scale))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
-    hipLaunchKernelGGL(quant_rmsnorm_kernel, dim3((unsigned)m), dim3(kNormThreads), 0,
-                       static_cast<hipStream_t>(stream), x, gamma, eps, xq, x_scale, (int)k);
+    const int64_t cpt = (k / 8 + kNormThreads - 1) / kNormThreads;   // 16-byte chunks per thread
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)m), block(kNormThreads);
+    if (cpt <= 1)
+        hipLaunchKernelGGL(quant_rmsnorm_kernel<1>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+    else if (cpt <= 2)
+        hipLaunchKernelGGL(quant_rmsnorm_kernel<2>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+    else if (cpt <= 4)
+        hipLaunchKernelGGL(quant_rmsnorm_kernel<4>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+    else if (cpt <= 8)
+        hipLaunchKernelGGL(quant_rmsnorm_kernel<8>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+    else
+        hipLaunchKernelGGL(quant_rmsnorm_kernel<0>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
     return launch_status(who);
 }
 
