@@ -60,8 +60,6 @@ __device__ __forceinline__ h8_t dequant_word8(uint32_t w, h2_t zb, h2_t s2)
     return __builtin_bit_cast(h8_t, make_uint4(h2u(o[0]), h2u(o[1]), h2u(o[2]), h2u(o[3])));
 }
 
-// Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
-// (0,4)(1,5)(2,6)(3,7) that matches dequant_word.
 // dequant_word8 over the eight words of a 256-k decode block (words 0-3 in
 // group a, 4-7 in group b), written stage by stage -- all extractions, then
 // all zero subtractions, then all scale products -- so the 32 independent
@@ -137,6 +135,8 @@ __device__ __forceinline__ void dequant_words_natural(const uint32_t (&w)[N], co
                                                      h2u(d[j][2] * s2[j]), h2u(d[j][3] * s2[j])));
 }
 
+// Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
+// (0,4)(1,5)(2,6)(3,7) that matches dequant_word.
 __device__ __forceinline__ uint4 permute_x8(uint4 v)
 {
     uint4 p;
