@@ -91,9 +91,10 @@ def test_w4a16_gemm_validation():
 def test_workspace_sizes():
     assert LIB.ql_w4a16_workspace_bytes(0, 64, 128, 128) == 0
     assert LIB.ql_w4a16_workspace_bytes(512, 4096, 4096, 64) == 0        # GEMM path needs none
-    a = LIB.ql_w4a16_workspace_bytes(1, 22016, 4096, 128)
-    b = LIB.ql_w4a16_workspace_bytes(16, 22016, 4096, 128)
+    a = LIB.ql_w4a16_workspace_bytes(1, 4096, 11008, 128)          # few columns: K is split
+    b = LIB.ql_w4a16_workspace_bytes(16, 4096, 11008, 128)
     assert 0 < a < b
+    assert LIB.ql_w4a16_workspace_bytes(16, 4096, 4096, 128) > 0
 
 
 def test_dequant_validation():

@@ -36,7 +36,11 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float v)
 }
 
 // ---------------------------------------------------------------------------
-// dequant export: one thread per packed word
+// dequant export: one thread per 8-word block of a row (the row length K/8 is
+// a multiple of 8 words when K is a multiple of 64; otherwise the last block
+// of a row is partial).  Even blocks take the interleaved routine (put back
+// in natural order), odd blocks the natural one, so the exported weights check
+// both.  Words 0-3 and 4-7 of a block each lie in one group (G >= 32).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __restrict__ qw,
                                                             const uint16_t* __restrict__ sc,
@@ -45,36 +49,47 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
                                                             uint8_t* __restrict__ q8, int N, int K, int G)
 {
     const int KW = K / 8, NG = K / G, ZW = (NG + 7) / 8;
-    const int64_t total = (int64_t)N * KW;
+    const int BPR = (KW + 7) / 8;                     // blocks per row
+    const int64_t total = (int64_t)N * BPR;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int n = (int)(i / KW), j = (int)(i - (int64_t)n * KW);
-        const int g = (8 * j) / G;
-        const uint32_t w = qw[i];
-        const h2_t zb = ql::zero_bias(ql::zero_of(qz + (int64_t)n * ZW, g));
-        const h2_t s2 = ql::scale2(sc[(int64_t)n * NG + g]);
-        // Both in-register routines give the same natural-order values; even
-        // words take the natural-order one (GEMM), odd words the (0,4)(1,5)
-        // (2,6)(3,7) one (decode) put back in order, so the exported weights
-        // check both.
-        uint4 u;
-        if ((j & 1) == 0) {
-            u = __builtin_bit_cast(uint4, ql::dequant_word8_natural(w, zb, s2));
-        } else {
-            h2_t o[4];
-            ql::dequant_word(w, zb, s2, o);
-            const uint32_t a = ql::h2u(o[0]), b = ql::h2u(o[1]), c = ql::h2u(o[2]), d = ql::h2u(o[3]);
-            u.x = (a & 0xFFFFu) | (b << 16);
-            u.y = (c & 0xFFFFu) | (d << 16);
-            u.z = (a >> 16) | (b & 0xFFFF0000u);
-            u.w = (c >> 16) | (d & 0xFFFF0000u);
+        const int n = (int)(i / BPR), jb = (int)(i - (int64_t)n * BPR);
+        const int j0 = jb * 8, nw = min(8, KW - j0);
+        uint32_t w[8];
+        ql::zb_t zb[8];
+        h2_t s2[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + min(u, nw - 1);
+            const int g = (8 * j) / G;
+            w[u] = qw[(int64_t)n * KW + j];
+            zb[u] = ql::make_zb(ql::zero_of(qz + (int64_t)n * ZW, g));
+            s2[u] = ql::scale2(sc[(int64_t)n * NG + g]);
         }
-        *reinterpret_cast<uint4*>(w16 + i * 8) = u;
-        if (q8) {
-            uint2 cq;
-            cq.x = (w & 0xFu) | ((w >> 4) & 0xFu) << 8 | ((w >> 8) & 0xFu) << 16 | ((w >> 12) & 0xFu) << 24;
-            cq.y = ((w >> 16) & 0xFu) | ((w >> 20) & 0xFu) << 8 | ((w >> 24) & 0xFu) << 16 | (w >> 28) << 24;
-            *reinterpret_cast<uint2*>(q8 + i * 8) = cq;
+        h8_t v[8];
+        if ((jb & 1) == 0) {
+            ql::dequant_words<8>(w, zb, s2, v);
+        } else {
+            ql::dequant_words_natural<8>(w, zb, s2, v);
+        }
+        for (int u = 0; u < nw; ++u) {
+            uint4 o = __builtin_bit_cast(uint4, v[u]);
+            if ((jb & 1) == 0) {
+                const uint32_t a = o.x, b = o.y, c = o.z, d = o.w;   // (0,4)(1,5)(2,6)(3,7)
+                o.x = (a & 0xFFFFu) | (b << 16);
+                o.y = (c & 0xFFFFu) | (d << 16);
+                o.z = (a >> 16) | (b & 0xFFFF0000u);
+                o.w = (c >> 16) | (d & 0xFFFF0000u);
+            }
+            const int64_t wi = (int64_t)n * KW + j0 + u;
+            *reinterpret_cast<uint4*>(w16 + wi * 8) = o;
+            if (q8) {
+                const uint32_t ww = w[u];
+                uint2 cq;
+                cq.x = (ww & 0xFu) | ((ww >> 4) & 0xFu) << 8 | ((ww >> 8) & 0xFu) << 16 | ((ww >> 12) & 0xFu) << 24;
+                cq.y = ((ww >> 16) & 0xFu) | ((ww >> 20) & 0xFu) << 8 | ((ww >> 24) & 0xFu) << 16 | (ww >> 28) << 24;
+                *reinterpret_cast<uint2*>(q8 + wi * 8) = cq;
+            }
         }
     }
 }
@@ -82,26 +97,33 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 // ---------------------------------------------------------------------------
 // decode: m <= MT (16 or 32)
 //
-// Workgroup = T waves; wave t owns 16 output channels, so a workgroup covers
-// 16T channels and one K slice of KS (a multiple of 256).  The slice's
-// activations (rows < m) are staged once in LDS, in the dequantiser's element
-// order, and shared by the T waves.  Each wave then streams its 16 rows of the
-// slice in blocks of 256 k through a P-deep register ring: as soon as block b
-// is consumed its slot is refilled with block b + P, so every wave keeps about
-// P x 2 KB of weights in flight.
+// Workgroup = 4 waves; wave w owns R tiles of 16 output channels, so a
+// workgroup covers TW = 64 R channels and one K slice of KS (a multiple of
+// 256; one slice when K is not split).  K advances in blocks of 256.  Per
+// block each wave streams its rows' weights through a P-deep register ring,
+// and the workgroup streams the block's activations (rows < m) through a
+// two-slot LDS ring: the threads load block b + P's activations together with
+// the weights of block b + P, reorder each 16-byte chunk for the dequantiser
+// in registers and write it to LDS one block ahead of its use; one barrier per
+// block publishes it.  Every load is an ordinary (compiler-tracked) load, so
+// each wait names exactly the block it needs.
 //
 // In a block, lane l (row l%16, quarter q = l/16) loads two 16-byte pieces of
 // its row: words [4q, 4q+4) and [16+4q, 16+4q+4), so 4 lanes read 64
-// contiguous bytes of a row per load.  Word j of piece i is the B operand of
-// one MFMA directly; weights never pass through LDS.
+// contiguous bytes of a row per load.  Word j of piece h is the B operand of
+// one MFMA directly; weights never pass through LDS.  An activation fragment
+// read from LDS serves all R tiles of the wave.
+//
+// With 128-channel groups (POST) every MFMA sums 32 k of one group per output
+// channel, so the kernel feeds the exact integers q - z and applies the group
+// scale to the fp32 result of each group's MFMAs; otherwise the dequantised
+// fp16 weights (q - z) * s are fed.
 //
 // Weights, scales and zero points are read with buffer loads: a scalar
-// resource per tensor and a 32-bit per-lane offset, so the per-block address
-// arithmetic is one add or an immediate offset.  A read past a resource's end
-// returns zero.  Lanes past N read row N-1 and their outputs are discarded;
-// pieces past the slice end read finite words of the same tensor that meet
-// zero activations (the staged slice is zero past K).  MFMA rows past m read
-// a real activation row and are never stored.
+// resource per tensor and a 32-bit per-lane offset.  A read past a resource's
+// end returns zero.  Lanes past N read row N-1 and their outputs are
+// discarded; pieces past the slice end read finite words of the same tensor
+// that meet zero activations.  Activation rows past m are zero in LDS.
 //
 // Split-K (S > 1 slices): each slice writes its fp32 partial tile with
 // agent-scope stores, waits for them to complete, then bumps a per-column-block
@@ -117,191 +139,343 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
-template <int MT, int T, int P>
-__global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
+// Activation blocks in LDS: chunk c (16 bytes) of row m sits at chunk
+// c ^ xswz(m) of the row.  The image of xswz never sets bit 2, so for the
+// chunks a fragment read touches (16 h + 4q + j, j < 4) the 32 lanes with
+// q < 2 -- and the 32 with q >= 2 -- land on 32 distinct chunks of one
+// 512-byte span.
+__device__ __forceinline__ int xswz(int m) { return (m & 3) | ((m & 12) << 1); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t s16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)s16);
+}
+
+// Workgroups per CU the register budget is held to: three for one 16-row
+// tile (a 1376-wave launch stays resident in one round), two for 32 rows.
+template <int MT, int R>
+constexpr int decode_wg_per_cu()
+{
+    return R > 1 ? 1 : (MT == 16 ? 3 : 2);
+}
+
+template <int MT, int R, int P, bool POST>
+__global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
     uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
 {
-    // LDS: activations [min(M, MT)][RS] uint4, then per (row, group) of the
-    // slice one word holding (fp16 scale | zero point << 16)
-    extern __shared__ uint4 xs[];
+    constexpr int T = 4;
+    constexpr int TW = 16 * T * R;                 // channels per workgroup
+    constexpr int MTI = MT / 16;                   // MFMA row tiles
+    constexpr int XPT = MT / 8;                    // activation chunks per thread and block
+    constexpr int NJ = POST ? 1 : (R * MTI >= 4 ? 1 : 4 / (R * MTI));   // accumulator chains
+    constexpr int NW = 8 * R;                      // words per lane and block
+    __shared__ uint4 xs[2][MT * 32];               // activation ring: two 256-k blocks
+    extern __shared__ uint32_t tab[];              // scale and zero-point tables
     __shared__ int s_last;
 
     const int S = gridDim.y;
     const int k0 = blockIdx.y * KS;
     const int kend = min(K, k0 + KS);
-    const int nch = (kend - k0) >> 3;
-    const int nb = (kend - k0 + 255) >> 8;
+    const int nch = (kend - k0) >> 3;             // valid chunks of the slice
+    const int nb = (kend - k0 + 255) >> 8;        // blocks of this slice
     const int nbp = (nb + P - 1) / P * P;         // blocks streamed, padded to the ring
-    const int RS = ((KS >> 8) + P - 1) / P * P * 32 + 1;   // padded slice + 16-byte pad
     const int mrows = M < MT ? M : MT;
     const int gs = KS >> lg;                      // groups per slice
-    uint32_t* sz = reinterpret_cast<uint32_t*>(xs + mrows * RS);   // [16T][gs]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
-    const int n0 = blockIdx.x * T * 16;
-    const int n = n0 + wave * 16 + r16;
-    const bool nok = n < N;
+    const int n0 = blockIdx.x * TW;
     const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
-    const uint32_t nr = (uint32_t)(nok ? n : N - 1);
 
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
-    const uint32_t ow = nr * (uint32_t)KW * 4u + (uint32_t)(k0 + 32 * q) / 2u;   // block 0, piece 0
-    auto load_block = [&](int b, uint4& w0, uint4& w1) {
-        const uint32_t bw = ow + (uint32_t)b * 128u;
-        w0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)bw, 0, 0));
-        w1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(bw + 64u), 0, 0));
+    // activation chunks of this thread: chunk tid + 256 u of a block is chunk
+    // (tid + 256 u) % 32 of row (tid + 256 u) / 32
+    const uint16_t* xsrc[XPT];
+    int xdst[XPT], xcc[XPT];
+    bool xok[XPT];
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+        const int c = tid + 256 * u, m = c >> 5, cc = c & 31;
+        xok[u] = m < mrows;
+        xcc[u] = cc;
+        xsrc[u] = x + (int64_t)(m < mrows ? m : mrows - 1) * K + k0;
+        xdst[u] = m * 32 + (cc ^ xswz(m));
+    }
+    auto x_load = [&](int j, uint4 (&v)[XPT]) {
+#pragma unroll
+        for (int u = 0; u < XPT; ++u)
+            v[u] = *reinterpret_cast<const uint4*>(xsrc[u] + 8 * min(j * 32 + xcc[u], nch - 1));
+    };
+    auto x_store = [&](int j, const uint4 (&v)[XPT]) {
+#pragma unroll
+        for (int u = 0; u < XPT; ++u) {
+            const bool ok = xok[u] && j * 32 + xcc[u] < nch;
+            xs[j & 1][xdst[u]] = ok ? ql::permute_x8(v[u]) : make_uint4(0u, 0u, 0u, 0u);
+        }
     };
 
-    // 1. the first P weight blocks (unconditional: blocks past the slice
-    // re-read block nb-1, so every wait in the stream has a static count)
-    uint4 ring[P][2];
+    // scales and zero points of this workgroup's channels and slice, as
+    // dwords: per channel SD dwords of scales starting at the even element at
+    // or below its first group (the dword holding it), then ZD words of zero
+    // points.  (The scales are read in 4-byte units, up to the 4-byte
+    // boundary at or after their end.)
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(sc, ((uint32_t)N * (uint32_t)NG * 2u + 3u) & ~3u);
+    const __amdgpu_buffer_rsrc_t rzr = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
+    const int g0 = k0 >> lg;
+    const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
+    const int stot = TW * SD, ztot = TW * ZD;     // scale dwords, zero-point words
+    constexpr int kSB = 6 * R, kZB = 2 * R;       // entries per thread and batch
+    uint32_t sv[kSB], zv[kZB];
+    // (each table has its own loop: a per-lane choice of buffer resource
+    // would make the compiler loop over the distinct resources)
+    auto tab_load = [&](int e0, int z0) {
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const int e = min(e0 + u * 256 + tid, stot - 1);
+            const int rr = e / SD, col = e - rr * SD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t dw = ((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col;
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(dw * 4u), 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kZB; ++u) {
+            const int e = min(z0 + u * 256 + tid, ztot - 1);
+            const int rr = e / ZD, col = e - rr * ZD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t wd = row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col;
+            zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rzr, (int)(wd * 4u), 0, 0);
+        }
+    };
+    // (threads past the end rewrite the last entry with its own value, so the
+    // loads above have no conditional use the compiler could sink them into)
+    auto tab_store = [&](int e0, int z0) {
+#pragma unroll
+        for (int u = 0; u < kSB; ++u)
+            tab[min(e0 + u * 256 + tid, stot - 1)] = sv[u];
+#pragma unroll
+        for (int u = 0; u < kZB; ++u)
+            tab[stot + min(z0 + u * 256 + tid, ztot - 1)] = zv[u];
+    };
+
+    // weights: block b of this lane's tile t, two 16-byte pieces
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
+    uint32_t ow[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int n = n0 + (wave * R + t) * 16 + r16;
+        ow[t] = (uint32_t)(n < N ? n : N - 1) * (uint32_t)KW * 4u + (uint32_t)(k0 + 32 * q) / 2u;
+    }
+    auto load_block = [&](int b, uint4 (&rg)[R][2]) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            const uint32_t bw = ow[t] + (uint32_t)b * 128u;
+            rg[t][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)bw, 0, 0));
+            rg[t][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(bw + 64u), 0, 0));
+        }
+    };
+
+    // 1. requests: tables, then activations and weights of the first P blocks
+    //    (weights past the slice re-read block nb-1, so every wait in the
+    //    stream has a static count)
+    tab_load(0, 0);
+    uint4 ring[P][R][2];
+    uint4 xr[P][XPT];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        load_block(p < nb ? p : nb - 1, ring[p][0], ring[p][1]);
+        x_load(p, xr[p]);
+        load_block(p < nb ? p : nb - 1, ring[p]);
         __builtin_amdgcn_sched_barrier(0);
     }
-
-    // 2. scales and zero points of this workgroup's rows and slice -> LDS.
-    //    Each thread issues four entries' loads (clamped, always in bounds)
-    //    before using any, so the staging costs one memory latency, not four.
-    {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(sc, (uint32_t)N * (uint32_t)NG * 2u);
-        const __amdgpu_buffer_rsrc_t rz = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
-        const int g0 = k0 >> lg;
-        const int total = 16 * T * gs;
-        for (int e0 = 0; e0 < total; e0 += 4 * 64 * T) {
-            uint32_t sv[4], zw[4], gv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = min(e0 + u * 64 * T + (int)threadIdx.x, total - 1);
-                const int rr = e / gs, gg = e - rr * gs;
-                const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
-                const uint32_t g = (uint32_t)(g0 + gg);
-                gv[u] = g;
-                sv[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)((row * (uint32_t)NG + g) * 2u), 0, 0);
-                zw[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, (int)((row * (uint32_t)ZW + (g >> 3)) * 4u), 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = e0 + u * 64 * T + (int)threadIdx.x;
-                if (e < total)
-                    sz[e] = sv[u] | (((zw[u] >> (4 * (gv[u] & 7))) & 0xFu) << 16);
-            }
-        }
+    // 2. tables and block 0's activations -> LDS
+    tab_store(0, 0);
+    for (int e0 = kSB * 256, z0 = kZB * 256; e0 < stot || z0 < ztot; e0 += kSB * 256, z0 += kZB * 256) {
+        tab_load(e0, z0);
+        tab_store(e0, z0);
     }
-
-    // 3. activations of the slice -> LDS (zero past K and in the ring padding),
-    //    eight 16-byte loads in flight per thread before any is stored
-    {
-        const int cpr = nbp * 32;
-        const int total = mrows * cpr;
-        for (int i0 = 0; i0 < total; i0 += 8 * 64 * T) {
-            uint4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int idx = i0 + u * 64 * T + (int)threadIdx.x;
-                const int m = min(idx / cpr, mrows - 1), c = min(idx % cpr, nch - 1);
-                v[u] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0 + 8 * c);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int idx = i0 + u * 64 * T + (int)threadIdx.x;
-                if (idx < total) {
-                    const int m = idx / cpr, c = idx % cpr;
-                    xs[m * RS + c] = c < nch ? ql::permute_x8(v[u]) : make_uint4(0u, 0u, 0u, 0u);
-                }
-            }
-        }
-    }
+    x_store(0, xr[0]);
     __syncthreads();
 
-    // 4. stream the slice: consume block b, refill its slot with block b + P
-    f4_t acc[4][MT / 16];
+    // 3. stream the slice
+    f4_t acc[R][MTI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int t = 0; t < MT / 16; ++t)
-            acc[i][t] = f4_t{0.f, 0.f, 0.f, 0.f};
-    int arow[MT / 16];
+        for (int i = 0; i < MTI; ++i)
 #pragma unroll
-    for (int t = 0; t < MT / 16; ++t) {
-        const int m = t * 16 + r16;
-        arow[t] = (m < mrows ? m : mrows - 1) * RS + 4 * q;
+            for (int c = 0; c < NJ; ++c)
+                acc[t][i][c] = f4_t{0.f, 0.f, 0.f, 0.f};
+    // this lane's fragment addresses within a block slot: chunk
+    // (16 h + 4q + jj) ^ xswz(m) of row m, h = j >> 2, jj = j & 3.  Bit 4 of
+    // the swizzle only flips the half h, so the second half is the first
+    // shifted by hoff = +-16 chunks.
+    int arow[MTI][4], hoff[MTI];
+#pragma unroll
+    for (int i = 0; i < MTI; ++i) {
+        const int m = i * 16 + r16;
+        const int f = xswz(m);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            arow[i][jj] = m * 32 + ((4 * q + jj) ^ (f & 15)) + (f & 16);
+        hoff[i] = (f & 16) ? -16 : 16;
     }
-    const uint32_t* szrow = sz + (wave * 16 + r16) * gs;
     const int glane = (32 * q) >> lg;             // this lane's group offset within a block
     const int gmax = gs - 1;
+    // table row of each of this lane's channels, and the element offset of
+    // its first group within its scale dwords
+    int trow[R], spar[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        trow[t] = (wave * R + t) * 16 + r16;
+        const uint32_t row = (uint32_t)min(n0 + trow[t], N - 1);
+        spar[t] = (int)((row * (uint32_t)NG + (uint32_t)g0) & 1u);
+    }
 
     for (int b0 = 0; b0 < nbp; b0 += P) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
             const int b = b0 + p;
+            // activation fragments of block b: requested first, so the LDS
+            // latency passes while the weights are dequantised
+            uint4 af[8][MTI];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < MTI; ++i)
+                    af[j][i] = xs[b & 1][arow[i][j & 3] + (j >> 2) * hoff[i]];
             // groups of the two pieces (padding blocks clamp to the last group;
             // their activations are zero)
             const int ga = min(((256 * b) >> lg) + glane, gmax);
             const int gb = min(((256 * b + 128) >> lg) + glane, gmax);
-            const uint32_t ea = szrow[ga], eb = szrow[gb];
-            const h2_t zb[2] = {ql::zero_bias(ea >> 16), ql::zero_bias(eb >> 16)};
-            const h2_t s2[2] = {ql::scale2(ea & 0xFFFFu), ql::scale2(eb & 0xFFFFu)};
-            const uint4 w0 = ring[p][0], w1 = ring[p][1];
-            const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-            h8_t bw[8];
-            ql::dequant_block8(words, zb, s2, bw);
-            // Refill in place and in order.  Without the scheduling barriers the
-            // compiler sinks and regroups the refills, so waiting for one block
-            // means waiting for the whole ring.
+            uint32_t words[NW];
+            ql::zb_t zb[NW];
+            uint32_t s16[R][2];
+#pragma unroll
+            for (int t = 0; t < R; ++t) {
+                const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + trow[t] * SD);
+                const uint32_t* zrow = tab + stot + trow[t] * ZD;
+                const uint32_t za_ = (zrow[((g0 + ga) >> 3) - (g0 >> 3)] >> (4 * ((g0 + ga) & 7))) & 0xFu;
+                const uint32_t zb_ = (zrow[((g0 + gb) >> 3) - (g0 >> 3)] >> (4 * ((g0 + gb) & 7))) & 0xFu;
+                s16[t][0] = srow[spar[t] + ga];
+                s16[t][1] = srow[spar[t] + gb];
+                const ql::zb_t za = ql::make_zb(za_), zc = ql::make_zb(zb_);
+                const uint4 w0 = ring[p][t][0], w1 = ring[p][t][1];
+                const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    words[8 * t + j] = wv[j];
+                    zb[8 * t + j] = j < 4 ? za : zc;
+                }
+            }
+            h8_t bw[NW];
+            if constexpr (POST) {
+                h2_t d[NW][4];
+                ql::dequant_words_qz<NW>(words, zb, d);
+#pragma unroll
+                for (int j = 0; j < NW; ++j)
+                    bw[j] = __builtin_bit_cast(h8_t, make_uint4(ql::h2u(d[j][0]), ql::h2u(d[j][1]),
+                                                                ql::h2u(d[j][2]), ql::h2u(d[j][3])));
+            } else {
+                h2_t s2[NW];
+#pragma unroll
+                for (int t = 0; t < R; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        s2[8 * t + j] = ql::scale2(s16[t][j >> 2]);
+                ql::dequant_words<NW>(words, zb, s2, bw);
+            }
+            // Requests for block b + P, in place and in order: activations
+            // first, so waiting for them never waits for younger weights.
+            // Without the scheduling barriers the compiler sinks and
+            // regroups the loads, so waiting for one block means waiting for
+            // the whole ring.
             const int nxt = b + P < nb ? b + P : nb - 1;
             __builtin_amdgcn_sched_barrier(0);
-            load_block(nxt, ring[p][0], ring[p][1]);
+            x_load(b + P, xr[p]);
+            load_block(nxt, ring[p]);
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (POST) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+                for (int t = 0; t < R; ++t) {
+                    const float sa = f16_bits_to_f32(s16[t][0]), sb = f16_bits_to_f32(s16[t][1]);
 #pragma unroll
-                for (int t = 0; t < MT / 16; ++t) {
-                    const int c = b * 32 + (j >> 2) * 16 + (j & 3);
-                    const h8_t af = __builtin_bit_cast(h8_t, xs[arow[t] + c]);
-                    acc[j & 3][t] = mfma16x16x32(af, bw[j], acc[j & 3][t]);
+                    for (int i = 0; i < MTI; ++i) {
+                        f4_t da = f4_t{0.f, 0.f, 0.f, 0.f}, db = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            da = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[8 * t + j], da);
+                            db = mfma16x16x32(__builtin_bit_cast(h8_t, af[4 + j][i]), bw[8 * t + 4 + j], db);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[t][i][0][r] = __builtin_fmaf(sb, db[r], __builtin_fmaf(sa, da[r], acc[t][i][0][r]));
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < MTI; ++i)
+#pragma unroll
+                        for (int t = 0; t < R; ++t)
+                            acc[t][i][j % NJ] =
+                                mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[8 * t + j], acc[t][i][j % NJ]);
+            }
+            // block b + 1's activations -> the other slot; the barrier
+            // publishes them and frees this slot for block b + 2
+            x_store(b + 1, xr[(p + 1) % P]);
+            __syncthreads();
         }
     }
-    f4_t res[MT / 16];
+    f4_t res[R][MTI];
 #pragma unroll
-    for (int t = 0; t < MT / 16; ++t)
-        res[t] = (acc[0][t] + acc[1][t]) + (acc[2][t] + acc[3][t]);
+    for (int t = 0; t < R; ++t)
+#pragma unroll
+        for (int i = 0; i < MTI; ++i) {
+            if constexpr (NJ == 4)
+                res[t][i] = (acc[t][i][0] + acc[t][i][1]) + (acc[t][i][2] + acc[t][i][3]);
+            else if constexpr (NJ == 2)
+                res[t][i] = acc[t][i][0] + acc[t][i][1];
+            else
+                res[t][i] = acc[t][i][0];
+        }
 
     if (S == 1) {
 #pragma unroll
-        for (int t = 0; t < MT / 16; ++t)
+        for (int t = 0; t < R; ++t) {
+            const int n = n0 + (wave * R + t) * 16 + r16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = t * 16 + 4 * q + r;
-                if (m < M && nok)
-                    y[(int64_t)m * N + n] = f32_to_f16_bits(res[t][r]);
-            }
+            for (int i = 0; i < MTI; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = i * 16 + 4 * q + r;
+                    if (m < M && n < N)
+                        y[(int64_t)m * N + n] = f32_to_f16_bits(res[t][i][r]);
+                }
+        }
         return;
     }
 
-    // 5. split-K: publish this slice's partial tile -- [M][16T] fp32, row-major,
-    //    at part[(slice * nblk + column block) * M * 16T] -- with agent-scope
+    // 6. split-K: publish this slice's partial tile -- [M][TW] fp32, row-major,
+    //    at part[(slice * nblk + column block) * M * TW] -- with agent-scope
     //    stores, wait for them, then arrive
-    constexpr int TW = 16 * T;                    // tile width (columns)
     const int nblk = gridDim.x;
     float* tile = part + ((int64_t)blockIdx.y * nblk + blockIdx.x) * (int64_t)M * TW;
 #pragma unroll
-    for (int t = 0; t < MT / 16; ++t)
+    for (int t = 0; t < R; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = t * 16 + 4 * q + r;
-            if (m < M)
-                __hip_atomic_store(&tile[m * TW + wave * 16 + r16], res[t][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int i = 0; i < MTI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = i * 16 + 4 * q + r;
+                if (m < M)
+                    __hip_atomic_store(&tile[m * TW + (wave * R + t) * 16 + r16], res[t][i][r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
     __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
     __syncthreads();                    // ... and so have every other thread's
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
         const uint32_t prev =
             __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(S - 1));
@@ -319,7 +493,7 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
         const uint32_t tile_bytes = (uint32_t)(M * TW * sizeof(float));
         const uint32_t col_bytes = (uint32_t)blockIdx.x * tile_bytes;
         const uint32_t slice_bytes = (uint32_t)nblk * tile_bytes;
-        for (int v = threadIdx.x; v < M * (TW / 4); v += 64 * T) {
+        for (int v = tid; v < M * (TW / 4); v += 256) {
             const uint32_t off = col_bytes + (uint32_t)v * 16u;
             f4_t sum = f4_t{0.f, 0.f, 0.f, 0.f};
             for (int s0 = 0; s0 < S; s0 += 8) {
@@ -351,7 +525,7 @@ __global__ __launch_bounds__(64 * T) void w4a16_decode_kernel(
             }
         }
     }
-    if (threadIdx.x == 0)
+    if (tid == 0)
         __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -447,12 +621,17 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
             const int c = tid + u * 256;
             const int row = c >> 1;
             if (row < BN) {
-                const h2_t zb = ql::zero_bias(rz[u] & 0xFu), s2 = ql::scale2(rs[u]);
+                const ql::zb_t zb1 = ql::make_zb(rz[u] & 0xFu);
+                const h2_t s21 = ql::scale2(rs[u]);
                 const uint32_t words[4] = {rb[u].x, rb[u].y, rb[u].z, rb[u].w};
+                const ql::zb_t zb[4] = {zb1, zb1, zb1, zb1};
+                const h2_t s2[4] = {s21, s21, s21, s21};
+                h8_t wv[4];
+                ql::dequant_words<4>(words, zb, s2, wv);
                 uint8_t* dst = Bs + buf * BN * kGRow + row * kGRow + (c & 1) * 64;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<h8_t*>(dst + j * 16) = ql::dequant_word8(words[j], zb, s2);
+                    *reinterpret_cast<h8_t*>(dst + j * 16) = wv[j];
             }
         }
     };
@@ -725,7 +904,8 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
 
     uint4 fa[2][FI], fb[2][FJ];
     uint32_t zr[2][FJ], sr[2][FJ];
-    h2_t zb[2][FJ], s2[2][FJ];
+    ql::zb_t zb[2][FJ];
+    h2_t s2[2][FJ];
     h8_t bw[2][FJ];
     const int nk = K / 128;
     auto word = [](const uint4& w4, int st) { return st == 0 ? w4.x : st == 1 ? w4.y : st == 2 ? w4.z : w4.w; };
@@ -734,7 +914,7 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
         const int zsh = 4 * (((kb * 128 + 32 * q) >> lg) & 7);
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
-            zb[p][j] = ql::zero_bias((zr[p][j] >> zsh) & 0xFu);
+            zb[p][j] = ql::make_zb((zr[p][j] >> zsh) & 0xFu);
             s2[p][j] = ql::scale2(sr[p][j]);
         }
     };
@@ -833,8 +1013,9 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
 // ---------------------------------------------------------------------------
 struct DecodePlan {
     int mt;     // 16 or 32
-    int t;      // waves (16-channel tiles) per workgroup
+    int r;      // 16-channel tiles per wave (the workgroup has 4 waves)
     int p;      // blocks in flight per wave
+    bool post;  // group scale applied to the fp32 MFMA result (128-channel groups)
     int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
@@ -848,42 +1029,39 @@ struct DecodePlan {
 // sums as counters when they share one workspace.
 constexpr size_t kCounterBytes = 32768;
 constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
-constexpr size_t kDecodeLdsBudget = 80 * 1024;   // staged activations + scales per workgroup (two per CU)
-constexpr int kDecodeWaveTarget = 2048;          // >= 8 streaming waves per CU
+constexpr int kDecodeWaveMin = 1024;             // 4 streaming waves per CU (MI355X: 256 CUs)
+constexpr int kDecodeWaveTarget = 2048;          // 8 streaming waves per CU
 
-// Tile choice.  Activations of one slice are staged per workgroup, so the
-// slice length is capped by the LDS budget (two workgroups per CU); within that cap the slice is
-// as long as possible (fewer partial sums), but K is split further when the
-// column tiles alone give fewer than ~8 streaming waves per CU.
+// Dynamic LDS of the decode kernel: the scale and zero-point tables.
+size_t decode_tables(int64_t sblocks, int r, int group)
+{
+    const int64_t gs = sblocks * 256 / group;
+    return (size_t)(64 * r) * (size_t)((gs >> 1) + 1 + (gs >> 3) + 2) * 4;
+}
+// Tile and split choice (measured on the MLP decode shapes).  K is split
+// until the launch has ~8 streaming waves per CU, except that from 9 rows on
+// a launch whose column tiles alone give >= 4 waves per CU is not split: there
+// the partial sums (which grow with m) cost more than the extra waves gain.
 DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
 {
     DecodePlan p{};
     p.mt = m <= 16 ? 16 : 32;
-    p.t = 4;
-    p.nblk = (int)((n + p.t * 16 - 1) / (p.t * 16));
-    const int64_t rows = std::min<int64_t>(m, p.mt);
+    p.p = 2;
+    p.r = 1;
+    p.post = group == 128;
+    const int64_t tw = 64 * p.r;
+    p.nblk = (int)((n + tw - 1) / tw);
     const int64_t kblocks = (k + 255) / 256;
-    const int64_t waves = (int64_t)p.nblk * p.t;
-    int64_t slices = waves >= kDecodeWaveTarget ? 1 : (kDecodeWaveTarget + waves - 1) / waves;
-    slices = std::min<int64_t>(slices, kblocks);
-    for (;; ++slices) {
-        const int64_t sblocks = (kblocks + slices - 1) / slices;
-        const int pd = 2;   // a ring of 2 measured at least as fast as 4 on every MLP decode shape
-        const int64_t nbp = (sblocks + pd - 1) / pd * pd;
-        const int64_t gs = sblocks * 256 / group;
-        const size_t lds = (size_t)rows * (size_t)(nbp * 32 + 1) * 16 + (size_t)(16 * p.t * gs) * 4;
-        if (lds <= kDecodeLdsBudget || sblocks == 1) {
-            p.p = pd;
-            p.ks = (int)(sblocks * 256);
-            p.lds_bytes = lds;
-            break;
-        }
-    }
+    const int64_t waves = (int64_t)p.nblk * 4;
+    const int64_t target = (m > 8 && waves >= kDecodeWaveMin) ? waves : kDecodeWaveTarget;
+    int64_t slices = std::min<int64_t>((target + waves - 1) / waves, kblocks);
+    const int64_t sblocks = (kblocks + slices - 1) / slices;
+    p.ks = (int)(sblocks * 256);
+    p.lds_bytes = decode_tables(sblocks, p.r, group);
     p.slices = (int)((k + p.ks - 1) / p.ks);
     p.part_offset = kCounterBytes;
-    // partial tiles [slices][nblk][m][16 t] fp32
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)(16 * p.t) * sizeof(float)
-                                : 0;
+    // partial tiles [slices][nblk][m][64 r] fp32
+    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)tw * sizeof(float) : 0;
     return p;
 }
 
@@ -914,14 +1092,14 @@ int launch_status(const char* who)
     return QL_OK;
 }
 
-template <int MT, int T, int P>
+template <int MT, int R, int P, bool POST>
 void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                      const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<MT, T, P>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes, st, x, qw,
-                       sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+    hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST>), dim3(p.nblk, p.slices), dim3(256), p.lds_bytes, st, x,
+                       qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
 }
 
 // Exact dispatch on the plan; returns false for a combination that is not
@@ -929,12 +1107,15 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                    const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
-#define QL_DECODE_CASE(MT_, T_, P_)                                                    \
-    if (p.mt == MT_ && p.t == T_ && p.p == P_) {                                       \
-        launch_decode_t<MT_, T_, P_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);        \
-        return true;                                                                   \
+#define QL_DECODE_CASE(MT_, R_, P_)                                                          \
+    if (p.mt == MT_ && p.r == R_ && p.p == P_) {                                             \
+        if (p.post)                                                                          \
+            launch_decode_t<MT_, R_, P_, true>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
+        else                                                                                 \
+            launch_decode_t<MT_, R_, P_, false>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
+        return true;                                                                         \
     }
-    QL_DECODE_CASE(16, 4, 2) QL_DECODE_CASE(32, 4, 2)
+    QL_DECODE_CASE(16, 1, 2) QL_DECODE_CASE(32, 1, 2) QL_DECODE_CASE(16, 2, 2) QL_DECODE_CASE(32, 2, 2)
 #undef QL_DECODE_CASE
     return false;
 }
@@ -995,7 +1176,7 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
             QL_FAIL(QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
         const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
         if (!launch_decode(p, xw, qw, scales, qz, y, workspace, mi, ni, ki, lg, st))
-            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d t=%d p=%d", who, p.mt, p.t, p.p);
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d r=%d p=%d", who, p.mt, p.r, p.p);
         return launch_status(who);
     }
     const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
@@ -1035,8 +1216,8 @@ extern "C" int ql_w4a16_dequant(const int32_t* qweight, const uint16_t* scales, 
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
     if (!ql::aligned16(w16) || (q_u8 && !ql::aligned16(q_u8)))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
-    const int64_t words = n * (k / 8);
-    const unsigned blocks = (unsigned)std::min<int64_t>((words + 255) / 256, 65536);
+    const int64_t wblocks = n * ((k / 8 + 7) / 8);
+    const unsigned blocks = (unsigned)std::min<int64_t>((wblocks + 255) / 256, 65536);
     hipLaunchKernelGGL(w4a16_dequant_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        reinterpret_cast<const uint32_t*>(qweight), scales, reinterpret_cast<const uint32_t*>(qzeros),
                        w16, q_u8, (int)n, (int)k, group);
