@@ -72,7 +72,10 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
         } else {
             ql::dequant_words_natural<8>(w, zb, s2, v);
         }
-        for (int u = 0; u < nw; ++u) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u >= nw)
+                break;
             uint4 o = __builtin_bit_cast(uint4, v[u]);
             if ((jb & 1) == 0) {
                 const uint32_t a = o.x, b = o.y, c = o.z, d = o.w;   // (0,4)(1,5)(2,6)(3,7)
@@ -192,21 +195,23 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 
     // activation chunks of this thread: chunk tid + 256 u of a block is chunk
     // (tid + 256 u) % 32 of row (tid + 256 u) / 32
-    const uint16_t* xsrc[XPT];
-    int xdst[XPT], xcc[XPT];
+    int xsrc[XPT], xdst[XPT], xcc[XPT];
     bool xok[XPT];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
         const int c = tid + 256 * u, m = c >> 5, cc = c & 31;
         xok[u] = m < mrows;
         xcc[u] = cc;
-        xsrc[u] = x + (int64_t)(m < mrows ? m : mrows - 1) * K + k0;
+        xsrc[u] = (m < mrows ? m : mrows - 1) * K + k0;   // element offset of the row's slice
         xdst[u] = m * 32 + (cc ^ xswz(m));
     }
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
     auto x_load = [&](int j, uint4 (&v)[XPT]) {
 #pragma unroll
-        for (int u = 0; u < XPT; ++u)
-            v[u] = *reinterpret_cast<const uint4*>(xsrc[u] + 8 * min(j * 32 + xcc[u], nch - 1));
+        for (int u = 0; u < XPT; ++u) {
+            const uint32_t e = (uint32_t)(xsrc[u] + 8 * min(j * 32 + xcc[u], nch - 1));
+            v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(e * 2u), 0, 0));
+        }
     };
     auto x_store = [&](int j, const uint4 (&v)[XPT]) {
 #pragma unroll
@@ -1165,6 +1170,9 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
         if (p.slices > 1 && p.nblk > kMaxDecodeBlocks)
             QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld exceeds the decode path's %d column blocks", who, (long long)n,
                     kMaxDecodeBlocks);
+        if (m * k * 2 >= (1LL << 31))
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: decode activations of %lld x %lld exceed 2 GiB", who, (long long)m,
+                    (long long)k);
         if (p.part_bytes >= ((size_t)1 << 32))
             QL_FAIL(QL_ERR_UNSUPPORTED, "%s: m=%lld n=%lld k=%lld needs %zu bytes of partial sums (limit 4 GiB)", who,
                     (long long)m, (long long)n, (long long)k, p.part_bytes);
