@@ -30,6 +30,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base)
     asm volatile("global_load_lds_dwordx4 %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
 }
 
+// 4-byte direct load: each lane's dword at `src` -> LDS `lds_base` + 4 * lane
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base)
+{
+    asm volatile("global_load_lds_dword %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory operations are pending
 // (they complete in issue order) and its LDS reads have returned, then
 // synchronise the workgroup.  Also a compiler barrier for memory accesses.

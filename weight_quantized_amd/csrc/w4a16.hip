@@ -773,11 +773,6 @@ __device__ __forceinline__ void interleave()
     }
 }
 
-// 4-byte direct load: each lane's dword at `src` -> LDS `lds_base` + 4 * lane
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base)
-{
-    asm volatile("global_load_lds_dword %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
-}
 
 template <class C>
 __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __restrict__ x,
@@ -869,7 +864,7 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
                 // 64 rows x 4 bytes, lane l -> row 64 * part + l
                 const bool is_scale = step[u] == -1;
                 const uint8_t* p = src[u] + (is_scale ? soff : zoff);
-                dma4(p, (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
+                ql::dma4(p, (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
             }
         }
     };

@@ -19,6 +19,7 @@
 namespace {
 
 typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef int i16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // QRMSNorm
@@ -379,6 +380,15 @@ __device__ __forceinline__ i4_t mfma_i8(i4_t a, i4_t b, i4_t c)
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// MFMA 32x32x32 int8 -> int32.  Lane l supplies A[l%32][16(l/32) .. +15] and
+// B[16(l/32) .. +15][l%32]; it receives D[8(v/4) + 4(l/32) + v%4][l%32] in
+// element v, v = 0..15.  At one wave per SIMD it sustains over 90% of the
+// int8 peak, against under 60% for the 16x16x64 form.
+__device__ __forceinline__ i16_t mfma_i8_32(i4_t a, i4_t b, i16_t c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
 // tile index of workgroup `wg` so that each XCD gets a contiguous run of tiles
 __device__ __forceinline__ int xcd_tile(int wg, int ntiles)
 {
@@ -451,6 +461,72 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
                     static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][r];
                 else
                     static_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)to_h(i, j, r);
+            }
+    }
+}
+
+// Epilogue of the pipelined kernel (32x32 MFMA tiles, weights as the A
+// operand): fragment (i, j) of a wave holds y rows mrow + 32 i + l%32 and
+// columns ncol + 32 j + 8 (v/4) + 4 (l/32) + v%4, so each lane owns runs of
+// four consecutive columns (8-byte fp16 stores).  Same rounding as store_tile.
+template <int FI, int FJ, bool kRaw>
+__device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const float* __restrict__ xs,
+                                             const float* __restrict__ ws, void* __restrict__ out, int M, int N,
+                                             int mrow, int ncol, bool vec)
+{
+    float xsv[FI], wsv[FJ][16];
+    if (!kRaw) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+            xsv[i] = xs[min(mrow + 32 * i, M - 1)];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                wsv[j][v] = ws[min(ncol + 32 * j + 8 * (v >> 2) + (v & 3), N - 1)];
+    }
+    auto to_h = [&](int i, int j, int v) -> uint32_t {
+        float f = __fmul_rn(__fmul_rn((float)acc[i][j][v], xsv[i]), wsv[j][v]);
+        asm volatile("" : "+v"(f));
+        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    };
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t o = (int64_t)(mrow + 32 * i) * N + ncol + 32 * j + 8 * g;
+                    if (kRaw) {
+                        const i4_t v4 = i4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                             acc[i][j][4 * g + 3]};
+                        *reinterpret_cast<i4_t*>(static_cast<int32_t*>(out) + o) = v4;
+                    } else {
+                        uint2 h;
+                        h.x = to_h(i, j, 4 * g) | (to_h(i, j, 4 * g + 1) << 16);
+                        h.y = to_h(i, j, 4 * g + 2) | (to_h(i, j, 4 * g + 3) << 16);
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = h;
+                    }
+                }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+        const int m = mrow + 32 * i;
+        if (m >= M)
+            continue;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int n = ncol + 32 * j + 8 * (v >> 2) + (v & 3);
+                if (n >= N)
+                    continue;
+                if (kRaw)
+                    static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][v];
+                else
+                    static_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)to_h(i, j, v);
             }
     }
 }
@@ -593,7 +669,7 @@ template <int BM_, int BN_, int BK_, int S_, bool kMapN_>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr bool kMapN = kMapN_;   // tile order: m fastest (true) or n fastest
-    static constexpr int KS = BK / 64;       // MFMA k-steps per stage
+    static constexpr int KS = BK / 32;       // MFMA k-steps per stage
     static constexpr int CH = BK / 16;       // 16-byte chunks per LDS row
     static constexpr int RPB = 1024 / BK;    // rows filled by one 1 KiB wave load
     static constexpr int kStageBytes = (BM + BN) * BK;
@@ -614,7 +690,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
 {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, KS = C::KS, D = C::D;
     constexpr int TM = BM / 2, TN = BN / 2;
-    constexpr int FI = TM / 16, FJ = TN / 16;
+    constexpr int FI = TM / 32, FJ = TN / 32;          // 32x32 MFMA tiles per wave
     extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // S * kStageBytes
 
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -627,7 +703,6 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int q = lane >> 4, r16 = lane & 15;
     const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
 
     // This wave's direct loads: the stage is (BM + BN) rows of BK bytes in
@@ -657,27 +732,29 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
                   (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * C::kStageBytes + dst[u]));
     };
 
-    i4_t acc[FI][FJ];
+    i16_t acc[FI][FJ];
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
-            acc[i][j] = i4_t{0, 0, 0, 0};
+            acc[i][j] = i16_t{};
 
-    // fragments of k-step j of a stage, row-relative with the swizzled chunk
-    const int arow0 = wm * TM + r16, brow0 = BM + wn * TN + r16;
+    // fragments of k-step j (32 bytes of k) of a stage: lane l reads row
+    // l%32 of the fragment, chunk 2j + l/32, swizzled
+    const int r32 = lane & 31, h32 = lane >> 5;
+    const int arow0 = wm * TM + r32, brow0 = BM + wn * TN + r32;
     i4_t fa[2][FI], fb[2][FJ];
     auto read_frags = [&](int slot, int j, i4_t (&af)[FI], i4_t (&bf)[FJ]) {
         const uint8_t* base = pl + slot * C::kStageBytes;
-        const int c = 4 * j + q;
+        const int c = 2 * j + h32;
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
-            const int r = arow0 + 16 * i;
+            const int r = arow0 + 32 * i;
             af[i] = *reinterpret_cast<const i4_t*>(base + r * BK + 16 * (c ^ swz<BK>(r)));
         }
 #pragma unroll
         for (int jj = 0; jj < FJ; ++jj) {
-            const int r = brow0 + 16 * jj;
+            const int r = brow0 + 32 * jj;
             bf[jj] = *reinterpret_cast<const i4_t*>(base + r * BK + 16 * (c ^ swz<BK>(r)));
         }
     };
@@ -711,15 +788,63 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
                     for (int i = 0; i < FI; ++i)
 #pragma unroll
                         for (int jj = 0; jj < FJ; ++jj)
-                            acc[i][jj] = mfma_i8(fb[cur][jj], fa[cur][i], acc[i][jj]);
+                            acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
                 }
             }
         }
     }
     ql::stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
 
-    const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
-    store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+    if constexpr (!kRaw) {
+        if (full && (N & 7) == 0) {
+            // Whole tile: each wave converts its TM x TN sub-tile to fp16 into
+            // its own LDS area (row pitch TN + 8 halves), then writes whole
+            // 16-byte chunks of whole rows, TN / 8 lanes per row, so every
+            // store instruction fills complete 128-byte lines.  (The MFMA layout
+            // alone would give each lane runs of 4 columns in 32 rows.)
+            constexpr int PITCH = TN + 8;
+            static_assert(4 * TM * PITCH * 2 <= C::kLds, "epilogue staging fits the stage ring");
+            uint16_t* ot = reinterpret_cast<uint16_t*>(pl) + wave * TM * PITCH;
+            float xsv[FI], wsv[FJ][16];
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+                xsv[i] = xs[m0 + wm * TM + 32 * i + r32];
+#pragma unroll
+            for (int jj = 0; jj < FJ; ++jj)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    wsv[jj][v] = ws[n0 + wn * TN + 32 * jj + 8 * (v >> 2) + 4 * h32 + (v & 3)];
+            auto to_h = [&](int i, int jj, int v) -> uint32_t {
+                float f = __fmul_rn(__fmul_rn((float)acc[i][jj][v], xsv[i]), wsv[jj][v]);
+                asm volatile("" : "+v"(f));
+                return __builtin_bit_cast(uint16_t, (_Float16)f);
+            };
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int jj = 0; jj < FJ; ++jj)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        uint2 h;
+                        h.x = to_h(i, jj, 4 * g) | (to_h(i, jj, 4 * g + 1) << 16);
+                        h.y = to_h(i, jj, 4 * g + 2) | (to_h(i, jj, 4 * g + 3) << 16);
+                        *reinterpret_cast<uint2*>(ot + (32 * i + r32) * PITCH + 32 * jj + 8 * g + 4 * h32) = h;
+                    }
+            constexpr int LPR = TN / 8;             // lanes per row
+            constexpr int RPI = 64 / LPR;           // rows per store instruction
+            uint16_t* yb = static_cast<uint16_t*>(out) + (int64_t)(m0 + wm * TM) * N + n0 + wn * TN;
+#pragma unroll
+            for (int it = 0; it < TM / RPI; ++it) {
+                const int row = it * RPI + lane / LPR, c = lane % LPR;
+                const uint4 v = *reinterpret_cast<const uint4*>(ot + row * PITCH + 8 * c);
+                *reinterpret_cast<uint4*>(yb + (int64_t)row * N + 8 * c) = v;
+            }
+            return;
+        }
+    }
+    store_tile32<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r32, n0 + wn * TN + 4 * h32,
+                               full && (N & 3) == 0);
 }
 
 using Pipe = PipeCfg<kQBM, kQBN, 128, 3, true>;
