@@ -682,7 +682,7 @@ struct PipeCfg {
 };
 
 template <class C, bool kRaw>
-__global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
+__global__ __launch_bounds__(256, 2) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
                                                              const float* __restrict__ ws, void* __restrict__ out,
@@ -796,16 +796,17 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
     ql::stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
 
     const bool full = m0 + BM <= M && n0 + BN <= N;
-    if constexpr (!kRaw) {
+    // Whole tile: each wave converts its TM x TN sub-tile to fp16 through its
+    // own LDS area (half the rows at a time, row pitch TN + 8 halves), then
+    // writes whole 16-byte chunks of whole rows, TN / 8 lanes per row, so every
+    // store instruction fills complete 128-byte lines.  (The MFMA layout alone
+    // would give each lane runs of 4 columns in 32 rows.)
+    constexpr int PITCH = TN + 8;
+    constexpr int HALF = TM / 2;
+    constexpr bool kStaged = 4 * HALF * PITCH * 2 <= C::kLds && FI % 2 == 0;
+    if constexpr (!kRaw && kStaged) {
         if (full && (N & 7) == 0) {
-            // Whole tile: each wave converts its TM x TN sub-tile to fp16 into
-            // its own LDS area (row pitch TN + 8 halves), then writes whole
-            // 16-byte chunks of whole rows, TN / 8 lanes per row, so every
-            // store instruction fills complete 128-byte lines.  (The MFMA layout
-            // alone would give each lane runs of 4 columns in 32 rows.)
-            constexpr int PITCH = TN + 8;
-            static_assert(4 * TM * PITCH * 2 <= C::kLds, "epilogue staging fits the stage ring");
-            uint16_t* ot = reinterpret_cast<uint16_t*>(pl) + wave * TM * PITCH;
+            uint16_t* ot = reinterpret_cast<uint16_t*>(pl) + wave * HALF * PITCH;
             float xsv[FI], wsv[FJ][16];
 #pragma unroll
             for (int i = 0; i < FI; ++i)
@@ -820,25 +821,29 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
                 asm volatile("" : "+v"(f));
                 return __builtin_bit_cast(uint16_t, (_Float16)f);
             };
-#pragma unroll
-            for (int i = 0; i < FI; ++i)
-#pragma unroll
-                for (int jj = 0; jj < FJ; ++jj)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        uint2 h;
-                        h.x = to_h(i, jj, 4 * g) | (to_h(i, jj, 4 * g + 1) << 16);
-                        h.y = to_h(i, jj, 4 * g + 2) | (to_h(i, jj, 4 * g + 3) << 16);
-                        *reinterpret_cast<uint2*>(ot + (32 * i + r32) * PITCH + 32 * jj + 8 * g + 4 * h32) = h;
-                    }
             constexpr int LPR = TN / 8;             // lanes per row
             constexpr int RPI = 64 / LPR;           // rows per store instruction
-            uint16_t* yb = static_cast<uint16_t*>(out) + (int64_t)(m0 + wm * TM) * N + n0 + wn * TN;
 #pragma unroll
-            for (int it = 0; it < TM / RPI; ++it) {
-                const int row = it * RPI + lane / LPR, c = lane % LPR;
-                const uint4 v = *reinterpret_cast<const uint4*>(ot + row * PITCH + 8 * c);
-                *reinterpret_cast<uint4*>(yb + (int64_t)row * N + 8 * c) = v;
+            for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                for (int i = hf * FI / 2; i < (hf + 1) * FI / 2; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FJ; ++jj)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            uint2 h;
+                            h.x = to_h(i, jj, 4 * g) | (to_h(i, jj, 4 * g + 1) << 16);
+                            h.y = to_h(i, jj, 4 * g + 2) | (to_h(i, jj, 4 * g + 3) << 16);
+                            *reinterpret_cast<uint2*>(ot + (32 * (i - hf * FI / 2) + r32) * PITCH + 32 * jj + 8 * g +
+                                                      4 * h32) = h;
+                        }
+                uint16_t* yb = static_cast<uint16_t*>(out) + (int64_t)(m0 + wm * TM + hf * HALF) * N + n0 + wn * TN;
+#pragma unroll
+                for (int it = 0; it < HALF / RPI; ++it) {
+                    const int row = it * RPI + lane / LPR, c = lane % LPR;
+                    const uint4 v = *reinterpret_cast<const uint4*>(ot + row * PITCH + 8 * c);
+                    *reinterpret_cast<uint4*>(yb + (int64_t)row * N + 8 * c) = v;
+                }
             }
             return;
         }
@@ -847,7 +852,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_pipe_kernel(const int8_t* __res
                                full && (N & 3) == 0);
 }
 
-using Pipe = PipeCfg<kQBM, kQBN, 128, 3, true>;
+using Pipe = PipeCfg<kQBM, kQBN, 64, 3, true>;
 
 template <bool kRaw>
 void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, void* out, int64_t m,
