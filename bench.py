@@ -51,7 +51,7 @@ def w4a16_bytes(m, n, k, g):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("w4a16.hip", "dequant.hpp"):
+    for f in ("w4a16.hip", "dequant.hpp", "lds_dma.hpp"):
         with open(os.path.join(ROOT, "weight_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -48,7 +48,13 @@ __device__ __forceinline__ void stage_barrier()
 
 //   64-byte rows (4 chunks), lane quarter q reads chunk q
 __device__ __forceinline__ int swz64(int r) { return (r >> 2) & 2; }
-//   128-byte rows (8 chunks), lane quarter q reads chunk 4j + q
+// Rows read by 32-row MFMA fragments (lane half h reads chunk 2j + h of row
+// l % 32), swizzles measured free of bank conflicts on gfx950:
+//   64-byte rows (4 chunks); swz64 above conflicts 2-way here
+__device__ __forceinline__ int swz64x32(int r) { return (r >> 3) & 3; }
+//   128-byte rows (8 chunks): swz128 below, which also serves 16-row reads
+//
+// 128-byte rows (8 chunks), lane quarter q reads chunk 4j + q
 __device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 //   256-byte rows (16 chunks), lane quarter q reads chunk 4q + s: the linear
 //   map with bit images 1 -> 4, 2 -> 2, 4 -> 8, 8 -> 3 on the low four row bits

@@ -162,6 +162,141 @@ constexpr int decode_wg_per_cu()
     return R > 1 ? 1 : (MT == 16 ? 3 : 2);
 }
 
+// Scale and zero-point tables of TW channels [n0, n0 + TW) for the groups
+// [g0, g0 + gs) of a slice, staged in LDS as dwords: per channel SD dwords of
+// scales starting at the even element at or below its first group (the dword
+// holding it), then per channel ZD words of zero points.  (The scales are read
+// in 4-byte units, up to the 4-byte boundary at or after their end.)  load()
+// requests a batch of SB scale dwords and ZB zero words per thread; store_all()
+// writes it to LDS, then loads and writes any further batches.  Threads past
+// the end rewrite the last entry with its own value, so no load has a
+// conditional use the compiler could sink it into; each table has its own loop,
+// since a per-lane choice of buffer resource would make the compiler loop over
+// the distinct resources.
+template <int TW, int SB, int ZB>
+struct DecodeTables {
+    __amdgpu_buffer_rsrc_t rsc, rzr;
+    int n0, N, NG, ZW, g0, SD, ZD, stot, ztot;
+    uint32_t sv[SB], zv[ZB];
+
+    __device__ __forceinline__ DecodeTables(const uint16_t* sc, const uint32_t* qz, int n0_, int N_, int NG_,
+                                            int ZW_, int g0_, int gs)
+        : n0(n0_), N(N_), NG(NG_), ZW(ZW_), g0(g0_)
+    {
+        rsc = make_rsrc(sc, ((uint32_t)N * (uint32_t)NG * 2u + 3u) & ~3u);
+        rzr = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
+        SD = (gs >> 1) + 1;
+        ZD = (gs >> 3) + 2;
+        stot = TW * SD;
+        ztot = TW * ZD;
+    }
+    __device__ __forceinline__ void load(int e0, int z0)
+    {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int e = min(e0 + u * 256 + tid, stot - 1);
+            const int rr = e / SD, col = e - rr * SD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t dw = ((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col;
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(dw * 4u), 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < ZB; ++u) {
+            const int e = min(z0 + u * 256 + tid, ztot - 1);
+            const int rr = e / ZD, col = e - rr * ZD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t wd = row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col;
+            zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rzr, (int)(wd * 4u), 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(uint32_t* tab, int e0, int z0) const
+    {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+            tab[min(e0 + u * 256 + tid, stot - 1)] = sv[u];
+#pragma unroll
+        for (int u = 0; u < ZB; ++u)
+            tab[stot + min(z0 + u * 256 + tid, ztot - 1)] = zv[u];
+    }
+    // the first batch was requested by load(0, 0)
+    __device__ __forceinline__ void store_all(uint32_t* tab)
+    {
+        store(tab, 0, 0);
+        for (int e0 = SB * 256, z0 = ZB * 256; e0 < stot || z0 < ztot; e0 += SB * 256, z0 += ZB * 256) {
+            load(e0, z0);
+            store(tab, e0, z0);
+        }
+    }
+    // element offset of a channel's first group within its scale dwords
+    __device__ __forceinline__ int parity(int rr) const
+    {
+        return (int)(((uint32_t)min(n0 + rr, N - 1) * (uint32_t)NG + (uint32_t)g0) & 1u);
+    }
+};
+
+// Split-K completion, after this thread's agent-scope stores of its part of
+// the workgroup's partial tile ([M][TW] fp32 at part[(slice * nblk + column
+// block) * M * TW]): wait for them, arrive on the column block's counter, and
+// if this workgroup arrived last, sum the S tiles in slice order and store y.
+// Each thread of the last workgroup owns four consecutive columns of one row;
+// the slices' 16-byte pieces are read with agent-scope buffer loads, eight
+// slices in flight at a time.  The last arrival resets the counter.
+template <int TW>
+__device__ __forceinline__ void splitk_finish(float* __restrict__ part, uint32_t* __restrict__ cnt,
+                                              uint16_t* __restrict__ y, int M, int N, int n0, int* s_last)
+{
+    const int S = gridDim.y, nblk = gridDim.x, tid = threadIdx.x;
+    __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
+    __syncthreads();                    // ... and so have every other thread's
+    if (tid == 0) {
+        const uint32_t prev =
+            __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (prev == (uint32_t)(S - 1));
+    }
+    __syncthreads();
+    if (!*s_last)
+        return;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)((int64_t)S * nblk * M * TW * (int64_t)sizeof(float)));
+    constexpr int kSc1 = 16;                  // cache policy: agent scope (bypasses this CU's L1)
+    const uint32_t tile_bytes = (uint32_t)(M * TW * sizeof(float));
+    const uint32_t col_bytes = (uint32_t)blockIdx.x * tile_bytes;
+    const uint32_t slice_bytes = (uint32_t)nblk * tile_bytes;
+    for (int v = tid; v < M * (TW / 4); v += blockDim.x) {
+        const uint32_t off = col_bytes + (uint32_t)v * 16u;
+        f4_t sum = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += 8) {
+            f4_t pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sl = min(s0 + u, S - 1);
+                pv[u] = __builtin_bit_cast(
+                    f4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (int)(off + (uint32_t)sl * slice_bytes), 0, kSc1));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < S)
+                    sum += pv[u];
+        }
+        const int m = v / (TW / 4), nn = n0 + (v % (TW / 4)) * 4;
+        uint16_t* yr = y + (int64_t)m * N;
+        if (nn + 3 < N && (N & 3) == 0) {
+            uint2 h;
+            h.x = f32_to_f16_bits(sum[0]) | ((uint32_t)f32_to_f16_bits(sum[1]) << 16);
+            h.y = f32_to_f16_bits(sum[2]) | ((uint32_t)f32_to_f16_bits(sum[3]) << 16);
+            *reinterpret_cast<uint2*>(yr + nn) = h;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (nn + e < N)
+                    yr[nn + e] = f32_to_f16_bits(sum[e]);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int MT, int R, int P, bool POST>
 __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
@@ -221,48 +356,9 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
         }
     };
 
-    // scales and zero points of this workgroup's channels and slice, as
-    // dwords: per channel SD dwords of scales starting at the even element at
-    // or below its first group (the dword holding it), then ZD words of zero
-    // points.  (The scales are read in 4-byte units, up to the 4-byte
-    // boundary at or after their end.)
-    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(sc, ((uint32_t)N * (uint32_t)NG * 2u + 3u) & ~3u);
-    const __amdgpu_buffer_rsrc_t rzr = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
+    // scale and zero-point tables of this workgroup's channels and slice
     const int g0 = k0 >> lg;
-    const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
-    const int stot = TW * SD, ztot = TW * ZD;     // scale dwords, zero-point words
-    constexpr int kSB = 6 * R, kZB = 2 * R;       // entries per thread and batch
-    uint32_t sv[kSB], zv[kZB];
-    // (each table has its own loop: a per-lane choice of buffer resource
-    // would make the compiler loop over the distinct resources)
-    auto tab_load = [&](int e0, int z0) {
-#pragma unroll
-        for (int u = 0; u < kSB; ++u) {
-            const int e = min(e0 + u * 256 + tid, stot - 1);
-            const int rr = e / SD, col = e - rr * SD;
-            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
-            const uint32_t dw = ((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col;
-            sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)(dw * 4u), 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < kZB; ++u) {
-            const int e = min(z0 + u * 256 + tid, ztot - 1);
-            const int rr = e / ZD, col = e - rr * ZD;
-            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
-            const uint32_t wd = row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col;
-            zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rzr, (int)(wd * 4u), 0, 0);
-        }
-    };
-    // (threads past the end rewrite the last entry with its own value, so the
-    // loads above have no conditional use the compiler could sink them into)
-    auto tab_store = [&](int e0, int z0) {
-#pragma unroll
-        for (int u = 0; u < kSB; ++u)
-            tab[min(e0 + u * 256 + tid, stot - 1)] = sv[u];
-#pragma unroll
-        for (int u = 0; u < kZB; ++u)
-            tab[stot + min(z0 + u * 256 + tid, ztot - 1)] = zv[u];
-    };
+    DecodeTables<TW, 6 * R, 2 * R> tb(sc, qz, n0, N, NG, ZW, g0, gs);
 
     // weights: block b of this lane's tile t, two 16-byte pieces
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
@@ -284,7 +380,7 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
     // 1. requests: tables, then activations and weights of the first P blocks
     //    (weights past the slice re-read block nb-1, so every wait in the
     //    stream has a static count)
-    tab_load(0, 0);
+    tb.load(0, 0);
     uint4 ring[P][R][2];
     uint4 xr[P][XPT];
 #pragma unroll
@@ -294,11 +390,7 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
         __builtin_amdgcn_sched_barrier(0);
     }
     // 2. tables and block 0's activations -> LDS
-    tab_store(0, 0);
-    for (int e0 = kSB * 256, z0 = kZB * 256; e0 < stot || z0 < ztot; e0 += kSB * 256, z0 += kZB * 256) {
-        tab_load(e0, z0);
-        tab_store(e0, z0);
-    }
+    tb.store_all(tab);
     x_store(0, xr[0]);
     __syncthreads();
 
@@ -333,8 +425,7 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 #pragma unroll
     for (int t = 0; t < R; ++t) {
         trow[t] = (wave * R + t) * 16 + r16;
-        const uint32_t row = (uint32_t)min(n0 + trow[t], N - 1);
-        spar[t] = (int)((row * (uint32_t)NG + (uint32_t)g0) & 1u);
+        spar[t] = tb.parity(trow[t]);
     }
 
     for (int b0 = 0; b0 < nbp; b0 += P) {
@@ -358,8 +449,8 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
             uint32_t s16[R][2];
 #pragma unroll
             for (int t = 0; t < R; ++t) {
-                const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + trow[t] * SD);
-                const uint32_t* zrow = tab + stot + trow[t] * ZD;
+                const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + trow[t] * tb.SD);
+                const uint32_t* zrow = tab + tb.stot + trow[t] * tb.ZD;
                 const uint32_t za_ = (zrow[((g0 + ga) >> 3) - (g0 >> 3)] >> (4 * ((g0 + ga) & 7))) & 0xFu;
                 const uint32_t zb_ = (zrow[((g0 + gb) >> 3) - (g0 >> 3)] >> (4 * ((g0 + gb) & 7))) & 0xFu;
                 s16[t][0] = srow[spar[t] + ga];
@@ -462,11 +553,9 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
         return;
     }
 
-    // 6. split-K: publish this slice's partial tile -- [M][TW] fp32, row-major,
-    //    at part[(slice * nblk + column block) * M * TW] -- with agent-scope
-    //    stores, wait for them, then arrive
-    const int nblk = gridDim.x;
-    float* tile = part + ((int64_t)blockIdx.y * nblk + blockIdx.x) * (int64_t)M * TW;
+    // 6. split-K: this slice's partial tile with agent-scope stores, then
+    //    the arrival and the last arrival's reduction
+    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)M * TW;
 #pragma unroll
     for (int t = 0; t < R; ++t)
 #pragma unroll
@@ -478,60 +567,7 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
                     __hip_atomic_store(&tile[m * TW + (wave * R + t) * 16 + r16], res[t][i][r], __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
-    __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
-    __syncthreads();                    // ... and so have every other thread's
-    if (tid == 0) {
-        const uint32_t prev =
-            __hip_atomic_fetch_add(&cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (uint32_t)(S - 1));
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    // The last arrival sums the S tiles in slice order.  Each thread owns four
-    // consecutive columns of one row; the slices' 16-byte pieces are read with
-    // agent-scope buffer loads, eight slices in flight at a time.
-    {
-        const __amdgpu_buffer_rsrc_t rp =
-            make_rsrc(part, (uint32_t)((int64_t)S * nblk * M * TW * (int64_t)sizeof(float)));
-        constexpr int kSc1 = 16;                  // cache policy: agent scope (bypasses this CU's L1)
-        const uint32_t tile_bytes = (uint32_t)(M * TW * sizeof(float));
-        const uint32_t col_bytes = (uint32_t)blockIdx.x * tile_bytes;
-        const uint32_t slice_bytes = (uint32_t)nblk * tile_bytes;
-        for (int v = tid; v < M * (TW / 4); v += 256) {
-            const uint32_t off = col_bytes + (uint32_t)v * 16u;
-            f4_t sum = f4_t{0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < S; s0 += 8) {
-                f4_t pv[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int sl = min(s0 + u, S - 1);
-                    pv[u] = __builtin_bit_cast(
-                        f4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (int)(off + (uint32_t)sl * slice_bytes), 0,
-                                                                    kSc1));
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (s0 + u < S)
-                        sum += pv[u];
-            }
-            const int m = v / (TW / 4), nn = n0 + (v % (TW / 4)) * 4;
-            uint16_t* yr = y + (int64_t)m * N;
-            if (nn + 3 < N && (N & 3) == 0) {
-                uint2 h;
-                h.x = f32_to_f16_bits(sum[0]) | ((uint32_t)f32_to_f16_bits(sum[1]) << 16);
-                h.y = f32_to_f16_bits(sum[2]) | ((uint32_t)f32_to_f16_bits(sum[3]) << 16);
-                *reinterpret_cast<uint2*>(yr + nn) = h;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (nn + e < N)
-                        yr[nn + e] = f32_to_f16_bits(sum[e]);
-            }
-        }
-    }
-    if (tid == 0)
-        __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    splitk_finish<TW>(part, cnt, y, M, N, n0, &s_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1107,6 +1143,7 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                    const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
+
 #define QL_DECODE_CASE(MT_, R_, P_)                                                          \
     if (p.mt == MT_ && p.r == R_ && p.p == P_) {                                             \
         if (p.post)                                                                          \

@@ -656,13 +656,13 @@ constexpr int kQBM = 256, kQBN = 128;
 // whole previous stage, whose slot is then refilled.
 //
 // LDS rows are BK bytes (BK/16 chunks of 16).  Logical chunk c of tile row r
-// sits at physical chunk c ^ f(r), f = the shared 64- or 128-byte-row swizzle,
-// which keeps the fragment reads free of bank conflicts.
+// sits at physical chunk c ^ f(r), f = a 64-byte-row swizzle for 32-row fragments
+// or the 128-byte-row one, measured free of bank conflicts for these reads.
 // ---------------------------------------------------------------------------
 template <int BK>
 __device__ __forceinline__ int swz(int r)
 {
-    return BK == 64 ? ql::swz64(r) : ql::swz128(r);
+    return BK == 64 ? ql::swz64x32(r) : ql::swz128(r);
 }
 
 template <int BM_, int BN_, int BK_, int S_, bool kMapN_>
@@ -675,14 +675,14 @@ struct PipeCfg {
     static constexpr int kStageBytes = (BM + BN) * BK;
     static constexpr int kLds = S * kStageBytes;
     static constexpr int D = (BM + BN) / RPB / 4;   // direct loads per wave per stage
+    static constexpr int kWgPerCu = kLds <= 80 * 1024 ? 2 : 1;   // workgroups that fit one CU's LDS
     static_assert(BK == 64 || BK == 128, "k-tile of 64 or 128 bytes");
     static_assert((BM + BN) % (4 * RPB) == 0 && BM % RPB == 0, "whole 1 KiB blocks, X/W split on a block");
-    static_assert((S * KS) % 2 == 0, "register buffer index taken from the unrolled step");
     static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
 };
 
 template <class C, bool kRaw>
-__global__ __launch_bounds__(256, 2) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
+__global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
                                                              const float* __restrict__ ws, void* __restrict__ out,
@@ -767,31 +767,37 @@ __global__ __launch_bounds__(256, 2) void w8a8_gemm_pipe_kernel(const int8_t* __
     ql::stage_barrier<D * (S - 1)>();   // tile 0 landed
     read_frags(0, 0, fa[0], fb[0]);
 
-    for (int kt0 = 0; kt0 < nk; kt0 += S) {
+    // One k-tile per iteration with its KS steps unrolled and no branch
+    // inside: the last tile, too, refills its slot (with itself) and reads
+    // fragments of the next slot that are never used.  A branch there would
+    // join two paths, and the compiler's LDS wait before the last step's
+    // MFMAs would then also cover the next tile's reads issued just before.
+    static_assert(KS % 2 == 0, "register buffer index restarts with each tile");
+    for (int kt = 0, slot = 0; kt < nk; ++kt) {
+        const int next = slot + 1 == S ? 0 : slot + 1;
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int kt = kt0 + s;
-            if (kt < nk) {
-#pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                    const int cur = (s * KS + j) & 1;
-                    if (j + 1 < KS) {
-                        read_frags(s, j + 1, fa[cur ^ 1], fb[cur ^ 1]);
-                    } else if (kt + 1 < nk) {
-                        // tile kt+1 landed (S-2 younger tiles may be pending) and
-                        // every wave has read tile kt: refill its slot
-                        ql::stage_barrier<D * (S - 2)>();
-                        issue(kt + S < nk ? kt + S : nk - 1, s);
-                        read_frags((s + 1) % S, 0, fa[cur ^ 1], fb[cur ^ 1]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < FI; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < FJ; ++jj)
-                            acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
-                }
+        for (int j = 0; j < KS; ++j) {
+            const int cur = j & 1;
+            if (j + 1 < KS) {
+                read_frags(slot, j + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            } else {
+                // tile kt+1 landed (S-2 younger tiles may be pending) and
+                // every wave has read tile kt: refill its slot
+                ql::stage_barrier<D * (S - 2)>();
+                issue(kt + S < nk ? kt + S : nk - 1, slot);
+                read_frags(next, 0, fa[cur ^ 1], fb[cur ^ 1]);
             }
+            // keep the reads ahead of this step's MFMAs (the scheduler would
+            // otherwise sink each read to its use in the next step)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int jj = 0; jj < FJ; ++jj)
+                    acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        slot = next;
     }
     ql::stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
 
