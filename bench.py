@@ -18,9 +18,12 @@ algorithmic bytes per launch over that kernel's launches divided by their
 average duration, measured with HIP events around graphs of back-to-back
 launches on the launch stream.  `traffic` is filled from the committed
 rocprofv3 counter summary when it was taken on the current kernel source.
+`detail` gives every launch of the step its graph-averaged duration and the
+p10 / median / p90 of 100 single launches (event pairs, cold weights).
 `extra` reports the W4A16 prefill GEMM (M=512 fused QKV) and the W8A8 layer
-(QRMSNorm + int8 GEMM, M=2048) against their rooflines.  `cpu_baseline` times
-the CPU oracle on a bounded sample of the same step.
+(QRMSNorm + int8 GEMM, M=2048) against their rooflines.  `reference` is a
+plain device copy's rate, the achievable HBM bandwidth on the device.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -66,7 +69,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
-                    help="output channels per launch for the oracle sample (0 = auto)")
+                    help="output channels per launch for the oracle sample (0 = all of them)")
     ap.add_argument("--profile-launch", metavar="SHAPE,M",
                     help="run one workload for counter collection and exit: gate_up,M or down,M (decode, cold "
                          "weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM); then a plain "
@@ -99,6 +102,35 @@ def time_graph(torch, g, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def launch_percentiles(torch, fns, blocker):
+    """p10 / median / p90 of single-launch durations (us): each launch is
+    bracketed by its own HIP events on the launch stream.  All launches are
+    enqueued while `blocker` keeps the GPU busy, so they run back to back and
+    no event pair includes host enqueue time."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+    torch.cuda.synchronize()
+    blocker()
+    for (a, b), f in zip(ev, fns):
+        a.record()
+        f()
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return [float(v) for v in np.percentile(us, [10, 50, 90])]
+
+
+def copy_rate(torch, dev, nbytes=1 << 30, reps=8):
+    """Plain device-to-device copy (torch copy_), read + write bytes per second
+    in GB/s: the achievable-bandwidth reference on this device."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    g = capture(torch, [lambda: b.copy_(a)])
+    ms = time_graph(torch, g, reps)
+    del g, a, b
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -163,6 +195,19 @@ def main():
         per[(name, m)] = time_graph(torch, g, reps) * 1e3 / args.copies      # us per launch
         del g
 
+    # ---------------- single-launch percentiles: 100 eager launches per shape, cold copies
+    pct = {}
+    big = [torch.empty(1 << 30, dtype=torch.uint8, device=dev) for _ in range(2)]
+
+    def blocker():
+        for _ in range(12):
+            big[1].copy_(big[0])
+
+    for name, m in launches:
+        pct[(name, m)] = launch_percentiles(torch, [launch(name, m, c) for c in range(100)], blocker)
+    del big
+    copy_gbs = copy_rate(torch, dev)
+
     # ---------------- the step: graphs rotating the weight copies
     nphase = args.copies // np.gcd(len(launches), args.copies)
     step_graphs = [capture(torch, [launch(name, m, p * len(launches) + i) for i, (name, m) in enumerate(launches)])
@@ -186,9 +231,12 @@ def main():
         n, k, g = shapes[name]
         b = w4a16_bytes(m, n, k, g)
         us = per[(name, m)]
+        p10, p50, p90 = pct[(name, m)]
         detail.append({"shape": name, "m": m, "n": n, "k": k, "us": round(us, 2),
                        "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-                       "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+                       "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "single_launch_us": {"p10": round(p10, 2), "median": round(p50, 2), "p90": round(p90, 2),
+                                            "launches": 100}})
     dom = max(launches, key=lambda key: per[key])
     n, k, g = shapes[dom[0]]
     dom_bytes = w4a16_bytes(dom[1], n, k, g)
@@ -223,6 +271,9 @@ def main():
                    "group": GROUP, "m": list(DECODE_M), "cold_weight_copies": args.copies,
                    "bytes_per_step": step_bytes, "launch": "hip graph per step"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "extra": extra,
+        "reference": {"d2d_copy_GBps": round(copy_gbs, 1),
+                      "note": "torch copy_ of 1 GiB on the device, read + write bytes; "
+                              "achievable HBM rate on this device (fractions stay against 8 TB/s)"},
     }
     print(json.dumps(line), flush=True)
 
@@ -288,7 +339,7 @@ def cpu_baseline(host, shapes, launches, rows_opt, log):
     import workloads
 
     cores = oracle.num_threads()
-    rows_per_opt = rows_opt or 2048
+    rows_per_opt = rows_opt or max(shapes[name][0] for name in shapes)   # the whole step: ~8 s on 16 cores
     total_bytes = 0.0
     total_s = 0.0
     for name, m in launches:
