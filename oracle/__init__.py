@@ -49,6 +49,9 @@ def _load():
         "or_quant_rmsnorm": (C.c_int, [_p, _i64, _i64, _p, C.c_float, _p, _p, _p]),
         "or_int8_gemm": (C.c_int, [_p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
         "or_w8a8_forward": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
+        "or_add_quant_rmsnorm": (C.c_int, [_p, _p, _i64, _i64, _p, C.c_float, _p, _p, _p, _p]),
+        "or_quant_per_token": (C.c_int, [_p, _i64, _i64, _p, _p]),
+        "or_w8a8_forward_ex": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p]),
         "or_sumsq_exact": (None, [_p, _i64, _p, _p]),
         "or_ratio_to_f32_parts": (C.c_float, [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int]),
         "or_num_threads": (C.c_int, []),
@@ -243,6 +246,34 @@ def quant_rmsnorm(x, gamma, eps=1e-6, return_ms=False):
     return (xq, sc, ms) if return_ms else (xq, sc)
 
 
+def add_quant_rmsnorm(x, residual, gamma, eps=1e-6):
+    """Step 7: (h fp16 bits uint16 [m,k], xq int8 [m,k], x_scale float32 [m])."""
+    lib = _load()
+    x = _bits16(x)
+    r = _bits16(residual)
+    g = _bits16(gamma)
+    m, k = x.shape
+    if r.shape != (m, k):
+        raise ValueError("residual shape differs from x")
+    h = np.empty((m, k), np.uint16)
+    xq = np.empty((m, k), np.int8)
+    sc = np.empty(m, np.float32)
+    _check(lib.or_add_quant_rmsnorm(_ptr(x), _ptr(r), m, k, _ptr(g), float(eps), _ptr(h), _ptr(xq), _ptr(sc),
+                                    None), "add_quant_rmsnorm")
+    return h, xq, sc
+
+
+def quant_per_token(x):
+    """Step 8: (xq int8 [m,k], x_scale float32 [m])."""
+    lib = _load()
+    x = _bits16(x)
+    m, k = x.shape
+    xq = np.empty((m, k), np.int8)
+    sc = np.empty(m, np.float32)
+    _check(lib.or_quant_per_token(_ptr(x), m, k, _ptr(xq), _ptr(sc)), "quant_per_token")
+    return xq, sc
+
+
 def int8_gemm(xq, wq, rows=None, cols=None):
     """Step 5: exact int64 acc [rows, cols] = xq[rows] @ wq[cols].T."""
     lib = _load()
@@ -275,6 +306,32 @@ def w8a8_forward(xq, x_scale, wq, w_scale, rows=None, cols=None):
     y = np.empty((nr, nc), np.float64)
     _check(lib.or_w8a8_forward(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(r), nr, _ptr(c), nc,
                                _ptr(y)), "w8a8_forward")
+    return y
+
+
+def w8a8_forward_ex(xq, x_scale, wq, w_scale, bias=None, residual=None, rows=None, cols=None):
+    """Step 9: y float64 [rows, cols] = acc * x_scale * w_scale + bias + residual
+    (bias fp16 [n], residual fp16 [m, n], either None)."""
+    lib = _load()
+    xq = _c(xq, np.int8)
+    wq = _c(wq, np.int8)
+    xs = _c(x_scale, np.float32)
+    ws = _c(w_scale, np.float32)
+    m, k = xq.shape
+    n = wq.shape[0]
+    b = None if bias is None else _bits16(bias)
+    res = None if residual is None else _bits16(residual)
+    if b is not None and b.shape != (n,):
+        raise ValueError("bias must be [n]")
+    if res is not None and res.shape != (m, n):
+        raise ValueError("residual must be [m, n]")
+    r = None if rows is None else _c(rows, np.int64)
+    c = None if cols is None else _c(cols, np.int64)
+    nr = m if r is None else len(r)
+    nc = n if c is None else len(c)
+    y = np.empty((nr, nc), np.float64)
+    _check(lib.or_w8a8_forward_ex(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(b), _ptr(res), _ptr(r), nr,
+                                  _ptr(c), nc, _ptr(y)), "w8a8_forward_ex")
     return y
 
 

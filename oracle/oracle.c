@@ -38,6 +38,14 @@
  *        mean(x^2) is the exact mean rounded once to fp32.
  *     5. acc = sum_j xq * wq in exact integer arithmetic.
  *     6. y = acc * x_scale * w_scale (fp64).
+ *   The same guide's kernel list adds the steps on either side of the path:
+ *     7. residual fusion of the norm: h = fp16(x + residual), the new
+ *        residual stream, then step 4 on h.
+ *     8. per-token quantisation of a plain activation (a QLinear whose input
+ *        did not come from QRMSNorm): x_scale = max|x| / 127,
+ *        xq = clamp(rint(x / x_scale), -127, 127).
+ *     9. the GEMM epilogue with an optional bias [n] and residual [m, n]:
+ *        y = acc * x_scale * w_scale + bias + residual (fp64).
  *
  * Rounding: rintf under the default environment (nearest, ties to even).
  * Built with -ffp-contract=off so every fp32 operation rounds on its own.
@@ -460,6 +468,47 @@ int or_quant_rmsnorm(const uint16_t* x, int64_t m, int64_t k, const uint16_t* ga
 }
 
 /*
+ * Step 7 for m tokens: h = fp16(x + residual) element by element, then step 4
+ * on h.  The fp32 sum of two binary16 values rounded to binary16 is the
+ * correctly rounded sum (24 >= 2 * 11 + 2 bits, so the double rounding is
+ * innocuous).  h fp16 [m, k] (written; may not alias x or residual here).
+ */
+int or_add_quant_rmsnorm(const uint16_t* x, const uint16_t* residual, int64_t m, int64_t k,
+                         const uint16_t* gamma, float eps, uint16_t* h, int8_t* xq, float* x_scale,
+                         float* ms_out)
+{
+    if (k <= 0)
+        return OR_BAD;
+    for (int64_t i = 0; i < m * k; ++i)
+        h[i] = or_f32_to_f16(or_f16_to_f32(x[i]) + or_f16_to_f32(residual[i]));
+    return or_quant_rmsnorm(h, m, k, gamma, eps, xq, x_scale, ms_out);
+}
+
+/*
+ * Step 8 for m tokens: x fp16 [m, k] -> xq int8 [m, k], x_scale float32 [m].
+ * The scale and the quotient are fp32 divisions; a zero row gets scale 0 and
+ * codes 0.
+ */
+int or_quant_per_token(const uint16_t* x, int64_t m, int64_t k, int8_t* xq, float* x_scale)
+{
+    if (k <= 0)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        const uint16_t* xr = x + i * k;
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j)
+            if (fabsf(or_f16_to_f32(xr[j])) > amax)
+                amax = fabsf(or_f16_to_f32(xr[j]));
+        float sc = amax / 127.0f;
+        x_scale[i] = sc;
+        for (int64_t j = 0; j < k; ++j)
+            xq[i * k + j] = (int8_t)(sc > 0.0f ? clampi((int)rintf(or_f16_to_f32(xr[j]) / sc), -127, 127) : 0);
+    }
+    return OR_OK;
+}
+
+/*
  * Step 5 on a sub-grid: acc int64 [nr, nc] for rows[] x cols[] (all when NULL).
  */
 int or_int8_gemm(const int8_t* xq, int64_t m, const int8_t* wq, int64_t n, int64_t k,
@@ -505,6 +554,35 @@ int or_w8a8_forward(const int8_t* xq, const float* x_scale, int64_t m, const int
         }
     }
     free(acc);
+    return OR_OK;
+}
+
+/*
+ * Step 9 on a sub-grid: steps 5-6 plus bias fp16 [n] and residual fp16
+ * [m, n] (either may be NULL), y float64 [nr, nc].
+ */
+int or_w8a8_forward_ex(const int8_t* xq, const float* x_scale, int64_t m, const int8_t* wq,
+                       const float* w_scale, int64_t n, int64_t k, const uint16_t* bias,
+                       const uint16_t* residual, const int64_t* rows, int64_t nr, const int64_t* cols,
+                       int64_t nc, double* y)
+{
+    if (!rows)
+        nr = m;
+    if (!cols)
+        nc = n;
+    int rc = or_w8a8_forward(xq, x_scale, m, wq, w_scale, n, k, rows, nr, cols, nc, y);
+    if (rc != OR_OK)
+        return rc;
+    for (int64_t a = 0; a < nr; ++a) {
+        int64_t i = rows ? rows[a] : a;
+        for (int64_t b = 0; b < nc; ++b) {
+            int64_t j = cols ? cols[b] : b;
+            if (bias)
+                y[a * nc + b] += (double)or_f16_to_f32(bias[j]);
+            if (residual)
+                y[a * nc + b] += (double)or_f16_to_f32(residual[i * n + j]);
+        }
+    }
     return OR_OK;
 }
 

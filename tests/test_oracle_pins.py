@@ -428,3 +428,89 @@ def test_int8_gemm_vs_python_ints_and_numpy():
     for a, i in enumerate([4, 1]):
         for b, j in enumerate([0, 6]):
             assert y[a, b] == float(acc[i, j]) * float(xs[i]) * float(ws[j])
+
+
+# --------------------------------------------------------------------------- steps beside the path
+def test_add_quant_rmsnorm_sum_is_correctly_rounded():
+    """h = fp16(x + residual) equals the exact sum rounded once to binary16,
+    by two routes that share nothing with the oracle's codec: NumPy's float16
+    addition, and the float64 sum (exact for two binary16 values) converted
+    by NumPy."""
+    rng = np.random.default_rng(21)
+    m, k = 6, 512
+    mag = rng.choice(np.array([1e-6, 1e-3, 1.0, 300.0]), (m, k))
+    x = (rng.standard_normal((m, k)) * mag).astype(np.float16)
+    r = (rng.standard_normal((m, k)) * rng.choice(np.array([1e-6, 1e-3, 1.0, 300.0]), (m, k))).astype(np.float16)
+    r[0, :16] = -x[0, :16]                                   # exact cancellation
+    r[1, :8] = np.float16(2.0 ** -24)                        # subnormal addend
+    gamma = rng.uniform(0.5, 1.5, k).astype(np.float16)
+    h, xq, sc = oracle.add_quant_rmsnorm(x, r, gamma)
+    assert np.array_equal(h, (x + r).view(np.uint16))
+    exact = x.astype(np.float64) + r.astype(np.float64)
+    assert np.array_equal(h, exact.astype(np.float16).view(np.uint16))
+    assert not h[0, :16].any()
+
+
+def test_add_quant_rmsnorm_reduces_to_qrmsnorm():
+    """A zero residual (either operand zero) reduces step 7 to the pinned
+    step 4 on the other operand; h is then that operand bit for bit."""
+    x, gamma, _ = workloads.smoothquant_inputs(m=16, k=1024, n=8, seed=3)
+    z = np.zeros_like(x)
+    for a, b in ((x, z), (z, x)):
+        h, xq, sc = oracle.add_quant_rmsnorm(a, b, gamma)
+        xq4, sc4 = oracle.quant_rmsnorm(x, gamma)
+        assert np.array_equal(h, x.view(np.uint16))
+        assert np.array_equal(xq, xq4) and np.array_equal(sc, sc4)
+
+
+def test_quant_per_token_closed_forms_and_bounds():
+    k = 304
+    x = np.zeros((4, k), np.float16)
+    x[0, 5] = -2.5                                           # single nonzero element
+    x[2] = np.float16(0.75)                                  # constant row
+    x[3, :] = np.linspace(-4, 4, k).astype(np.float16)
+    xq, sc = oracle.quant_per_token(x)
+    assert sc[0] == np.float32(2.5) / np.float32(127) and xq[0, 5] == -127 and np.count_nonzero(xq[0]) == 1
+    assert sc[1] == 0 and not xq[1].any()                    # all-zero token
+    assert (xq[2] == 127).all()
+    assert xq[3, 0] == -127 and xq[3, -1] == 127
+    # every code reconstructs its input within half a step (plus fp32 rounding of the quotient)
+    rng = np.random.default_rng(23)
+    xr = (rng.standard_normal((16, k)) * rng.uniform(0.01, 50, (16, 1))).astype(np.float16)
+    q, s = oracle.quant_per_token(xr)
+    err = np.abs(q.astype(np.float64) * s[:, None].astype(np.float64) - xr.astype(np.float64))
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 1e-5)).all()
+    assert (np.abs(q).max(axis=1) == 127).all()
+    # sign symmetry and power-of-two scaling leave the codes unchanged
+    qn, sn = oracle.quant_per_token(-xr)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    q8, s8 = oracle.quant_per_token((xr.astype(np.float32) * 8).astype(np.float16))
+    assert np.array_equal(q8, q) and np.array_equal(s8, s * np.float32(8))
+
+
+def test_w8a8_epilogue_bias_residual_closed_forms():
+    rng = np.random.default_rng(24)
+    m, n, k = 5, 7, 96
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    xs = rng.uniform(0.01, 1, m).astype(np.float32)
+    ws = rng.uniform(0.01, 1, n).astype(np.float32)
+    bias = rng.standard_normal(n).astype(np.float16)
+    res = rng.standard_normal((m, n)).astype(np.float16)
+    # a zero activation leaves exactly the bias, the residual, or their sum
+    x0 = np.zeros((m, k), np.int8)
+    assert np.array_equal(oracle.w8a8_forward_ex(x0, xs, wq, ws, bias=bias), np.tile(bias.astype(np.float64), (m, 1)))
+    assert np.array_equal(oracle.w8a8_forward_ex(x0, xs, wq, ws, residual=res), res.astype(np.float64))
+    # no bias and no residual: steps 5-6 as they stand
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    assert np.array_equal(oracle.w8a8_forward_ex(xq, xs, wq, ws), oracle.w8a8_forward(xq, xs, wq, ws))
+    # exact rationals with power-of-two scales: every term is exact, so is the float64 sum
+    xs2 = np.float32(2.0) ** rng.integers(-8, 0, m).astype(np.float32)
+    ws2 = np.float32(2.0) ** rng.integers(-8, 0, n).astype(np.float32)
+    y = oracle.w8a8_forward_ex(xq, xs2, wq, ws2, bias=bias, residual=res, rows=np.array([3, 0]),
+                               cols=np.array([6, 1, 2]))
+    for a, i in enumerate([3, 0]):
+        for b, j in enumerate([6, 1, 2]):
+            acc = sum(int(p) * int(q) for p, q in zip(xq[i], wq[j]))
+            want = (Fraction(acc) * Fraction(float(xs2[i])) * Fraction(float(ws2[j])) + Fraction(float(bias[j]))
+                    + Fraction(float(res[i, j])))
+            assert Fraction(y[a, b]) == want
