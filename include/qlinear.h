@@ -201,6 +201,56 @@ int ql_w8a8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps,
 int ql_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
                  uint16_t* y, int64_t m, int64_t n, int64_t k, void* stream);
 
+/*
+ * ql_w8a8_add_quant_rmsnorm (device).  QRMSNorm with the residual add fused in
+ * front (LMDeploy W8A8 guide, "inference kernels": the RMSNorm dynamic-quant
+ * kernel's residual fusion).  Per element h = fp16(x + residual), the exact
+ * sum rounded once; h is written to h_out (the updated residual stream), then
+ * xq / x_scale are QRMSNorm of h exactly as ql_w8a8_quant_rmsnorm defines it.
+ *   x, residual fp16 [m, k], gamma fp16 [k] (device); h_out fp16 [m, k], xq
+ *   int8 [m, k], x_scale float32 [m] (device, written).  h_out may be x or
+ *   residual (in-place update); it must not overlap them otherwise.
+ *   k <= 65536.  Inputs must be finite.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_VALUE, QL_ERR_ALIGN,
+ * QL_ERR_UNSUPPORTED, QL_ERR_HIP.
+ */
+int ql_w8a8_add_quant_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                              float eps, uint16_t* h_out, int8_t* xq, float* x_scale,
+                              int64_t m, int64_t k, void* stream);
+
+/*
+ * ql_w8a8_quant_per_token (device).  Per-token dynamic int8 quantisation of a
+ * plain activation, for a QLinear whose input does not come from QRMSNorm
+ * (LMDeploy W8A8 guide, "inference kernels": per_token_quant_int8, scale =
+ * absmax / Q_MAX).  Per token i, in fp32:
+ *   x_scale[i] = max_j |x[i,j]| / 127
+ *   xq[i,j]    = clamp(rint(x[i,j] / x_scale[i]), -127, 127)  (0 for x_scale 0)
+ * both correctly rounded divisions.
+ *   x fp16 [m, k] (device); xq int8 [m, k], x_scale float32 [m] (device,
+ *   written).  k <= 65536.  Inputs must be finite.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED,
+ * QL_ERR_HIP.
+ */
+int ql_w8a8_quant_per_token(const uint16_t* x, int8_t* xq, float* x_scale,
+                            int64_t m, int64_t k, void* stream);
+
+/*
+ * ql_w8a8_gemm_ex (device).  ql_w8a8_gemm with the optional bias and residual
+ * of the epilogue (LMDeploy W8A8 guide, "inference kernels": the int8 GEMM's
+ * residual and bias fusion after the rms_scale * linear_scale dequantisation):
+ *   y = fp16(fp32(fp32(fp32(fp32(acc * x_scale[i]) * w_scale[j]) + bias[j])
+ *            + residual[i,j]))
+ * each fp32 operation rounded on its own, a term skipped (not added as 0)
+ * when its pointer is NULL.
+ *   bias fp16 [n] or NULL, residual fp16 [m, n] or NULL (device); y fp16
+ *   [m, n] (device, written) may be residual itself (in-place add); other
+ *   arguments as ql_w8a8_gemm.
+ * Errors: as ql_w8a8_gemm.
+ */
+int ql_w8a8_gemm_ex(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                    const uint16_t* bias, const uint16_t* residual, uint16_t* y,
+                    int64_t m, int64_t n, int64_t k, void* stream);
+
 /* ql_w8a8_gemm_i32 (device).  The same int8 MFMA main loop writing the raw
  * int32 accumulator acc [m, n] instead of the fp16 epilogue. */
 int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,

@@ -134,3 +134,26 @@ def test_python_binding_raises():
     with pytest.raises(ql.QLError) as e:
         ql.awq_pack(np.zeros((4, 128), np.float32), 48)
     assert e.value.code == CODES["QL_ERR_GROUP"]
+
+
+def test_w8a8_fused_validation():
+    E = CODES
+    a = LIB.ql_w8a8_add_quant_rmsnorm
+    assert a(FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, 4, 100, DEF) == E["QL_ERR_SHAPE"]
+    assert a(FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, 4, 65544, DEF) == E["QL_ERR_UNSUPPORTED"]
+    assert a(FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_VALUE"]
+    assert a(FAKE, None, FAKE, 1e-6, FAKE, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+    assert a(FAKE, FAKE, FAKE, 1e-6, None, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+    assert a(FAKE, FAKE, FAKE, 1e-6, MIS, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert a(None, None, None, 1e-6, None, None, None, 0, 128, DEF) == E["QL_OK"]
+    p = LIB.ql_w8a8_quant_per_token
+    assert p(FAKE, FAKE, FAKE, 4, 100, DEF) == E["QL_ERR_SHAPE"]
+    assert p(FAKE, None, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+    assert p(MIS, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert p(None, None, None, 0, 128, DEF) == E["QL_OK"]
+    g = LIB.ql_w8a8_gemm_ex
+    assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 64, 100, DEF) == E["QL_ERR_SHAPE"]
+    assert g(FAKE, FAKE, FAKE, FAKE, MIS, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert g(FAKE, FAKE, FAKE, FAKE, None, MIS, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert g(FAKE, None, FAKE, FAKE, None, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
+    assert g(None, None, None, None, None, None, None, 0, 64, 128, DEF) == E["QL_OK"]

@@ -40,6 +40,9 @@ EXPORTS = {
     "ql_w8a8_quant_weight": (_i, [_p, _i64, _i64, _p, _p]),
     "ql_w8a8_quant_rmsnorm": (_i, [_p, _p, C.c_float, _p, _p, _i64, _i64, _p]),
     "ql_w8a8_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "ql_w8a8_add_quant_rmsnorm": (_i, [_p, _p, _p, C.c_float, _p, _p, _p, _i64, _i64, _p]),
+    "ql_w8a8_quant_per_token": (_i, [_p, _p, _p, _i64, _i64, _p]),
+    "ql_w8a8_gemm_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "ql_w8a8_gemm_i32": (_i, [_p, _p, _p, _i64, _i64, _i64, _p]),
     "ql_status_string": (C.c_char_p, [_i]),
     "ql_last_error": (C.c_char_p, []),
@@ -232,6 +235,73 @@ def w8a8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
     _check(_lib.ql_w8a8_quant_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), xq.data_ptr(),
                                       x_scale.data_ptr(), m, k, _stream(x)))
     return xq, x_scale
+
+
+def w8a8_add_quant_rmsnorm(x, residual, gamma, eps: float = 1e-6, h_out=None, xq=None, x_scale=None):
+    """Residual-fused QRMSNorm: h = fp16(x + residual) is written to h_out
+    (pass h_out=residual, or x, to update in place), then QRMSNorm of h.
+    Returns (h, xq int8 [m, k], x_scale float32 [m])."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    residual = _dev(residual, torch.float16, "residual")
+    gamma = _dev(gamma, torch.float16, "gamma")
+    if residual.shape != x.shape:
+        raise ValueError("residual must have x's shape")
+    m, k = x.shape
+    if h_out is None:
+        h_out = torch.empty_like(x)
+    h_out = _dev(h_out, torch.float16, "h_out")
+    if h_out.shape != x.shape:
+        raise ValueError("h_out must have x's shape")
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_w8a8_add_quant_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
+                                          h_out.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
+    return h_out, xq, x_scale
+
+
+def w8a8_quant_per_token(x, xq=None, x_scale=None):
+    """Per-token int8 quantisation of a plain activation: (xq int8 [m, k],
+    x_scale float32 [m]) with x_scale = max|x| / 127."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_w8a8_quant_per_token(x.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
+    return xq, x_scale
+
+
+def w8a8_gemm_ex(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
+    """y fp16 [m, n] = fp16((xq @ wq^T) * x_scale * w_scale [+ bias] [+ residual]),
+    bias fp16 [n], residual fp16 [m, n]; out may be residual (in place)."""
+    torch = _torch()
+    xq = _dev(xq, torch.int8, "xq")
+    wq = _dev(wq, torch.int8, "wq")
+    x_scale = _dev(x_scale, torch.float32, "x_scale")
+    w_scale = _dev(w_scale, torch.float32, "w_scale")
+    m, k = xq.shape
+    n = wq.shape[0]
+    if bias is not None:
+        bias = _dev(bias, torch.float16, "bias")
+        if bias.shape != (n,):
+            raise ValueError("bias must be [n]")
+    if residual is not None:
+        residual = _dev(residual, torch.float16, "residual")
+        if residual.shape != (m, n):
+            raise ValueError("residual must be [m, n]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
+    out = _dev(out, torch.float16, "out")
+    _check(_lib.ql_w8a8_gemm_ex(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
+                                bias.data_ptr() if bias is not None else None,
+                                residual.data_ptr() if residual is not None else None, out.data_ptr(), m, n, k,
+                                _stream(xq)))
+    return out
 
 
 def w8a8_gemm(xq, x_scale, wq, w_scale, out=None):

@@ -212,10 +212,37 @@ constexpr int kNormThreads = 256;
 // absmax and quantisation passes read registers.  CPT == 0: chunks are
 // re-read from memory in each pass (any k).  Chunks past k are zero: they add
 // nothing to the sum of squares or the absmax and are not stored.
-template <int CPT>
-__global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint16_t* __restrict__ x,
+// Eight fp16 pairs -> fp16(a + b) per element.  The fp32 sum of two binary16
+// values rounded to binary16 is their correctly rounded sum (24 >= 2 * 11 + 2
+// significand bits), so this is exact fp16 addition.
+__device__ __forceinline__ uint4 add_h8(uint4 a, uint4 b)
+{
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = __fadd_rn(h2f(aw[e] & 0xFFFFu), h2f(bw[e] & 0xFFFFu));
+        const float hi = __fadd_rn(h2f(aw[e] >> 16), h2f(bw[e] >> 16));
+        o[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Per-token quantisers, one workgroup per token.  MODE:
+//   kNormQuant    -- QRMSNorm: y = RMSNorm(x) * gamma, then per-token int8
+//   kAddNormQuant -- h = fp16(x + residual) written to h_out (the residual
+//                    stream; h_out may be residual itself), then QRMSNorm of h
+//   kTokenQuant   -- y = x (no norm, no gamma), then per-token int8
+// x, residual and h_out are not restrict: h_out may be x or residual, and an
+// in-place update reads each chunk before the same thread overwrites it.
+constexpr int kNormQuant = 0, kAddNormQuant = 1, kTokenQuant = 2;
+
+template <int CPT, int MODE>
+__global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint16_t* x,
+                                                                     const uint16_t* residual,
                                                                      const uint16_t* __restrict__ gamma, float eps,
-                                                                     int8_t* __restrict__ xq,
+                                                                     uint16_t* h_out, int8_t* __restrict__ xq,
                                                                      float* __restrict__ x_scale, int K)
 {
     __shared__ U128 s_sum[kNormThreads / 64];
@@ -227,49 +254,55 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     const int nch = K >> 3;
     constexpr int R = CPT > 0 ? CPT : 1;
     uint4 xv[R], gv[R];
+    if constexpr (MODE == kAddNormQuant && CPT == 0) {
+        // chunks are re-read in every pass: form h once, then read it back
+        // (each thread reads only the chunks it wrote)
+        const uint4* rr = reinterpret_cast<const uint4*>(residual + (int64_t)row * K);
+        uint4* hr = reinterpret_cast<uint4*>(h_out + (int64_t)row * K);
+        for (int c = (int)threadIdx.x; c < nch; c += kNormThreads)
+            hr[c] = add_h8(xr[c], rr[c]);
+        xr = hr;
+    }
     auto chunk = [&](int i, int c, uint4& v, uint4& g) {   // chunk c (loop slot i)
         if constexpr (CPT > 0) {
             v = xv[i];
             g = gv[i];
         } else {
             v = xr[c];
-            g = gr[c];
+            g = MODE == kTokenQuant ? make_uint4(0u, 0u, 0u, 0u) : gr[c];
         }
     };
     if constexpr (CPT > 0) {
+        uint4 rv[MODE == kAddNormQuant ? CPT : 1];
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = (int)threadIdx.x + i * kNormThreads;
             const int cc = c < nch ? c : nch - 1;
             xv[i] = xr[cc];
-            gv[i] = gr[cc];
+            gv[i] = MODE == kTokenQuant ? make_uint4(0u, 0u, 0u, 0u) : gr[cc];
+            if constexpr (MODE == kAddNormQuant)
+                rv[i] = reinterpret_cast<const uint4*>(residual + (int64_t)row * K)[cc];
         }
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            if ((int)threadIdx.x + i * kNormThreads >= nch)
+        for (int i = 0; i < CPT; ++i) {
+            const int c = (int)threadIdx.x + i * kNormThreads;
+            if constexpr (MODE == kAddNormQuant) {
+                xv[i] = add_h8(xv[i], rv[i]);
+                if (c < nch)
+                    reinterpret_cast<uint4*>(h_out + (int64_t)row * K)[c] = xv[i];
+            }
+            if (c >= nch)
                 xv[i] = gv[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
     const int npass = CPT > 0 ? CPT : (nch - (int)threadIdx.x + kNormThreads - 1) / kNormThreads;
 
     // mean of squares: fp64 sum of the exact squares, or, when its fp32
     // rounding is not certain, the exact 128-bit integer sum (the decision is
     // taken on the workgroup total, so the whole workgroup branches together)
-    double accd = 0.0;
-#pragma unroll R
-    for (int i = 0; i < npass; ++i) {
-        uint4 v, g;
-        chunk(i, (int)threadIdx.x + i * kNormThreads, v, g);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const double a = (double)h2f(w[e] & 0xFFFFu), b = (double)h2f(w[e] >> 16);
-            accd = __builtin_fma(a, a, accd);
-            accd = __builtin_fma(b, b, accd);
-        }
-    }
-    float ms;
-    if (!mean_fast(block_sum_f64<kNormThreads>(accd, s_sumd), K, &ms)) {
-        U128 acc{0, 0};
+    float r = 1.0f;
+    if constexpr (MODE != kTokenQuant) {
+        double accd = 0.0;
 #pragma unroll R
         for (int i = 0; i < npass; ++i) {
             uint4 v, g;
@@ -277,23 +310,44 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                add_square(acc, w[e] & 0xFFFFu);
-                add_square(acc, w[e] >> 16);
+                const double a = (double)h2f(w[e] & 0xFFFFu), b = (double)h2f(w[e] >> 16);
+                accd = __builtin_fma(a, a, accd);
+                accd = __builtin_fma(b, b, accd);
             }
         }
-        ms = mean_from_exact(block_sum128<kNormThreads>(acc, s_sum), (uint32_t)K);
+        float ms;
+        if (!mean_fast(block_sum_f64<kNormThreads>(accd, s_sumd), K, &ms)) {
+            U128 acc{0, 0};
+#pragma unroll R
+            for (int i = 0; i < npass; ++i) {
+                uint4 v, g;
+                chunk(i, (int)threadIdx.x + i * kNormThreads, v, g);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    add_square(acc, w[e] & 0xFFFFu);
+                    add_square(acc, w[e] >> 16);
+                }
+            }
+            ms = mean_from_exact(block_sum128<kNormThreads>(acc, s_sum), (uint32_t)K);
+        }
+        r = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
     }
-    const float r = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
 
-    // y = fp32(fp32(x * r) * gamma); kept per element when the chunks are in
-    // registers, recomputed per pass otherwise
+    // y = fp32(fp32(x * r) * gamma) (y = x without the norm); kept per
+    // element when the chunks are in registers, recomputed per pass otherwise
     float yk[R][8];
     auto y_of = [&](const uint4& v, const uint4& g, float (&yo)[8]) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            yo[2 * e] = __fmul_rn(__fmul_rn(h2f(w[e] & 0xFFFFu), r), h2f(gw[e] & 0xFFFFu));
-            yo[2 * e + 1] = __fmul_rn(__fmul_rn(h2f(w[e] >> 16), r), h2f(gw[e] >> 16));
+            if constexpr (MODE == kTokenQuant) {
+                yo[2 * e] = h2f(w[e] & 0xFFFFu);
+                yo[2 * e + 1] = h2f(w[e] >> 16);
+            } else {
+                yo[2 * e] = __fmul_rn(__fmul_rn(h2f(w[e] & 0xFFFFu), r), h2f(gw[e] & 0xFFFFu));
+                yo[2 * e + 1] = __fmul_rn(__fmul_rn(h2f(w[e] >> 16), r), h2f(gw[e] >> 16));
+            }
         }
     };
     float amax = 0.0f;
@@ -397,6 +451,28 @@ __device__ __forceinline__ int xcd_tile(int wg, int ntiles)
     return t;
 }
 
+// One output of the fp16 epilogue: y = fp16(fp32(fp32(acc * x_scale) *
+// w_scale) [+ bias] [+ residual]), every operation rounded to fp32 on its own
+// (the build does not contract), the bias and residual terms only when given,
+// then one rounding to fp16 (the empty asm keeps the conversion from being
+// fused with the last operation).
+struct EpiTerms {
+    const uint16_t* bias;   // [N] fp16 or null
+    const uint16_t* res;    // [M, N] fp16 or null; may be the output itself
+};
+__device__ __forceinline__ uint32_t epi_h(int32_t acc, float xs, float ws, const EpiTerms& et, float b, float r)
+{
+    float f = __fmul_rn(__fmul_rn((float)acc, xs), ws);
+    if (et.bias)
+        f = __fadd_rn(f, b);
+    if (et.res)
+        f = __fadd_rn(f, r);
+    asm volatile("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float h_lo(uint32_t w) { return h2f(w & 0xFFFFu); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return h2f(w >> 16); }
+
 // Epilogue of both int8 GEMM kernels.  The MFMA takes the weight fragment as
 // its A operand and the activation fragment as B, so fragment (i, j) holds the
 // transposed product: lane (q, r16) has y[m][n .. n+3] with m = mrow + 16 i,
@@ -406,10 +482,10 @@ __device__ __forceinline__ int xcd_tile(int wg, int ntiles)
 // together.  `vec`: the whole tile is in bounds and rows are 4-aligned.
 template <int FI, int FJ, bool kRaw>
 __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const float* __restrict__ xs,
-                                           const float* __restrict__ ws, void* __restrict__ out, int M, int N,
-                                           int mrow, int ncol, bool vec)
+                                           const float* __restrict__ ws, const EpiTerms& et, void* out, int M,
+                                           int N, int mrow, int ncol, bool vec)
 {
-    float xsv[FI], wsv[FJ][4];
+    float xsv[FI], wsv[FJ][4], bsv[FJ][4];
     if (!kRaw) {
 #pragma unroll
         for (int i = 0; i < FI; ++i)
@@ -417,16 +493,13 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 4; ++r) {
                 wsv[j][r] = ws[min(ncol + 16 * j + r, N - 1)];
+                bsv[j][r] = et.bias ? h2f(et.bias[min(ncol + 16 * j + r, N - 1)]) : 0.0f;
+            }
     }
-    // y = fp16(fp32(fp32(acc * x_scale) * w_scale)): each product rounded to
-    // fp32, then one rounding to fp16 (the empty asm keeps the conversion
-    // from being fused with the product into a single rounding)
-    auto to_h = [&](int i, int j, int r) -> uint32_t {
-        float v = __fmul_rn(__fmul_rn((float)acc[i][j][r], xsv[i]), wsv[j][r]);
-        asm volatile("" : "+v"(v));
-        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    auto to_h = [&](int i, int j, int r, float rv) -> uint32_t {
+        return epi_h(acc[i][j][r], xsv[i], wsv[j][r], et, bsv[j][r], rv);
     };
     if (vec) {
 #pragma unroll
@@ -437,9 +510,10 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
                 if (kRaw) {
                     *reinterpret_cast<i4_t*>(static_cast<int32_t*>(out) + o) = acc[i][j];
                 } else {
+                    const uint2 rr = et.res ? *reinterpret_cast<const uint2*>(et.res + o) : make_uint2(0u, 0u);
                     uint2 h;
-                    h.x = to_h(i, j, 0) | (to_h(i, j, 1) << 16);
-                    h.y = to_h(i, j, 2) | (to_h(i, j, 3) << 16);
+                    h.x = to_h(i, j, 0, h_lo(rr.x)) | (to_h(i, j, 1, h_hi(rr.x)) << 16);
+                    h.y = to_h(i, j, 2, h_lo(rr.y)) | (to_h(i, j, 3, h_hi(rr.y)) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = h;
                 }
             }
@@ -457,10 +531,11 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
                 const int n = ncol + 16 * j + r;
                 if (n >= N)
                     continue;
+                const int64_t o = (int64_t)m * N + n;
                 if (kRaw)
-                    static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][r];
+                    static_cast<int32_t*>(out)[o] = acc[i][j][r];
                 else
-                    static_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)to_h(i, j, r);
+                    static_cast<uint16_t*>(out)[o] = (uint16_t)to_h(i, j, r, et.res ? h2f(et.res[o]) : 0.0f);
             }
     }
 }
@@ -471,10 +546,10 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
 // four consecutive columns (8-byte fp16 stores).  Same rounding as store_tile.
 template <int FI, int FJ, bool kRaw>
 __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const float* __restrict__ xs,
-                                             const float* __restrict__ ws, void* __restrict__ out, int M, int N,
-                                             int mrow, int ncol, bool vec)
+                                             const float* __restrict__ ws, const EpiTerms& et, void* out, int M,
+                                             int N, int mrow, int ncol, bool vec)
 {
-    float xsv[FI], wsv[FJ][16];
+    float xsv[FI], wsv[FJ][16], bsv[FJ][16];
     if (!kRaw) {
 #pragma unroll
         for (int i = 0; i < FI; ++i)
@@ -482,13 +557,14 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                wsv[j][v] = ws[min(ncol + 32 * j + 8 * (v >> 2) + (v & 3), N - 1)];
+            for (int v = 0; v < 16; ++v) {
+                const int n = min(ncol + 32 * j + 8 * (v >> 2) + (v & 3), N - 1);
+                wsv[j][v] = ws[n];
+                bsv[j][v] = et.bias ? h2f(et.bias[n]) : 0.0f;
+            }
     }
-    auto to_h = [&](int i, int j, int v) -> uint32_t {
-        float f = __fmul_rn(__fmul_rn((float)acc[i][j][v], xsv[i]), wsv[j][v]);
-        asm volatile("" : "+v"(f));
-        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    auto to_h = [&](int i, int j, int v, float rv) -> uint32_t {
+        return epi_h(acc[i][j][v], xsv[i], wsv[j][v], et, bsv[j][v], rv);
     };
     if (vec) {
 #pragma unroll
@@ -503,9 +579,10 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
                                              acc[i][j][4 * g + 3]};
                         *reinterpret_cast<i4_t*>(static_cast<int32_t*>(out) + o) = v4;
                     } else {
+                        const uint2 rr = et.res ? *reinterpret_cast<const uint2*>(et.res + o) : make_uint2(0u, 0u);
                         uint2 h;
-                        h.x = to_h(i, j, 4 * g) | (to_h(i, j, 4 * g + 1) << 16);
-                        h.y = to_h(i, j, 4 * g + 2) | (to_h(i, j, 4 * g + 3) << 16);
+                        h.x = to_h(i, j, 4 * g, h_lo(rr.x)) | (to_h(i, j, 4 * g + 1, h_hi(rr.x)) << 16);
+                        h.y = to_h(i, j, 4 * g + 2, h_lo(rr.y)) | (to_h(i, j, 4 * g + 3, h_hi(rr.y)) << 16);
                         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = h;
                     }
                 }
@@ -523,10 +600,11 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
                 const int n = ncol + 32 * j + 8 * (v >> 2) + (v & 3);
                 if (n >= N)
                     continue;
+                const int64_t o = (int64_t)m * N + n;
                 if (kRaw)
-                    static_cast<int32_t*>(out)[(int64_t)m * N + n] = acc[i][j][v];
+                    static_cast<int32_t*>(out)[o] = acc[i][j][v];
                 else
-                    static_cast<uint16_t*>(out)[(int64_t)m * N + n] = (uint16_t)to_h(i, j, v);
+                    static_cast<uint16_t*>(out)[o] = (uint16_t)to_h(i, j, v, et.res ? h2f(et.res[o]) : 0.0f);
             }
     }
 }
@@ -535,7 +613,7 @@ template <int BM, int BN, bool kRaw>
 __global__ __launch_bounds__(256) void w8a8_gemm_kernel(const int8_t* __restrict__ xq,
                                                         const float* __restrict__ xs,
                                                         const int8_t* __restrict__ wq,
-                                                        const float* __restrict__ ws, void* __restrict__ out,
+                                                        const float* __restrict__ ws, EpiTerms et, void* out,
                                                         int M, int N, int K)
 {
     constexpr int TM = BM / 2, TN = BN / 2;           // wave tile
@@ -632,7 +710,7 @@ __global__ __launch_bounds__(256) void w8a8_gemm_kernel(const int8_t* __restrict
     }
 
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
-    store_tile<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
+    store_tile<FI, FJ, kRaw>(acc, xs, ws, et, out, M, N, m0 + wm * TM + r16, n0 + wn * TN + 4 * q, vec);
 }
 
 constexpr int kQBM = 256, kQBN = 128;
@@ -685,8 +763,8 @@ template <class C, bool kRaw>
 __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
-                                                             const float* __restrict__ ws, void* __restrict__ out,
-                                                             int M, int N, int K)
+                                                             const float* __restrict__ ws, EpiTerms et,
+                                                             void* out, int M, int N, int K)
 {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, KS = C::KS, D = C::D;
     constexpr int TM = BM / 2, TN = BN / 2;
@@ -813,20 +891,23 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
     if constexpr (!kRaw && kStaged) {
         if (full && (N & 7) == 0) {
             uint16_t* ot = reinterpret_cast<uint16_t*>(pl) + wave * HALF * PITCH;
-            float xsv[FI], wsv[FJ][16];
+            float xsv[FI], wsv[FJ][16], bsv[FJ][16];
 #pragma unroll
             for (int i = 0; i < FI; ++i)
                 xsv[i] = xs[m0 + wm * TM + 32 * i + r32];
 #pragma unroll
             for (int jj = 0; jj < FJ; ++jj)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    wsv[jj][v] = ws[n0 + wn * TN + 32 * jj + 8 * (v >> 2) + 4 * h32 + (v & 3)];
-            auto to_h = [&](int i, int jj, int v) -> uint32_t {
-                float f = __fmul_rn(__fmul_rn((float)acc[i][jj][v], xsv[i]), wsv[jj][v]);
-                asm volatile("" : "+v"(f));
-                return __builtin_bit_cast(uint16_t, (_Float16)f);
+                for (int v = 0; v < 16; ++v) {
+                    const int n = n0 + wn * TN + 32 * jj + 8 * (v >> 2) + 4 * h32 + (v & 3);
+                    wsv[jj][v] = ws[n];
+                    bsv[jj][v] = et.bias ? h2f(et.bias[n]) : 0.0f;
+                }
+            auto to_h = [&](int i, int jj, int v, float rv) -> uint32_t {
+                return epi_h(acc[i][jj][v], xsv[i], wsv[jj][v], et, bsv[jj][v], rv);
             };
+            // a residual that is the output itself: each half reads its rows
+            // before storing them, and the halves and waves cover disjoint rows
             constexpr int LPR = TN / 8;             // lanes per row
             constexpr int RPI = 64 / LPR;           // rows per store instruction
 #pragma unroll
@@ -837,9 +918,13 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
                     for (int jj = 0; jj < FJ; ++jj)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
+                            const int64_t o = (int64_t)(m0 + wm * TM + 32 * i + r32) * N + n0 + wn * TN + 32 * jj +
+                                              8 * g + 4 * h32;
+                            const uint2 rr =
+                                et.res ? *reinterpret_cast<const uint2*>(et.res + o) : make_uint2(0u, 0u);
                             uint2 h;
-                            h.x = to_h(i, jj, 4 * g) | (to_h(i, jj, 4 * g + 1) << 16);
-                            h.y = to_h(i, jj, 4 * g + 2) | (to_h(i, jj, 4 * g + 3) << 16);
+                            h.x = to_h(i, jj, 4 * g, h_lo(rr.x)) | (to_h(i, jj, 4 * g + 1, h_hi(rr.x)) << 16);
+                            h.y = to_h(i, jj, 4 * g + 2, h_lo(rr.y)) | (to_h(i, jj, 4 * g + 3, h_hi(rr.y)) << 16);
                             *reinterpret_cast<uint2*>(ot + (32 * (i - hf * FI / 2) + r32) * PITCH + 32 * jj + 8 * g +
                                                       4 * h32) = h;
                         }
@@ -854,15 +939,15 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
             return;
         }
     }
-    store_tile32<FI, FJ, kRaw>(acc, xs, ws, out, M, N, m0 + wm * TM + r32, n0 + wn * TN + 4 * h32,
+    store_tile32<FI, FJ, kRaw>(acc, xs, ws, et, out, M, N, m0 + wm * TM + r32, n0 + wn * TN + 4 * h32,
                                full && (N & 3) == 0);
 }
 
 using Pipe = PipeCfg<kQBM, kQBN, 64, 3, true>;
 
 template <bool kRaw>
-void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, void* out, int64_t m,
-                      int64_t n, int64_t k, hipStream_t st)
+void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, EpiTerms et,
+                      void* out, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
     // grid: whole rounds over the XCDs
     auto grid_for = [&](int bm, int bn) {
@@ -871,10 +956,10 @@ void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const
     };
     if (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds))
         hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(256),
-                           (size_t)Pipe::kLds, st, xq, xs, wq, ws, out, (int)m, (int)n, (int)k);
+                           (size_t)Pipe::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n, (int)k);
     else
         hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3(grid_for(kQBM, kQBN)), dim3(256), 0, st, xq, xs,
-                           wq, ws, out, (int)m, (int)n, (int)k);
+                           wq, ws, et, out, (int)m, (int)n, (int)k);
 }
 
 
@@ -904,55 +989,113 @@ int check_gemm(const void* xq, const void* wq, const void* out, int64_t m, int64
 
 }  // namespace
 
-extern "C" int ql_w8a8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int8_t* xq,
-                                     float* x_scale, int64_t m, int64_t k, void* stream)
+namespace {
+
+// Validation and launch shared by the per-token quantisers (one workgroup per
+// token; chunks per thread picked from k).
+template <int MODE>
+int launch_token_quant(const char* who, const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                       float eps, uint16_t* h_out, int8_t* xq, float* x_scale, int64_t m, int64_t k, void* stream)
 {
-    ql::clear_error();
-    const char* who = "ql_w8a8_quant_rmsnorm";
     if (m < 0 || k <= 0 || k % 8)
         QL_FAIL(QL_ERR_SHAPE, "%s: m=%lld k=%lld (k must be a positive multiple of 8)", who, (long long)m,
                 (long long)k);
     if (k > 65536 || m > (1LL << 31) - 1)
         QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld above 65536", who, (long long)k);
-    if (!(eps >= 0.0f) || !(eps < 1e30f))
+    if (MODE != kTokenQuant && (!(eps >= 0.0f) || !(eps < 1e30f)))
         QL_FAIL(QL_ERR_VALUE, "%s: eps must be finite and >= 0", who);
     if (m == 0)
         return QL_OK;
-    if (!x || !gamma || !xq || !x_scale)
+    if (!x || !xq || !x_scale || (MODE != kTokenQuant && !gamma) || (MODE == kAddNormQuant && (!residual || !h_out)))
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
-    if (!ql::aligned16(x) || !ql::aligned16(gamma) || !ql::aligned16(xq) || !ql::aligned16(x_scale))
+    if (!ql::aligned16(x) || !ql::aligned16(xq) || !ql::aligned16(x_scale) ||
+        (MODE != kTokenQuant && !ql::aligned16(gamma)) ||
+        (MODE == kAddNormQuant && (!ql::aligned16(residual) || !ql::aligned16(h_out))))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
     const int64_t cpt = (k / 8 + kNormThreads - 1) / kNormThreads;   // 16-byte chunks per thread
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)m), block(kNormThreads);
+    const int ki = (int)k;
     if (cpt <= 1)
-        hipLaunchKernelGGL(quant_rmsnorm_kernel<1>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+        hipLaunchKernelGGL((quant_rmsnorm_kernel<1, MODE>), grid, block, 0, st, x, residual, gamma, eps, h_out, xq,
+                           x_scale, ki);
     else if (cpt <= 2)
-        hipLaunchKernelGGL(quant_rmsnorm_kernel<2>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+        hipLaunchKernelGGL((quant_rmsnorm_kernel<2, MODE>), grid, block, 0, st, x, residual, gamma, eps, h_out, xq,
+                           x_scale, ki);
     else if (cpt <= 4)
-        hipLaunchKernelGGL(quant_rmsnorm_kernel<4>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+        hipLaunchKernelGGL((quant_rmsnorm_kernel<4, MODE>), grid, block, 0, st, x, residual, gamma, eps, h_out, xq,
+                           x_scale, ki);
     else if (cpt <= 8)
-        hipLaunchKernelGGL(quant_rmsnorm_kernel<8>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+        hipLaunchKernelGGL((quant_rmsnorm_kernel<8, MODE>), grid, block, 0, st, x, residual, gamma, eps, h_out, xq,
+                           x_scale, ki);
     else
-        hipLaunchKernelGGL(quant_rmsnorm_kernel<0>, grid, block, 0, st, x, gamma, eps, xq, x_scale, (int)k);
+        hipLaunchKernelGGL((quant_rmsnorm_kernel<0, MODE>), grid, block, 0, st, x, residual, gamma, eps, h_out, xq,
+                           x_scale, ki);
     return launch_status(who);
 }
 
-extern "C" int ql_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
-                            uint16_t* y, int64_t m, int64_t n, int64_t k, void* stream)
+}  // namespace
+
+extern "C" int ql_w8a8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int8_t* xq,
+                                     float* x_scale, int64_t m, int64_t k, void* stream)
 {
     ql::clear_error();
-    const char* who = "ql_w8a8_gemm";
+    return launch_token_quant<kNormQuant>("ql_w8a8_quant_rmsnorm", x, nullptr, gamma, eps, nullptr, xq, x_scale, m, k,
+                                          stream);
+}
+
+extern "C" int ql_w8a8_add_quant_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* gamma,
+                                         float eps, uint16_t* h_out, int8_t* xq, float* x_scale, int64_t m,
+                                         int64_t k, void* stream)
+{
+    ql::clear_error();
+    return launch_token_quant<kAddNormQuant>("ql_w8a8_add_quant_rmsnorm", x, residual, gamma, eps, h_out, xq,
+                                             x_scale, m, k, stream);
+}
+
+extern "C" int ql_w8a8_quant_per_token(const uint16_t* x, int8_t* xq, float* x_scale, int64_t m, int64_t k,
+                                       void* stream)
+{
+    ql::clear_error();
+    return launch_token_quant<kTokenQuant>("ql_w8a8_quant_per_token", x, nullptr, nullptr, 0.0f, nullptr, xq,
+                                           x_scale, m, k, stream);
+}
+
+namespace {
+
+int w8a8_gemm_fp16(const char* who, const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                   const uint16_t* bias, const uint16_t* residual, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                   void* stream)
+{
     if (int rc = check_gemm(xq, wq, y, m, n, k, who))
         return rc;
     if (m == 0 || n == 0)
         return QL_OK;
     if (!x_scale || !w_scale)
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
-    if (!ql::aligned16(x_scale) || !ql::aligned16(w_scale))
+    if (!ql::aligned16(x_scale) || !ql::aligned16(w_scale) || (bias && !ql::aligned16(bias)) ||
+        (residual && !ql::aligned16(residual)))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
-    launch_w8a8_gemm<false>(xq, x_scale, wq, w_scale, (void*)y, m, n, k, static_cast<hipStream_t>(stream));
+    launch_w8a8_gemm<false>(xq, x_scale, wq, w_scale, EpiTerms{bias, residual}, (void*)y, m, n, k,
+                            static_cast<hipStream_t>(stream));
     return launch_status(who);
+}
+
+}  // namespace
+
+extern "C" int ql_w8a8_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                            uint16_t* y, int64_t m, int64_t n, int64_t k, void* stream)
+{
+    ql::clear_error();
+    return w8a8_gemm_fp16("ql_w8a8_gemm", xq, x_scale, wq, w_scale, nullptr, nullptr, y, m, n, k, stream);
+}
+
+extern "C" int ql_w8a8_gemm_ex(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                               const uint16_t* bias, const uint16_t* residual, uint16_t* y, int64_t m, int64_t n,
+                               int64_t k, void* stream)
+{
+    ql::clear_error();
+    return w8a8_gemm_fp16("ql_w8a8_gemm_ex", xq, x_scale, wq, w_scale, bias, residual, y, m, n, k, stream);
 }
 
 extern "C" int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t m, int64_t n, int64_t k,
@@ -964,6 +1107,7 @@ extern "C" int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc
         return rc;
     if (m == 0 || n == 0)
         return QL_OK;
-    launch_w8a8_gemm<true>(xq, nullptr, wq, nullptr, (void*)acc, m, n, k, static_cast<hipStream_t>(stream));
+    launch_w8a8_gemm<true>(xq, nullptr, wq, nullptr, EpiTerms{nullptr, nullptr}, (void*)acc, m, n, k,
+                           static_cast<hipStream_t>(stream));
     return launch_status(who);
 }
