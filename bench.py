@@ -21,7 +21,9 @@ rocprofv3 counter summary when it was taken on the current kernel source.
 `detail` gives every launch of the step its graph-averaged duration and the
 p10 / median / p90 of 100 single launches (event pairs, cold weights).
 `extra` reports the W4A16 prefill GEMM (M=512 fused QKV) and the W8A8 layer
-(QRMSNorm + int8 GEMM, M=2048) against their rooflines.  `reference` is a
+(QRMSNorm + int8 GEMM, M=2048) against their rooflines, and the steps beside
+it (residual-fused QRMSNorm, per-token quantisation, the GEMM with bias and
+residual).  `reference` is a
 plain device copy's rate, the achievable HBM bandwidth on the device.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
@@ -329,6 +331,36 @@ def measure_extra(torch, ql, workloads, dev, log):
     out.append({"name": "w8a8_gemm", "m": m, "n": nn, "k": kk, "us": round(us_g, 2),
                 "TOP/s": round(ops / (us_g * 1e-6) / 1e12, 1),
                 "frac_mfma_int8": round(ops / (us_g * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)})
+
+    # the steps beside the path: residual-fused QRMSNorm, per-token
+    # quantisation of a plain activation, the GEMM with bias and residual
+    rng = np.random.default_rng(5)
+    rd = torch.from_numpy(workloads.activations(rng, m, kk)).to(dev)
+    hd = torch.empty_like(xd)
+    log("[bench] extra: fused W8A8 steps M=2048")
+    ql.w8a8_add_quant_rmsnorm(xd, rd, gd, 1e-6, h_out=hd, xq=xq, x_scale=xsc)
+    ga = capture(torch, [lambda: ql.w8a8_add_quant_rmsnorm(xd, rd, gd, 1e-6, h_out=hd, xq=xq, x_scale=xsc)] * 8)
+    us_a = time_graph(torch, ga, reps) * 1e3 / 8
+    nb = 3 * 2 * m * kk + 2 * kk + m * kk + 4 * m
+    out.append({"name": "w8a8_add_quant_rmsnorm", "m": m, "k": kk, "us": round(us_a, 2),
+                "GB/s": round(nb / (us_a * 1e-6) / 1e9, 1),
+                "frac_hbm": round(nb / (us_a * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    ql.w8a8_quant_per_token(xd, xq=xq, x_scale=xsc)
+    gp = capture(torch, [lambda: ql.w8a8_quant_per_token(xd, xq=xq, x_scale=xsc)] * 8)
+    us_p = time_graph(torch, gp, reps) * 1e3 / 8
+    nb = 2 * m * kk + m * kk + 4 * m
+    out.append({"name": "w8a8_quant_per_token", "m": m, "k": kk, "us": round(us_p, 2),
+                "GB/s": round(nb / (us_p * 1e-6) / 1e9, 1),
+                "frac_hbm": round(nb / (us_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    bias = torch.from_numpy(workloads.activations(rng, 1, nn)[0].copy()).to(dev)
+    res = torch.from_numpy(workloads.activations(rng, m, nn)).to(dev)
+    ql.w8a8_gemm_ex(xq, xsc, wqs[0], wsd, bias=bias, residual=res, out=yy)
+    ge = capture(torch, [(lambda wqd=wqd: ql.w8a8_gemm_ex(xq, xsc, wqd, wsd, bias=bias, residual=res, out=yy))
+                         for wqd in wqs])
+    us_e = time_graph(torch, ge, reps) * 1e3 / copies
+    out.append({"name": "w8a8_gemm_bias_residual", "m": m, "n": nn, "k": kk, "us": round(us_e, 2),
+                "TOP/s": round(ops / (us_e * 1e-6) / 1e12, 1),
+                "frac_mfma_int8": round(ops / (us_e * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)})
     return out
 
 
