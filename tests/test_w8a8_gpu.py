@@ -147,3 +147,33 @@ def test_gemm_fp16_epilogue_rounding(ql, m, n, k):
     want = ((acc * xs[:, None]).astype(np.float32) * ws[None, :]).astype(np.float32).astype(np.float16)
     got = y.cpu().numpy()
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+# Shapes whose 256 x 256 tiles fill whole rounds of the CUs take the 8-wave
+# 256 x 256 ring with 128-byte k-tiles: whole tiles, ragged m and n inside it,
+# n % 8 != 0 (no LDS-staged epilogue) and n % 4 != 0 (element stores).  The
+# int32 accumulator and the fp16 epilogue (with bias and residual) are checked
+# bit for bit on sampled rows.
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 512), (2000, 8100, 384), (2048, 8098, 256)])
+def test_gemm_big_tiles(ql, m, n, k):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-m // 256) * -(-n // 256)
+    if tiles % cus:
+        pytest.skip(f"{tiles} tiles do not fill whole rounds of {cus} CUs")
+    rng = np.random.default_rng(m + n + k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    xs = rng.uniform(1e-3, 1e-1, m).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    bias = (rng.standard_normal(n) * 4).astype(np.float16)
+    res = (rng.standard_normal((m, n)) * 4).astype(np.float16)
+    rows = np.unique(np.concatenate([np.arange(0, m, 37), [m - 1, m - 2, 255, 256]]))
+    acc = ql.w8a8_gemm_i32(dev(xq), dev(wq))
+    y = ql.w8a8_gemm_ex(dev(xq), dev(xs), dev(wq), dev(ws), bias=dev(bias), residual=dev(res))
+    torch.cuda.synchronize()
+    oacc = oracle.int8_gemm(xq, wq, rows=rows)
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), oacc)
+    f = (oacc.astype(np.float32) * xs[rows, None]).astype(np.float32) * ws[None, :]
+    f = (f + bias.astype(np.float32)[None, :]).astype(np.float32)
+    f = (f + res[rows].astype(np.float32)).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy()[rows].view(np.uint16), f.astype(np.float16).view(np.uint16))

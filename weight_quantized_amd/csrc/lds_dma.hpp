@@ -65,6 +65,25 @@ __device__ __forceinline__ int swz256(int r)
 
 // Host: whether the current device grants `bytes` of LDS to one workgroup
 // (gfx950: 160 KiB); queried once per device.
+// Host: compute units of the current device, queried once per device (0 if
+// the query fails).
+inline int cu_count()
+{
+    static std::atomic<int> cus[64];   // compute units + 1; 0 = not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            n = 0;
+        v = n + 1;
+        cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
 inline bool lds_fits(int bytes)
 {
     static std::atomic<int> cap[64];   // LDS bytes per workgroup + 1; 0 = not yet queried

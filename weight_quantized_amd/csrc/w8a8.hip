@@ -743,31 +743,34 @@ __device__ __forceinline__ int swz(int r)
     return BK == 64 ? ql::swz64x32(r) : ql::swz128(r);
 }
 
-template <int BM_, int BN_, int BK_, int S_, bool kMapN_>
+template <int BM_, int BN_, int BK_, int S_, bool kMapN_, int NW_ = 4>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr bool kMapN = kMapN_;   // tile order: m fastest (true) or n fastest
+    static constexpr int NW = NW_;           // waves, 2 x NW/2 over the tile
+    static constexpr int WN = NW / 2;
     static constexpr int KS = BK / 32;       // MFMA k-steps per stage
     static constexpr int CH = BK / 16;       // 16-byte chunks per LDS row
     static constexpr int RPB = 1024 / BK;    // rows filled by one 1 KiB wave load
     static constexpr int kStageBytes = (BM + BN) * BK;
     static constexpr int kLds = S * kStageBytes;
-    static constexpr int D = (BM + BN) / RPB / 4;   // direct loads per wave per stage
+    static constexpr int D = (BM + BN) / RPB / NW;  // direct loads per wave per stage
     static constexpr int kWgPerCu = kLds <= 80 * 1024 ? 2 : 1;   // workgroups that fit one CU's LDS
     static_assert(BK == 64 || BK == 128, "k-tile of 64 or 128 bytes");
-    static_assert((BM + BN) % (4 * RPB) == 0 && BM % RPB == 0, "whole 1 KiB blocks, X/W split on a block");
+    static_assert((BM + BN) % (NW * RPB) == 0 && BM % RPB == 0, "whole 1 KiB blocks, X/W split on a block");
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
 };
 
 template <class C, bool kRaw>
-__global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
+__global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
                                                              const float* __restrict__ ws, EpiTerms et,
                                                              void* out, int M, int N, int K)
 {
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, KS = C::KS, D = C::D;
-    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, KS = C::KS, D = C::D, NW = C::NW;
+    constexpr int TM = BM / 2, TN = BN / C::WN;
     constexpr int FI = TM / 32, FJ = TN / 32;          // 32x32 MFMA tiles per wave
     extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // S * kStageBytes
 
@@ -780,18 +783,18 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
     const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
 
     // This wave's direct loads: the stage is (BM + BN) rows of BK bytes in
-    // blocks of RPB rows (1 KiB); wave w fills blocks w, w+4, ...  Lane l of a
+    // blocks of RPB rows (1 KiB); wave w fills blocks w, w+NW, ...  Lane l of a
     // block writes physical chunk l % CH of row l / CH, i.e. it reads logical
     // chunk (l % CH) ^ f(row).  Rows past M or N re-read the last row.
     const uint8_t* src[D];
     uint32_t dst[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-        const int blk = wave + 4 * u;
+        const int blk = wave + NW * u;
         const int row = blk * C::RPB + lane / C::CH;
         const int c = (lane % C::CH) ^ swz<BK>(row);
         if (row < BM) {
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
     // would give each lane runs of 4 columns in 32 rows.)
     constexpr int PITCH = TN + 8;
     constexpr int HALF = TM / 2;
-    constexpr bool kStaged = 4 * HALF * PITCH * 2 <= C::kLds && FI % 2 == 0;
+    constexpr bool kStaged = NW * HALF * PITCH * 2 <= C::kLds && FI % 2 == 0;
     if constexpr (!kRaw && kStaged) {
         if (full && (N & 7) == 0) {
             uint16_t* ot = reinterpret_cast<uint16_t*>(pl) + wave * HALF * PITCH;
@@ -943,7 +946,29 @@ __global__ __launch_bounds__(256, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const 
                                full && (N & 3) == 0);
 }
 
+// Two ring configurations (measured on MI355X, K = 4096):
+//   Pipe    -- 256 x 128 tiles, 64-byte k-tiles, 3 stages (72 KiB): two
+//              workgroups per CU, so a partial last round of tiles costs little
+//   PipeBig -- 256 x 256 tiles, 128-byte k-tiles, 2 stages (128 KiB), 8 waves:
+//              a third fewer L2 -> LDS bytes per MFMA, read as whole 128-byte
+//              lines; 13% faster when its tiles fill whole rounds of the CUs
+//              (2048 x 8192: 69 vs 80 us), slower with a partial last round
+//              (2048 x 11008, 344 tiles on 256 CUs: 124 vs 114 us)
 using Pipe = PipeCfg<kQBM, kQBN, 64, 3, true>;
+using PipeBig = PipeCfg<256, 256, 128, 2, true, 8>;
+
+// PipeBig when its tiles fill whole rounds of the CUs, or at least four
+// rounds (the partial round is then a small share)
+bool use_big_tiles(int64_t m, int64_t n, int64_t k)
+{
+    if (k % PipeBig::BK || !ql::lds_fits(PipeBig::kLds))
+        return false;
+    const int64_t cus = ql::cu_count();
+    if (cus <= 0)
+        return false;
+    const int64_t tiles = ((m + PipeBig::BM - 1) / PipeBig::BM) * ((n + PipeBig::BN - 1) / PipeBig::BN);
+    return tiles >= cus && (tiles % cus == 0 || tiles >= 4 * cus);
+}
 
 template <bool kRaw>
 void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, EpiTerms et,
@@ -954,8 +979,12 @@ void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const
         const int64_t tiles = ((n + bn - 1) / bn) * ((m + bm - 1) / bm);
         return (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
     };
-    if (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds))
-        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(256),
+    if (use_big_tiles(m, n, k))
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<PipeBig, kRaw>), dim3(grid_for(PipeBig::BM, PipeBig::BN)),
+                           dim3(PipeBig::NW * 64), (size_t)PipeBig::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n,
+                           (int)k);
+    else if (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds))
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(Pipe::NW * 64),
                            (size_t)Pipe::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n, (int)k);
     else
         hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3(grid_for(kQBM, kQBN)), dim3(256), 0, st, xq, xs,
