@@ -113,6 +113,28 @@ def test_gemm_path_mid_m(ql, m, n, k, group):
     assert rel_err(y.cpu().numpy(), ref) <= TOL
 
 
+# Launches of two or more rounds of 128 x 192 tiles take the 8-wave ring
+# kernel: 1000 x 12200 gives 8 x 64 tiles with a ragged last m-tile and
+# n-tile; checked on sampled output channels at each group size.
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_gemm_eight_wave_ring(ql, group):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    m, n, k = 1000, 12200, 1024
+    if -(-m // 128) * -(-n // 192) < 2 * cus:
+        pytest.skip("fewer than two rounds of tiles on this device")
+    rng = np.random.default_rng(group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y = ql.w4a16_gemm(dev(x), *d, group, path=2)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, group)
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got[:, rows], ref) <= TOL
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_gemm_closed_forms(ql, path):
     k, group, n = 1024, 64, 96

@@ -36,6 +36,18 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base)
     asm volatile("global_load_lds_dword %1, off" : : "{m0}"(lds_base), "v"(src) : "memory");
 }
 
+// The same two loads addressed as a wave-uniform 64-bit base (scalar
+// registers) plus a 32-bit per-lane byte offset (the instructions' saddr
+// form), so a lane keeps one register per load instead of a 64-bit address.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("global_load_lds_dwordx4 %1, %2" : : "{m0}"(lds_base), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("global_load_lds_dword %1, %2" : : "{m0}"(lds_base), "v"(off), "s"(base) : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory operations are pending
 // (they complete in issue order) and its LDS reads have returned, then
 // synchronise the workgroup.  Also a compiler barrier for memory accesses.

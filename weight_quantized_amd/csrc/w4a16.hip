@@ -773,10 +773,11 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 // Tiles go to XCDs in groups of GM m-tiles (m fastest within a group), so the
 // 32 workgroups an XCD runs at once share a few activation and weight panels.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WM_, int S_, int GM_>
+template <int BM_, int BN_, int WM_, int S_, int GM_, int NW_ = 4>
 struct W4PipeCfg {
     static constexpr int BM = BM_, BN = BN_, S = S_, GM = GM_;
-    static constexpr int WM = WM_, WN = 4 / WM_;       // waves along m and n
+    static constexpr int NW = NW_;                     // waves; the first 4 issue the ring loads
+    static constexpr int WM = WM_, WN = NW_ / WM_;     // waves along m and n
     static constexpr int kArow = 256;                  // activation LDS row: 128 fp16
     static constexpr int kBrow = 64;                   // weight LDS row: 16 packed words
     static constexpr int kAbytes = BM * kArow, kBbytes = BN * kBrow;
@@ -789,8 +790,9 @@ struct W4PipeCfg {
     static constexpr int DW = (4 * kDwRows + 3) / 4;   // per wave: zero words, scale dwords 0 and 1
     static constexpr int D = DA + DB + DW;
     static_assert(kAbytes % 4096 == 0 && kBbytes % 4096 == 0, "whole 1 KiB loads for every wave");
-    static_assert(WM * WN == 4 && BM % (16 * WM) == 0 && BN % (16 * WN) == 0 && BN % 64 == 0,
-                  "4 waves of 16-row fragments, 64-row tables");
+    static_assert(WM * WN == NW && (NW == 4 || NW == 8) && BM % (16 * WM) == 0 && BN % (16 * WN) == 0 &&
+                      BN % 64 == 0,
+                  "4 or 8 waves of 16-row fragments, 64-row tables");
     static_assert(kStageBytes % 256 == 0, "stages keep the 256-byte row bank alignment");
 };
 
@@ -811,7 +813,7 @@ __device__ __forceinline__ void interleave()
 
 
 template <class C>
-__global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint16_t* __restrict__ x,
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ sc,
                                                               const uint32_t* __restrict__ qz,
@@ -842,65 +844,74 @@ __global__ __launch_bounds__(256) void w4a16_gemm_pipe_kernel(const uint16_t* __
     const int NG = K >> lg, ZW = (NG + 7) >> 3;
     const int gsh = lg - 4;                            // block kb's first group is kb << (7 - lg)
 
-    // Ring loads of this wave.  Activations: 1 KiB = 4 rows of 256 bytes,
+    // Ring loads of this wave (waves 0-3 issue them all; with 8 waves, waves
+    // 4-7 only compute, and their waits for the ring are trivially met).
+    // Activations: 1 KiB = 4 rows of 256 bytes,
     // lane l writes physical chunk l % 16 of row l / 16.  Weights: 1 KiB =
     // 16 rows of 64 bytes, lane l writes physical chunk l % 4 of row l / 4.
     // Tables: 64 rows of 4 bytes per load; load t (of 4 * BN/64, spread over
     // the waves) is zero words (t / kDwRows == 0), scale dword 0 (1), scale
     // dword 1 (2, G = 32 only, else a repeat of dword 0) or a repeat of the
     // zero words (3).  Rows past M or N re-read the last row (never stored).
-    const uint8_t* src[D];
-    uint32_t dst[D];
-    int step[D];                                       // bytes per block (tables: see issue)
+    // Each load's per-lane source is a 32-bit byte offset from its tensor
+    // (the host sends tensors of 4 GiB or more to the register-staged kernel).
+    uint32_t soff[D];
+    uint32_t tdst[D - DA - DB];                        // LDS offsets of the table loads
+    bool tscale[D - DA - DB];                          // scale dwords (else zero words)
+    const int lw = wave & 3;                           // loading wave
 #pragma unroll
     for (int u = 0; u < D; ++u) {
         if (u < DA) {
-            const int blk = wave + 4 * u;
+            const int blk = lw + 4 * u;
             const int row = blk * 4 + (lane >> 4);
             const int c = (lane & 15) ^ ql::swz256(row);
             const int m = min(m0 + row, M - 1);
-            src[u] = reinterpret_cast<const uint8_t*>(x) + (int64_t)m * K * 2 + 16 * c;
-            dst[u] = (uint32_t)(blk * 1024);
-            step[u] = 256;
+            soff[u] = (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)c;
         } else if (u < DA + DB) {
-            const int blk = wave + 4 * (u - DA);
+            const int blk = lw + 4 * (u - DA);
             const int row = blk * 16 + (lane >> 2);
             const int c = (lane & 3) ^ ql::swz64(row);
             const int n = min(n0 + row, N - 1);
-            src[u] = reinterpret_cast<const uint8_t*>(qw) + (int64_t)n * (K / 2) + 16 * c;
-            dst[u] = (uint32_t)(C::kAbytes + blk * 1024);
-            step[u] = 64;
+            soff[u] = (uint32_t)n * (uint32_t)(K / 2) + 16u * (uint32_t)c;
         } else {
-            const int t = wave + 4 * (u - DA - DB);
+            const int t = lw + 4 * (u - DA - DB);
             const int kind = t / C::kDwRows, part = t % C::kDwRows;
             const int row = 64 * part + lane;
             const int n = min(n0 + row, N - 1);
+            tscale[u - DA - DB] = kind == 1 || kind == 2;
             if (kind == 1 || kind == 2) {
                 const int extra = (kind == 2 && lg == 5) ? 4 : 0;
-                src[u] = reinterpret_cast<const uint8_t*>(sc) + (int64_t)n * NG * 2 + extra;
-                dst[u] = (uint32_t)(C::kSoff + (kind == 2 ? 4 * BN : 0) + 4 * 64 * part);
-                step[u] = -1;                          // scale dwords
+                soff[u] = (uint32_t)n * (uint32_t)NG * 2u + (uint32_t)extra;
+                tdst[u - DA - DB] = (uint32_t)(C::kSoff + (kind == 2 ? 4 * BN : 0) + 4 * 64 * part);
             } else {
-                src[u] = reinterpret_cast<const uint8_t*>(qz) + (int64_t)n * ZW * 4;
-                dst[u] = (uint32_t)(C::kZoff + 4 * 64 * part);
-                step[u] = -2;                          // zero words
+                soff[u] = (uint32_t)n * (uint32_t)ZW * 4u;
+                tdst[u - DA - DB] = (uint32_t)(C::kZoff + 4 * 64 * part);
             }
         }
     }
     auto issue = [&](int kb, int slot) {
+        if (C::NW > 4 && wave >= 4)
+            return;
         const uint32_t sbase = lds0 + slot * C::kStageBytes;
         // scale byte offset of block kb: first group * 2, aligned down to 4
-        const int soff = ((kb << (7 - lg)) * 2) & ~3;
-        const int zoff = 4 * (kb >> gsh);
+        const int sofs = ((kb << (7 - lg)) * 2) & ~3;
+        const int zofs = 4 * (kb >> gsh);
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            if (u < DA + DB) {
-                ql::dma16(src[u] + (int64_t)kb * step[u], (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
+            if (u < DA) {
+                ql::dma16s(reinterpret_cast<const uint8_t*>(x) + (int64_t)kb * 256, soff[u],
+                           (uint32_t)__builtin_amdgcn_readfirstlane(sbase + (uint32_t)((lw + 4 * u) * 1024)));
+            } else if (u < DA + DB) {
+                ql::dma16s(reinterpret_cast<const uint8_t*>(qw) + (int64_t)kb * 64, soff[u],
+                           (uint32_t)__builtin_amdgcn_readfirstlane(
+                               sbase + (uint32_t)(C::kAbytes + (lw + 4 * (u - DA)) * 1024)));
             } else {
-                // 64 rows x 4 bytes, lane l -> row 64 * part + l
-                const bool is_scale = step[u] == -1;
-                const uint8_t* p = src[u] + (is_scale ? soff : zoff);
-                ql::dma4(p, (uint32_t)__builtin_amdgcn_readfirstlane(sbase + dst[u]));
+                // 64 rows x 4 bytes, lane l -> row 64 * part + l; the table
+                // kind is the same for the whole wave
+                const bool ts = __builtin_amdgcn_readfirstlane((int)tscale[u - DA - DB]) != 0;
+                const uint8_t* b = ts ? reinterpret_cast<const uint8_t*>(sc) + sofs
+                                      : reinterpret_cast<const uint8_t*>(qz) + zofs;
+                ql::dma4s(b, soff[u], (uint32_t)__builtin_amdgcn_readfirstlane(sbase + tdst[u - DA - DB]));
             }
         }
     };
@@ -1222,13 +1233,25 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
     // 128 x 192 tiles: M=512, N=12288 gives exactly one tile per CU
     constexpr int BM = 128, BN = 192;
+    // 4 waves (1 x 4) for launches of one round of tiles; 8 waves (2 x 4, each
+    // weight word dequantised twice, two waves per SIMD) from two rounds on
+    // (M = 2048 fused QKV: 248 us against 260)
     using Pipe = W4PipeCfg<BM, BN, 1, 3, 4>;
+    using Pipe8 = W4PipeCfg<BM, BN, 2, 3, 4, 8>;
     const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
     const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);   // whole rounds over the XCDs
-    // G = 128 reads scale pairs, which needs an even number of 128-blocks
-    if (k % 128 == 0 && (group != 128 || (k / 128) % 2 == 0) && ql::lds_fits(Pipe::kLds))
-        hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe>), dim3(grid), dim3(256), (size_t)Pipe::kLds, st, xw, qw,
-                           scales, qz, y, mi, ni, ki, lg);
+    // G = 128 reads scale pairs, which needs an even number of 128-blocks;
+    // the ring kernel addresses its tensors with 32-bit offsets
+    const bool small = m * k * 2 < (1LL << 32) && n * k / 2 < (1LL << 32);
+    const int64_t cus = ql::cu_count();
+    if (k % 128 == 0 && (group != 128 || (k / 128) % 2 == 0) && small && ql::lds_fits(Pipe::kLds)) {
+        if (cus > 0 && tiles >= 2 * cus)
+            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8>), dim3(grid), dim3(Pipe8::NW * 64), (size_t)Pipe8::kLds,
+                               st, xw, qw, scales, qz, y, mi, ni, ki, lg);
+        else
+            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe>), dim3(grid), dim3(Pipe::NW * 64), (size_t)Pipe::kLds,
+                               st, xw, qw, scales, qz, y, mi, ni, ki, lg);
+    }
     else
         hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN>), dim3(grid), dim3(256), 0, st, xw, qw, scales, qz, y, mi, ni,
                            ki, lg);
