@@ -135,6 +135,25 @@ def test_gemm_eight_wave_ring(ql, group):
     assert rel_err(got[:, rows], ref) <= TOL
 
 
+# The 32-row decode kernel with 17 to 32 rows: 18 column blocks of 64
+# channels with a ragged last one, K split into slices, 128-channel groups
+# (scale after the MFMA) and 32/64-channel groups (scaled fp16 weights);
+# deterministic reruns.
+@pytest.mark.parametrize("m,group", [(24, 128), (20, 64), (32, 32)])
+def test_decode_17_to_32_rows(ql, m, group):
+    n, k = 1100, 11008 if group != 32 else 4096
+    rng = np.random.default_rng(m + group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y1 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group)
+    assert rel_err(y1.cpu().numpy(), ref) <= TOL
+
+
 @pytest.mark.parametrize("path", [1, 2])
 def test_gemm_closed_forms(ql, path):
     k, group, n = 1024, 64, 96
