@@ -52,6 +52,11 @@ def _load():
         "or_add_quant_rmsnorm": (C.c_int, [_p, _p, _i64, _i64, _p, C.c_float, _p, _p, _p, _p]),
         "or_quant_per_token": (C.c_int, [_p, _i64, _i64, _p, _p]),
         "or_w8a8_forward_ex": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p]),
+        "or_e4m3_to_f32": (C.c_float, [C.c_uint8]),
+        "or_f32_to_e4m3": (C.c_uint8, [C.c_float]),
+        "or_quant_fp8": (C.c_int, [_p, _i64, _i64, _p, C.c_float, _p, _p]),
+        "or_fp8_quant_weight": (C.c_int, [_p, _i64, _i64, _p, _p]),
+        "or_fp8_forward": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
         "or_sumsq_exact": (None, [_p, _i64, _p, _p]),
         "or_ratio_to_f32_parts": (C.c_float, [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int]),
         "or_num_threads": (C.c_int, []),
@@ -332,6 +337,64 @@ def w8a8_forward_ex(xq, x_scale, wq, w_scale, bias=None, residual=None, rows=Non
     y = np.empty((nr, nc), np.float64)
     _check(lib.or_w8a8_forward_ex(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(b), _ptr(res), _ptr(r), nr,
                                   _ptr(c), nc, _ptr(y)), "w8a8_forward_ex")
+    return y
+
+
+# ---------------------------------------------------------------- FP8 E4M3
+def e4m3_to_f32(codes):
+    """e4m3 bytes (uint8 array) -> float32 values (NaN for the NaN codes)."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    return np.array([lib.or_e4m3_to_f32(int(v)) for v in c.ravel()], np.float32).reshape(c.shape)
+
+
+def f32_to_e4m3(x):
+    """float32 -> e4m3 bytes, nearest with ties to even (NaN above 464)."""
+    lib = _load()
+    x = _c(x, np.float32)
+    return np.array([lib.or_f32_to_e4m3(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def quant_fp8(x, gamma=None, eps=1e-6):
+    """Step 10 on activations: (xq e4m3 bytes [m,k], x_scale float32 [m]);
+    RMSNorm first when gamma is given, else the plain per-token cast."""
+    lib = _load()
+    x = _bits16(x)
+    g = None if gamma is None else _bits16(gamma)
+    m, k = x.shape
+    xq = np.empty((m, k), np.uint8)
+    sc = np.empty(m, np.float32)
+    _check(lib.or_quant_fp8(_ptr(x), m, k, _ptr(g), float(eps), _ptr(xq), _ptr(sc)), "quant_fp8")
+    return xq, sc
+
+
+def fp8_quant_weight(w):
+    """Step 10 on weights: (wq e4m3 bytes [n,k], w_scale float32 [n])."""
+    lib = _load()
+    w = _c(w, np.float32)
+    n, k = w.shape
+    wq = np.empty((n, k), np.uint8)
+    sc = np.empty(n, np.float32)
+    _check(lib.or_fp8_quant_weight(_ptr(w), n, k, _ptr(wq), _ptr(sc)), "fp8_quant_weight")
+    return wq, sc
+
+
+def fp8_forward(xq, x_scale, wq, w_scale, rows=None, cols=None):
+    """Step 11: y float64 [rows, cols]; the bare accumulator when the scales are None."""
+    lib = _load()
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    xs = None if x_scale is None else _c(x_scale, np.float32)
+    ws = None if w_scale is None else _c(w_scale, np.float32)
+    m, k = xq.shape
+    n = wq.shape[0]
+    r = None if rows is None else _c(rows, np.int64)
+    c = None if cols is None else _c(cols, np.int64)
+    nr = m if r is None else len(r)
+    nc = n if c is None else len(c)
+    y = np.empty((nr, nc), np.float64)
+    _check(lib.or_fp8_forward(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(r), nr, _ptr(c), nc, _ptr(y)),
+           "fp8_forward")
     return y
 
 

@@ -46,6 +46,18 @@
  *        xq = clamp(rint(x / x_scale), -127, 127).
  *     9. the GEMM epilogue with an optional bias [n] and residual [m, n]:
  *        y = acc * x_scale * w_scale + bias + residual (fp64).
+ *   The guide's second 8-bit type, float8_e4m3fn (--quant-dtype fp8), takes
+ *   the same steps with Q_MAX = the format's largest finite value, 448, and
+ *   a cast to the format in place of rint + clamp:
+ *    10. per token x_scale = max|y| / 448, xq = e4m3(y / x_scale); per output
+ *        channel w_scale = max|W'| / 448, wq = e4m3(W' / w_scale).
+ *    11. acc = sum_j e4m3 value of xq * e4m3 value of wq (exact products,
+ *        fp64 sum), y = acc * x_scale * w_scale (fp64).
+ *   e4m3 (OCP FP8 E4M3, "fn": no infinities): sign, 4 exponent bits with bias
+ *   7, 3 fraction bits; exponent field 0 is subnormal (fraction * 2^-9); the
+ *   all-ones pattern S.1111.111 is NaN, so the largest finite value is
+ *   1.75 * 2^8 = 448.  The cast rounds to nearest, ties to even; magnitudes
+ *   above 464 (halfway to the next step) become NaN.
  *
  * Rounding: rintf under the default environment (nearest, ties to even).
  * Built with -ffp-contract=off so every fp32 operation rounds on its own.
@@ -58,6 +70,69 @@
 
 #define OR_OK 0
 #define OR_BAD -1
+
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3 ("e4m3fn"), from the format's definition                     */
+/* ------------------------------------------------------------------------ */
+
+float or_e4m3_to_f32(uint8_t b)
+{
+    const int sgn = b >> 7, e = (b >> 3) & 15, f = b & 7;
+    float v;
+    if (e == 15 && f == 7)
+        return sgn ? -NAN : NAN;
+    if (e == 0)
+        v = ldexpf((float)f, -9);
+    else
+        v = ldexpf(1.0f + (float)f / 8.0f, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Values of the non-negative finite codes 0..126 (increasing with the code). */
+static float e4m3_val[127];
+static int e4m3_ready;
+static void e4m3_init(void)
+{
+    if (e4m3_ready)
+        return;
+    for (int c = 0; c < 127; ++c)
+        e4m3_val[c] = or_e4m3_to_f32((uint8_t)c);
+    e4m3_ready = 1;
+}
+
+/* float32 -> e4m3, nearest with ties to even: find the code just below |x|
+ * (binary search over the increasing code values), then step up if |x| lies
+ * past the midpoint to the next code, or on it with an odd code below (the
+ * midpoint is exact in fp32: adjacent codes differ by a power of two).
+ * e4m3_init() must have run. */
+static uint8_t f32_to_e4m3(float x)
+{
+    const uint8_t sgn = signbit(x) ? 0x80 : 0;
+    const float a = fabsf(x);
+    if (isnan(x) || a > 464.0f)
+        return (uint8_t)(sgn | 0x7F);
+    if (a >= 448.0f)
+        return (uint8_t)(sgn | 0x7E);
+    int lo = 0, hi = 126;                         /* e4m3_val[lo] <= a < e4m3_val[hi] */
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (e4m3_val[mid] <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const float half = e4m3_val[lo] + (e4m3_val[lo + 1] - e4m3_val[lo]) / 2.0f;
+    int c = lo;
+    if (a > half || (a == half && (lo & 1)))
+        c = lo + 1;
+    return (uint8_t)(sgn | c);
+}
+
+uint8_t or_f32_to_e4m3(float x)
+{
+    e4m3_init();
+    return f32_to_e4m3(x);
+}
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16, from the format's definition                           */
@@ -581,6 +656,93 @@ int or_w8a8_forward_ex(const int8_t* xq, const float* x_scale, int64_t m, const 
                 y[a * nc + b] += (double)or_f16_to_f32(bias[j]);
             if (residual)
                 y[a * nc + b] += (double)or_f16_to_f32(residual[i * n + j]);
+        }
+    }
+    return OR_OK;
+}
+
+/*
+ * Step 10, activations: RMSNorm as step 4 (or y = x without the norm when
+ * gamma is NULL), x_scale = max|y| / 448, xq = e4m3(y / x_scale) (bytes).
+ */
+int or_quant_fp8(const uint16_t* x, int64_t m, int64_t k, const uint16_t* gamma, float eps, uint8_t* xq,
+                 float* x_scale)
+{
+    if (k <= 0)
+        return OR_BAD;
+    e4m3_init();
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* y = (float*)malloc((size_t)k * sizeof(float));
+        if (!y) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < m; ++i) {
+                const uint16_t* xr = x + i * k;
+                float r = 1.0f;
+                if (gamma) {
+                    float ms = or_ratio_to_f32(sumsq_exact(xr, k), (uint64_t)k, -48);
+                    r = 1.0f / sqrtf(ms + eps);
+                }
+                float amax = 0.0f;
+                for (int64_t j = 0; j < k; ++j) {
+                    y[j] = gamma ? (or_f16_to_f32(xr[j]) * r) * or_f16_to_f32(gamma[j]) : or_f16_to_f32(xr[j]);
+                    if (fabsf(y[j]) > amax)
+                        amax = fabsf(y[j]);
+                }
+                float sc = amax / 448.0f;
+                x_scale[i] = sc;
+                for (int64_t j = 0; j < k; ++j)
+                    xq[i * k + j] = sc > 0.0f ? f32_to_e4m3(y[j] / sc) : 0;
+            }
+        }
+        free(y);
+    }
+    return bad ? OR_BAD : OR_OK;
+}
+
+/* Step 10, weights: per output channel w_scale = max_j |W'| / 448,
+ * wq = e4m3(W' / w_scale); an all-zero row gets codes 0 and scale 0. */
+int or_fp8_quant_weight(const float* w, int64_t n, int64_t k, uint8_t* wq, float* w_scale)
+{
+    e4m3_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < k; ++j)
+            if (fabsf(w[i * k + j]) > amax)
+                amax = fabsf(w[i * k + j]);
+        float sc = amax / 448.0f;
+        w_scale[i] = sc;
+        for (int64_t j = 0; j < k; ++j)
+            wq[i * k + j] = sc > 0.0f ? f32_to_e4m3(w[i * k + j] / sc) : 0;
+    }
+    return OR_OK;
+}
+
+/* Step 11 on a sub-grid: y float64 [nr, nc] (acc alone when the scales are NULL). */
+int or_fp8_forward(const uint8_t* xq, const float* x_scale, int64_t m, const uint8_t* wq, const float* w_scale,
+                   int64_t n, int64_t k, const int64_t* rows, int64_t nr, const int64_t* cols, int64_t nc, double* y)
+{
+    if (!rows)
+        nr = m;
+    if (!cols)
+        nc = n;
+    double lut[256];
+    for (int c = 0; c < 256; ++c)
+        lut[c] = (double)or_e4m3_to_f32((uint8_t)c);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t a = 0; a < nr; ++a) {
+        int64_t i = rows ? rows[a] : a;
+        for (int64_t b = 0; b < nc; ++b) {
+            int64_t j = cols ? cols[b] : b;
+            double s = 0.0;
+            for (int64_t c = 0; c < k; ++c)
+                s += lut[xq[i * k + c]] * lut[wq[j * k + c]];
+            y[a * nc + b] = (x_scale && w_scale) ? s * (double)x_scale[i] * (double)w_scale[j] : s;
         }
     }
     return OR_OK;

@@ -514,3 +514,95 @@ def test_w8a8_epilogue_bias_residual_closed_forms():
             want = (Fraction(acc) * Fraction(float(xs2[i])) * Fraction(float(ws2[j])) + Fraction(float(bias[j]))
                     + Fraction(float(res[i, j])))
             assert Fraction(y[a, b]) == want
+
+
+# --------------------------------------------------------------------------- FP8 E4M3 (float8_e4m3fn)
+def _torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    import torch
+    c = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_to_f32(c)
+    want = torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    assert got[0x7E] == 448 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_encode_vs_torch_midpoints_and_random():
+    vals = oracle.e4m3_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2                        # exact in float32
+    pts = np.concatenate([vals, mids, [464.0, 460.0]]).astype(np.float32)
+    near = np.concatenate([pts, np.nextafter(pts, np.float32(np.inf)), np.nextafter(pts, np.float32(0))])
+    rng = np.random.default_rng(41)
+    rnd = (rng.standard_normal(20000) * rng.choice(np.array([1e-3, 0.05, 1.0, 30.0, 150.0]), 20000)).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 464]
+    x = np.concatenate([near, -near, rnd, np.float32([0.0, -0.0])]).astype(np.float32)
+    assert np.array_equal(oracle.f32_to_e4m3(x), _torch_e4m3(x))
+
+
+def test_quant_fp8_closed_forms_and_bound():
+    k = 256
+    x = np.zeros((4, k), np.float16)
+    x[0, 3] = -2.5                                           # single nonzero element
+    x[2] = np.float16(0.75)                                  # constant row
+    x[3] = np.linspace(-6, 6, k).astype(np.float16)
+    q, s = oracle.quant_fp8(x)
+    assert s[0] == np.float32(2.5) / np.float32(448) and q[0, 3] == 0xFE and np.count_nonzero(q[0]) == 1
+    assert s[1] == 0 and not q[1].any()
+    assert (q[2] == 0x7E).all()
+    rng = np.random.default_rng(42)
+    xr = (rng.standard_normal((16, k)) * rng.uniform(0.01, 50, (16, 1))).astype(np.float16)
+    q, s = oracle.quant_fp8(xr)
+    dq = oracle.e4m3_to_f32(q).astype(np.float64) * s[:, None].astype(np.float64)
+    y = xr.astype(np.float64)
+    # half a step of a 3-bit fraction, or half the subnormal step, plus the fp32 quotient's rounding
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 1e-6)
+    assert (np.abs(dq - y) <= bound).all()
+    assert (np.abs(oracle.e4m3_to_f32(q)).max(axis=1) == 448).all()
+    qn, sn = oracle.quant_fp8(-xr)
+    assert np.array_equal(qn, np.where(q & 0x7F, q ^ 0x80, q)) and np.array_equal(sn, s)
+    q8, s8 = oracle.quant_fp8((xr.astype(np.float32) * 8).astype(np.float16))
+    assert np.array_equal(q8, q) and np.array_equal(s8, s * np.float32(8))
+
+
+def test_quant_fp8_norm_matches_the_pinned_qrmsnorm():
+    """With gamma, step 10 normalises exactly as the pinned int8 QRMSNorm: both
+    scales come from the same max|y| (one fp32 division by 448, one by 127)."""
+    x, gamma, _ = workloads.smoothquant_inputs(m=16, k=1024, n=8, seed=4)
+    _, s8 = oracle.quant_fp8(x, gamma)
+    _, s1 = oracle.quant_rmsnorm(x, gamma)
+    a8 = s8.astype(np.float64) * 448
+    a1 = s1.astype(np.float64) * 127
+    assert np.allclose(a8, a1, rtol=2.0 ** -22)
+
+
+def test_fp8_weight_quant_closed_forms():
+    w = np.zeros((3, 64), np.float32)
+    w[0, 7] = -3.0
+    w[2] = np.linspace(-1, 1, 64, dtype=np.float32)
+    q, s = oracle.fp8_quant_weight(w)
+    assert s[0] == np.float32(3.0) / np.float32(448) and q[0, 7] == 0xFE and np.count_nonzero(q[0]) == 1
+    assert s[1] == 0 and not q[1].any()
+    assert q[2, 0] == 0xFE and q[2, -1] == 0x7E
+
+
+def test_fp8_gemm_exact_rationals():
+    rng = np.random.default_rng(43)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # no NaN codes
+    xq = rng.choice(codes, size=(3, 40))
+    wq = rng.choice(codes, size=(5, 40))
+    acc = oracle.fp8_forward(xq, None, wq, None)
+    xv, wv = oracle.e4m3_to_f32(xq), oracle.e4m3_to_f32(wq)
+    for i in range(3):
+        for j in range(5):
+            want = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xv[i], wv[j]))
+            assert Fraction(acc[i, j]) == want
+    xs = rng.uniform(0.01, 1, 3).astype(np.float32)
+    ws = rng.uniform(0.01, 1, 5).astype(np.float32)
+    y = oracle.fp8_forward(xq, xs, wq, ws, rows=np.array([2]), cols=np.array([4, 0]))
+    assert y[0, 0] == acc[2, 4] * float(xs[2]) * float(ws[4]) and y[0, 1] == acc[2, 0] * float(xs[2]) * float(ws[0])
