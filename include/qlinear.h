@@ -251,6 +251,60 @@ int ql_w8a8_gemm_ex(const int8_t* xq, const float* x_scale, const int8_t* wq, co
                     const uint16_t* bias, const uint16_t* residual, uint16_t* y,
                     int64_t m, int64_t n, int64_t k, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* W8A8 with FP8 E4M3 (float8_e4m3fn) codes                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * The LMDeploy W8A8 guide's second 8-bit type (--quant-dtype fp8 is
+ * float8_e4m3fn; Q_MAX is the type's largest finite value, 448; the codes are
+ * a cast, not rint + clamp; the GEMM accumulates in fp32).  Codes are OCP FP8
+ * E4M3 bytes: sign, 4 exponent bits with bias 7, 3 fraction bits, no
+ * infinities, S.1111.111 is NaN.  The cast rounds to nearest, ties to even.
+ */
+
+/*
+ * ql_fp8_quant_weight (host, synchronous).  Per output channel n:
+ *   w_scale[n] = max_j |w[n,j]| / 448,  wq[n,j] = e4m3(w[n,j] / w_scale[n])
+ * (an all-zero row gets scale 0 and codes 0).  w fp32 [n, k] (host); wq uint8
+ * [n, k] and w_scale float32 [n] (host, written).
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_VALUE (non-finite weight).
+ */
+int ql_fp8_quant_weight(const float* w, int64_t n, int64_t k, uint8_t* wq, float* w_scale);
+
+/*
+ * ql_fp8_quant_rmsnorm (device).  QRMSNorm with FP8 codes: y as in
+ * ql_w8a8_quant_rmsnorm, then x_scale[i] = max_j |y_j| / 448 and
+ * xq[i,j] = e4m3(y_j / x_scale[i]) (correctly rounded fp32 divisions).
+ *   x fp16 [m, k], gamma fp16 [k] (device); xq uint8 [m, k], x_scale float32
+ *   [m] (device, written).  k <= 65536.  Inputs must be finite.
+ * Errors: as ql_w8a8_quant_rmsnorm.
+ */
+int ql_fp8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps,
+                         uint8_t* xq, float* x_scale, int64_t m, int64_t k, void* stream);
+
+/*
+ * ql_fp8_quant_per_token (device).  Per-token FP8 quantisation of a plain
+ * activation: x_scale[i] = max_j |x[i,j]| / 448, xq[i,j] = e4m3(x[i,j] / x_scale[i]).
+ * Arguments and errors as ql_w8a8_quant_per_token (xq uint8 bytes).
+ */
+int ql_fp8_quant_per_token(const uint16_t* x, uint8_t* xq, float* x_scale,
+                           int64_t m, int64_t k, void* stream);
+
+/*
+ * ql_fp8_gemm (device).  FP8 QLinear: acc[i,j] = sum_k e4m3(xq[i,k]) *
+ * e4m3(wq[j,k]), products exact and summed in fp32 by the matrix cores (order
+ * unspecified), then the epilogue of ql_w8a8_gemm_ex:
+ *   y = fp16(fp32(fp32(fp32(fp32(acc * x_scale[i]) * w_scale[j]) + bias[j]) + residual[i,j]))
+ *   xq uint8 [m, k], x_scale float32 [m], wq uint8 [n, k], w_scale float32
+ *   [n], bias fp16 [n] or NULL, residual fp16 [m, n] or NULL (device); y fp16
+ *   [m, n] (device, written; may be residual).  k % 64 == 0.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED
+ * (k % 64, or k above 131072), QL_ERR_HIP.
+ */
+int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
+                const uint16_t* bias, const uint16_t* residual, uint16_t* y,
+                int64_t m, int64_t n, int64_t k, void* stream);
+
 /* ql_w8a8_gemm_i32 (device).  The same int8 MFMA main loop writing the raw
  * int32 accumulator acc [m, n] instead of the fp16 epilogue. */
 int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,

@@ -157,3 +157,26 @@ def test_w8a8_fused_validation():
     assert g(FAKE, FAKE, FAKE, FAKE, None, MIS, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
     assert g(FAKE, None, FAKE, FAKE, None, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
     assert g(None, None, None, None, None, None, None, 0, 64, 128, DEF) == E["QL_OK"]
+
+
+def test_fp8_validation():
+    E = CODES
+    q = LIB.ql_fp8_quant_rmsnorm
+    assert q(FAKE, FAKE, 1e-6, FAKE, FAKE, 4, 100, DEF) == E["QL_ERR_SHAPE"]
+    assert q(FAKE, None, 1e-6, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+    assert q(FAKE, FAKE, float("nan"), FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_VALUE"]
+    assert q(None, None, 1e-6, None, None, 0, 128, DEF) == E["QL_OK"]
+    p = LIB.ql_fp8_quant_per_token
+    assert p(FAKE, FAKE, FAKE, 4, 100, DEF) == E["QL_ERR_SHAPE"]
+    assert p(MIS, FAKE, FAKE, 4, 128, DEF) == E["QL_ERR_ALIGN"]
+    g = LIB.ql_fp8_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 64, 100, DEF) == E["QL_ERR_SHAPE"]       # k % 16
+    assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 64, 96, DEF) == E["QL_ERR_UNSUPPORTED"]  # k % 64
+    assert g(FAKE, None, FAKE, FAKE, None, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
+    assert g(FAKE, FAKE, FAKE, FAKE, MIS, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
+    assert g(None, None, None, None, None, None, None, 0, 64, 128, DEF) == E["QL_OK"]
+    w = np.zeros((2, 8), np.float32)
+    wq = np.zeros((2, 8), np.uint8)
+    ws = np.zeros(2, np.float32)
+    w[1, 3] = np.inf
+    assert LIB.ql_fp8_quant_weight(w.ctypes.data, 2, 8, wq.ctypes.data, ws.ctypes.data) == E["QL_ERR_VALUE"]

@@ -90,3 +90,28 @@ def test_smoothquant_full_workload_matches_oracle():
     wq, wsc = ql.w8a8_quant_weight(ws)
     owq, owsc = oracle.w8_quant_weight(ows)
     assert np.array_equal(wq, owq) and np.array_equal(wsc, owsc)
+
+
+def test_fp8_weight_quant_matches_oracle():
+    """Per-channel FP8 E4M3 weights of the smoothed SmoothQuant workload,
+    bit-exact against the oracle, plus rows that reach the subnormal codes,
+    a zero row and a single nonzero."""
+    x, gamma, w = workloads.smoothquant_inputs(m=64, k=1024, n=96, seed=9)
+    _, _, ws = ql.smooth(x, gamma, w)
+    ws[0] = 0
+    ws[1] = 0
+    ws[1, 5] = -7.0
+    ws[2] *= np.logspace(-6, 0, ws.shape[1], dtype=np.float32)   # values far below the row maximum
+    wq, wsc = ql.fp8_quant_weight(ws)
+    oq, osc = oracle.fp8_quant_weight(ws)
+    assert np.array_equal(wq, oq) and np.array_equal(wsc.view(np.uint32), osc.view(np.uint32))
+    assert not wq[0].any() and wsc[0] == 0 and wq[1, 5] == 0xFE
+    assert (wq[2] & 0x78 == 0).any()                           # subnormal codes reached
+
+
+def test_fp8_weight_quant_full_workload_matches_oracle():
+    x, gamma, w = workloads.smoothquant_inputs()
+    _, _, ws = ql.smooth(x, gamma, w)
+    wq, wsc = ql.fp8_quant_weight(ws)
+    oq, osc = oracle.fp8_quant_weight(ws)
+    assert np.array_equal(wq, oq) and np.array_equal(wsc.view(np.uint32), osc.view(np.uint32))

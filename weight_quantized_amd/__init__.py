@@ -44,6 +44,10 @@ EXPORTS = {
     "ql_w8a8_quant_per_token": (_i, [_p, _p, _p, _i64, _i64, _p]),
     "ql_w8a8_gemm_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "ql_w8a8_gemm_i32": (_i, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "ql_fp8_quant_weight": (_i, [_p, _i64, _i64, _p, _p]),
+    "ql_fp8_quant_rmsnorm": (_i, [_p, _p, C.c_float, _p, _p, _i64, _i64, _p]),
+    "ql_fp8_quant_per_token": (_i, [_p, _p, _p, _i64, _i64, _p]),
+    "ql_fp8_gemm": (_i, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "ql_status_string": (C.c_char_p, [_i]),
     "ql_last_error": (C.c_char_p, []),
     "ql_version": (_i, []),
@@ -317,6 +321,71 @@ def w8a8_gemm(xq, x_scale, wq, w_scale, out=None):
         out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
     _check(_lib.ql_w8a8_gemm(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
                              out.data_ptr(), m, n, k, _stream(xq)))
+    return out
+
+
+def fp8_quant_weight(w):
+    """Per-channel FP8 E4M3 weights: (wq uint8 codes [n, k], w_scale float32 [n])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    wq = np.empty((n, k), np.uint8)
+    sc = np.empty(n, np.float32)
+    _check(_lib.ql_fp8_quant_weight(w.ctypes.data, n, k, wq.ctypes.data, sc.ctypes.data))
+    return wq, sc
+
+
+def fp8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
+    """QRMSNorm with FP8 E4M3 codes: (xq uint8 [m, k], x_scale float32 [m])."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    gamma = _dev(gamma, torch.float16, "gamma")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_fp8_quant_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), xq.data_ptr(),
+                                     x_scale.data_ptr(), m, k, _stream(x)))
+    return xq, x_scale
+
+
+def fp8_quant_per_token(x, xq=None, x_scale=None):
+    """Per-token FP8 E4M3 quantisation: (xq uint8 [m, k], x_scale float32 [m])."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_fp8_quant_per_token(x.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
+    return xq, x_scale
+
+
+def fp8_gemm(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
+    """y fp16 [m, n] = fp16(sum(e4m3 xq * e4m3 wq) * x_scale * w_scale [+ bias] [+ residual])."""
+    torch = _torch()
+    xq = _dev(xq, torch.uint8, "xq")
+    wq = _dev(wq, torch.uint8, "wq")
+    x_scale = _dev(x_scale, torch.float32, "x_scale")
+    w_scale = _dev(w_scale, torch.float32, "w_scale")
+    m, k = xq.shape
+    n = wq.shape[0]
+    if bias is not None:
+        bias = _dev(bias, torch.float16, "bias")
+        if bias.shape != (n,):
+            raise ValueError("bias must be [n]")
+    if residual is not None:
+        residual = _dev(residual, torch.float16, "residual")
+        if residual.shape != (m, n):
+            raise ValueError("residual must be [m, n]")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
+    out = _dev(out, torch.float16, "out")
+    _check(_lib.ql_fp8_gemm(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
+                            bias.data_ptr() if bias is not None else None,
+                            residual.data_ptr() if residual is not None else None, out.data_ptr(), m, n, k,
+                            _stream(xq)))
     return out
 
 

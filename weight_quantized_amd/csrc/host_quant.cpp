@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <thread>
 #include <vector>
 
@@ -187,6 +188,63 @@ extern "C" int ql_w8a8_quant_weight(const float* w, int64_t n, int64_t k, int8_t
             w_scale[r] = sc;
             for (int64_t j = 0; j < k; ++j)
                 wq[r * k + j] = sc > 0.0f ? (int8_t)clamp_code((int)std::nearbyint(v[j] / sc), -127, 127) : 0;
+        }
+    });
+    return QL_OK;
+}
+
+// fp32 -> OCP FP8 E4M3 code, nearest with ties to even (|v| <= 448 here:
+// v = w / (max|w| / 448) stays within one fp32 rounding of 448).  Normal
+// range: the fp32 pattern rounded to 3 fraction bits by integer addition, the
+// exponent rebiased from 127 to 7; below 2^-6, multiples of 2^-9.
+static uint8_t e4m3_code(float v)
+{
+    uint32_t b;
+    std::memcpy(&b, &v, sizeof b);
+    const uint32_t sgn = (b >> 24) & 0x80u;
+    const float a = std::fabs(v);
+    uint32_t c;
+    if (a >= 448.0f) {
+        c = 0x7Eu;
+    } else if (a < 0x1p-6f) {
+        c = (uint32_t)std::nearbyint(a * 512.0f);
+    } else {
+        const uint32_t ab = b & 0x7FFFFFFFu;
+        const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & ~0xFFFFFu;
+        c = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    }
+    return (uint8_t)(sgn | c);
+}
+
+extern "C" int ql_fp8_quant_weight(const float* w, int64_t n, int64_t k, uint8_t* wq, float* w_scale)
+{
+    ql::clear_error();
+    if (!w || !wq || !w_scale)
+        QL_FAIL(QL_ERR_NULL, "ql_fp8_quant_weight: null pointer");
+    if (n < 0 || k <= 0)
+        QL_FAIL(QL_ERR_SHAPE, "ql_fp8_quant_weight: n=%lld k=%lld", (long long)n, (long long)k);
+    std::vector<float> amax((size_t)n, 0.0f);
+    std::atomic<int> bad{0};
+    parallel_rows(n, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r) {
+            float a = 0.0f;
+            for (int64_t j = 0; j < k; ++j) {
+                if (!std::isfinite(w[r * k + j]))
+                    bad.store(1);
+                a = std::max(a, std::fabs(w[r * k + j]));
+            }
+            amax[r] = a;
+        }
+    });
+    if (bad.load())
+        QL_FAIL(QL_ERR_VALUE, "ql_fp8_quant_weight: non-finite weight");
+    parallel_rows(n, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r) {
+            const float* v = w + r * k;
+            const float sc = amax[r] / 448.0f;
+            w_scale[r] = sc;
+            for (int64_t j = 0; j < k; ++j)
+                wq[r * k + j] = sc > 0.0f ? e4m3_code(v[j] / sc) : 0;
         }
     });
     return QL_OK;

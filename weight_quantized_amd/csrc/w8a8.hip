@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "lds_dma.hpp"
 #include "ql_common.hpp"
@@ -229,14 +230,40 @@ __device__ __forceinline__ uint4 add_h8(uint4 a, uint4 b)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// fp32 -> OCP FP8 E4M3 ("e4m3fn") code, nearest with ties to even, for
+// |v| <= 448 (larger magnitudes saturate to 448; the quantisers never pass
+// any).  Normal range: round the fp32 pattern to 3 fraction bits by integer
+// addition (ties to even) and rebias the exponent (127 -> 7).  Below 2^-6 the
+// codes are multiples of 2^-9: rint(|v| * 2^9) (exact scaling), where the
+// result 8 is the smallest normal code.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sgn = (b >> 24) & 0x80u;
+    const float a = fabsf(v);
+    uint32_t c;
+    if (a >= 448.0f) {
+        c = 0x7Eu;
+    } else if (a < 0x1p-6f) {
+        c = (uint32_t)rintf(a * 512.0f);
+    } else {
+        const uint32_t ab = b & 0x7FFFFFFFu;
+        const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & ~0xFFFFFu;
+        c = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    }
+    return sgn | c;
+}
+
 // Per-token quantisers, one workgroup per token.  MODE:
 //   kNormQuant    -- QRMSNorm: y = RMSNorm(x) * gamma, then per-token int8
 //   kAddNormQuant -- h = fp16(x + residual) written to h_out (the residual
 //                    stream; h_out may be residual itself), then QRMSNorm of h
 //   kTokenQuant   -- y = x (no norm, no gamma), then per-token int8
+//   kNormQuantF8, kTokenQuantF8 -- as kNormQuant and kTokenQuant with FP8
+//                    E4M3 codes: x_scale = max|y| / 448, code = e4m3(y / x_scale)
 // x, residual and h_out are not restrict: h_out may be x or residual, and an
 // in-place update reads each chunk before the same thread overwrites it.
-constexpr int kNormQuant = 0, kAddNormQuant = 1, kTokenQuant = 2;
+constexpr int kNormQuant = 0, kAddNormQuant = 1, kTokenQuant = 2, kNormQuantF8 = 3, kTokenQuantF8 = 4;
 
 template <int CPT, int MODE>
 __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint16_t* x,
@@ -245,6 +272,8 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
                                                                      uint16_t* h_out, int8_t* __restrict__ xq,
                                                                      float* __restrict__ x_scale, int K)
 {
+    constexpr bool kF8 = MODE == kNormQuantF8 || MODE == kTokenQuantF8;
+    constexpr bool kNoNorm = MODE == kTokenQuant || MODE == kTokenQuantF8;
     __shared__ U128 s_sum[kNormThreads / 64];
     __shared__ double s_sumd[kNormThreads / 64];
     __shared__ float s_max[kNormThreads / 64];
@@ -269,7 +298,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             g = gv[i];
         } else {
             v = xr[c];
-            g = MODE == kTokenQuant ? make_uint4(0u, 0u, 0u, 0u) : gr[c];
+            g = kNoNorm ? make_uint4(0u, 0u, 0u, 0u) : gr[c];
         }
     };
     if constexpr (CPT > 0) {
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             const int c = (int)threadIdx.x + i * kNormThreads;
             const int cc = c < nch ? c : nch - 1;
             xv[i] = xr[cc];
-            gv[i] = MODE == kTokenQuant ? make_uint4(0u, 0u, 0u, 0u) : gr[cc];
+            gv[i] = kNoNorm ? make_uint4(0u, 0u, 0u, 0u) : gr[cc];
             if constexpr (MODE == kAddNormQuant)
                 rv[i] = reinterpret_cast<const uint4*>(residual + (int64_t)row * K)[cc];
         }
@@ -301,7 +330,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     // rounding is not certain, the exact 128-bit integer sum (the decision is
     // taken on the workgroup total, so the whole workgroup branches together)
     float r = 1.0f;
-    if constexpr (MODE != kTokenQuant) {
+    if constexpr (!kNoNorm) {
         double accd = 0.0;
 #pragma unroll R
         for (int i = 0; i < npass; ++i) {
@@ -341,7 +370,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
         const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if constexpr (MODE == kTokenQuant) {
+            if constexpr (kNoNorm) {
                 yo[2 * e] = h2f(w[e] & 0xFFFFu);
                 yo[2 * e + 1] = h2f(w[e] >> 16);
             } else {
@@ -365,7 +394,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
         }
     }
     amax = block_max<kNormThreads>(amax, s_max);
-    const float scale = __fdiv_rn(amax, 127.0f);
+    const float scale = __fdiv_rn(amax, kF8 ? 448.0f : 127.0f);
     if (threadIdx.x == 0)
         x_scale[row] = scale;
 
@@ -377,6 +406,8 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     auto code = [&](float yv) -> uint32_t {
         if (!(scale > 0.0f))
             return 0u;
+        if constexpr (kF8)
+            return f32_to_e4m3(__fdiv_rn(yv, scale));
         const float q0 = yv * rcp;
         float qr = rintf(q0);
         const float half = floorf(q0) + 0.5f;
@@ -443,6 +474,22 @@ __device__ __forceinline__ i16_t mfma_i8_32(i4_t a, i4_t b, i16_t c)
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// FP8 E4M3 x E4M3 -> fp32 on the same 16-byte fragments: each half (8 codes
+// per lane) is one MFMA 32x32x16.  A and B are split alike, so the two
+// instructions cover the fragment's 32 k once, in some order of k.
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f16v_t mfma_f8_32(i4_t a, i4_t b, f16v_t c)
+{
+    const long a0 = (long)(uint32_t)a[0] | ((long)(uint32_t)a[1] << 32);
+    const long a1 = (long)(uint32_t)a[2] | ((long)(uint32_t)a[3] << 32);
+    const long b0 = (long)(uint32_t)b[0] | ((long)(uint32_t)b[1] << 32);
+    const long b1 = (long)(uint32_t)b[2] | ((long)(uint32_t)b[3] << 32);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, c, 0, 0, 0);
+}
+__device__ __forceinline__ float acc_f(int v) { return (float)v; }
+__device__ __forceinline__ float acc_f(float v) { return v; }
+
 // tile index of workgroup `wg` so that each XCD gets a contiguous run of tiles
 __device__ __forceinline__ int xcd_tile(int wg, int ntiles)
 {
@@ -460,9 +507,9 @@ struct EpiTerms {
     const uint16_t* bias;   // [N] fp16 or null
     const uint16_t* res;    // [M, N] fp16 or null; may be the output itself
 };
-__device__ __forceinline__ uint32_t epi_h(int32_t acc, float xs, float ws, const EpiTerms& et, float b, float r)
+__device__ __forceinline__ uint32_t epi_h(float acc, float xs, float ws, const EpiTerms& et, float b, float r)
 {
-    float f = __fmul_rn(__fmul_rn((float)acc, xs), ws);
+    float f = __fmul_rn(__fmul_rn(acc, xs), ws);
     if (et.bias)
         f = __fadd_rn(f, b);
     if (et.res)
@@ -499,7 +546,7 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
             }
     }
     auto to_h = [&](int i, int j, int r, float rv) -> uint32_t {
-        return epi_h(acc[i][j][r], xsv[i], wsv[j][r], et, bsv[j][r], rv);
+        return epi_h((float)acc[i][j][r], xsv[i], wsv[j][r], et, bsv[j][r], rv);
     };
     if (vec) {
 #pragma unroll
@@ -544,8 +591,8 @@ __device__ __forceinline__ void store_tile(const i4_t (&acc)[FI][FJ], const floa
 // operand): fragment (i, j) of a wave holds y rows mrow + 32 i + l%32 and
 // columns ncol + 32 j + 8 (v/4) + 4 (l/32) + v%4, so each lane owns runs of
 // four consecutive columns (8-byte fp16 stores).  Same rounding as store_tile.
-template <int FI, int FJ, bool kRaw>
-__device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const float* __restrict__ xs,
+template <int FI, int FJ, bool kRaw, class AccT>
+__device__ __forceinline__ void store_tile32(const AccT (&acc)[FI][FJ], const float* __restrict__ xs,
                                              const float* __restrict__ ws, const EpiTerms& et, void* out, int M,
                                              int N, int mrow, int ncol, bool vec)
 {
@@ -564,7 +611,7 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
             }
     }
     auto to_h = [&](int i, int j, int v, float rv) -> uint32_t {
-        return epi_h(acc[i][j][v], xsv[i], wsv[j][v], et, bsv[j][v], rv);
+        return epi_h(acc_f(acc[i][j][v]), xsv[i], wsv[j][v], et, bsv[j][v], rv);
     };
     if (vec) {
 #pragma unroll
@@ -574,7 +621,7 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int64_t o = (int64_t)(mrow + 32 * i) * N + ncol + 32 * j + 8 * g;
-                    if (kRaw) {
+                    if constexpr (kRaw) {
                         const i4_t v4 = i4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                              acc[i][j][4 * g + 3]};
                         *reinterpret_cast<i4_t*>(static_cast<int32_t*>(out) + o) = v4;
@@ -601,7 +648,7 @@ __device__ __forceinline__ void store_tile32(const i16_t (&acc)[FI][FJ], const f
                 if (n >= N)
                     continue;
                 const int64_t o = (int64_t)m * N + n;
-                if (kRaw)
+                if constexpr (kRaw)
                     static_cast<int32_t*>(out)[o] = acc[i][j][v];
                 else
                     static_cast<uint16_t*>(out)[o] = (uint16_t)to_h(i, j, v, et.res ? h2f(et.res[o]) : 0.0f);
@@ -762,7 +809,7 @@ struct PipeCfg {
     static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
 };
 
-template <class C, bool kRaw>
+template <class C, bool kRaw, bool kF8 = false>
 __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel(const int8_t* __restrict__ xq,
                                                              const float* __restrict__ xs,
                                                              const int8_t* __restrict__ wq,
@@ -813,12 +860,14 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
                   (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * C::kStageBytes + dst[u]));
     };
 
-    i16_t acc[FI][FJ];
+    using AccT = std::conditional_t<kF8, f16v_t, i16_t>;
+    static_assert(!(kF8 && kRaw), "FP8 has no raw accumulator export");
+    AccT acc[FI][FJ];
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
-            acc[i][j] = i16_t{};
+            acc[i][j] = AccT{};
 
     // fragments of k-step j (32 bytes of k) of a stage: lane l reads row
     // l%32 of the fragment, chunk 2j + l/32, swizzled
@@ -875,7 +924,10 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
             for (int i = 0; i < FI; ++i)
 #pragma unroll
                 for (int jj = 0; jj < FJ; ++jj)
-                    acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
+                    if constexpr (kF8)
+                        acc[i][jj] = mfma_f8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
+                    else
+                        acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
@@ -907,7 +959,7 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
                     bsv[jj][v] = et.bias ? h2f(et.bias[n]) : 0.0f;
                 }
             auto to_h = [&](int i, int jj, int v, float rv) -> uint32_t {
-                return epi_h(acc[i][jj][v], xsv[i], wsv[jj][v], et, bsv[jj][v], rv);
+                return epi_h(acc_f(acc[i][jj][v]), xsv[i], wsv[jj][v], et, bsv[jj][v], rv);
             };
             // a residual that is the output itself: each half reads its rows
             // before storing them, and the halves and waves cover disjoint rows
@@ -970,7 +1022,7 @@ bool use_big_tiles(int64_t m, int64_t n, int64_t k)
     return tiles >= cus && (tiles % cus == 0 || tiles >= 4 * cus);
 }
 
-template <bool kRaw>
+template <bool kRaw, bool kF8 = false>
 void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws, EpiTerms et,
                       void* out, int64_t m, int64_t n, int64_t k, hipStream_t st)
 {
@@ -980,11 +1032,11 @@ void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const
         return (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
     };
     if (use_big_tiles(m, n, k))
-        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<PipeBig, kRaw>), dim3(grid_for(PipeBig::BM, PipeBig::BN)),
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<PipeBig, kRaw, kF8>), dim3(grid_for(PipeBig::BM, PipeBig::BN)),
                            dim3(PipeBig::NW * 64), (size_t)PipeBig::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n,
                            (int)k);
-    else if (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds))
-        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(Pipe::NW * 64),
+    else if (kF8 || (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds)))   // FP8: the host checks k % 64 and LDS
+        hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw, kF8>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(Pipe::NW * 64),
                            (size_t)Pipe::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n, (int)k);
     else
         hipLaunchKernelGGL((w8a8_gemm_kernel<kQBM, kQBN, kRaw>), dim3(grid_for(kQBM, kQBN)), dim3(256), 0, st, xq, xs,
@@ -1031,14 +1083,15 @@ int launch_token_quant(const char* who, const uint16_t* x, const uint16_t* resid
                 (long long)k);
     if (k > 65536 || m > (1LL << 31) - 1)
         QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld above 65536", who, (long long)k);
-    if (MODE != kTokenQuant && (!(eps >= 0.0f) || !(eps < 1e30f)))
+    constexpr bool kNoNorm = MODE == kTokenQuant || MODE == kTokenQuantF8;
+    if (!kNoNorm && (!(eps >= 0.0f) || !(eps < 1e30f)))
         QL_FAIL(QL_ERR_VALUE, "%s: eps must be finite and >= 0", who);
     if (m == 0)
         return QL_OK;
-    if (!x || !xq || !x_scale || (MODE != kTokenQuant && !gamma) || (MODE == kAddNormQuant && (!residual || !h_out)))
+    if (!x || !xq || !x_scale || (!kNoNorm && !gamma) || (MODE == kAddNormQuant && (!residual || !h_out)))
         QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
     if (!ql::aligned16(x) || !ql::aligned16(xq) || !ql::aligned16(x_scale) ||
-        (MODE != kTokenQuant && !ql::aligned16(gamma)) ||
+        (!kNoNorm && !ql::aligned16(gamma)) ||
         (MODE == kAddNormQuant && (!ql::aligned16(residual) || !ql::aligned16(h_out))))
         QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
     const int64_t cpt = (k / 8 + kNormThreads - 1) / kNormThreads;   // 16-byte chunks per thread
@@ -1090,6 +1143,22 @@ extern "C" int ql_w8a8_quant_per_token(const uint16_t* x, int8_t* xq, float* x_s
                                            x_scale, m, k, stream);
 }
 
+extern "C" int ql_fp8_quant_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, uint8_t* xq,
+                                    float* x_scale, int64_t m, int64_t k, void* stream)
+{
+    ql::clear_error();
+    return launch_token_quant<kNormQuantF8>("ql_fp8_quant_rmsnorm", x, nullptr, gamma, eps, nullptr,
+                                            reinterpret_cast<int8_t*>(xq), x_scale, m, k, stream);
+}
+
+extern "C" int ql_fp8_quant_per_token(const uint16_t* x, uint8_t* xq, float* x_scale, int64_t m, int64_t k,
+                                      void* stream)
+{
+    ql::clear_error();
+    return launch_token_quant<kTokenQuantF8>("ql_fp8_quant_per_token", x, nullptr, nullptr, 0.0f, nullptr,
+                                             reinterpret_cast<int8_t*>(xq), x_scale, m, k, stream);
+}
+
 namespace {
 
 int w8a8_gemm_fp16(const char* who, const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
@@ -1125,6 +1194,31 @@ extern "C" int ql_w8a8_gemm_ex(const int8_t* xq, const float* x_scale, const int
 {
     ql::clear_error();
     return w8a8_gemm_fp16("ql_w8a8_gemm_ex", xq, x_scale, wq, w_scale, bias, residual, y, m, n, k, stream);
+}
+
+extern "C" int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
+                           const uint16_t* bias, const uint16_t* residual, uint16_t* y, int64_t m, int64_t n,
+                           int64_t k, void* stream)
+{
+    ql::clear_error();
+    const char* who = "ql_fp8_gemm";
+    if (int rc = check_gemm(xq, wq, y, m, n, k, who))
+        return rc;
+    if (k % Pipe::BK)
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld (the FP8 GEMM needs k % 64 == 0)", who, (long long)k);
+    if (m == 0 || n == 0)
+        return QL_OK;
+    if (!x_scale || !w_scale)
+        QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
+    if (!ql::aligned16(x_scale) || !ql::aligned16(w_scale) || (bias && !ql::aligned16(bias)) ||
+        (residual && !ql::aligned16(residual)))
+        QL_FAIL(QL_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", who);
+    if (!ql::lds_fits(Pipe::kLds))
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: the device lacks the LDS the FP8 GEMM needs", who);
+    launch_w8a8_gemm<false, true>(reinterpret_cast<const int8_t*>(xq), x_scale, reinterpret_cast<const int8_t*>(wq),
+                                  w_scale, EpiTerms{bias, residual}, (void*)y, m, n, k,
+                                  static_cast<hipStream_t>(stream));
+    return launch_status(who);
 }
 
 extern "C" int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc, int64_t m, int64_t n, int64_t k,
