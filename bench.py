@@ -23,7 +23,7 @@ p10 / median / p90 of 100 single launches (event pairs, cold weights).
 `extra` reports the W4A16 prefill GEMM (M=512 fused QKV) and the W8A8 layer
 (QRMSNorm + int8 GEMM, M=2048) against their rooflines, and the steps beside
 it (residual-fused QRMSNorm, per-token quantisation, the GEMM with bias and
-residual).  `reference` is a
+residual) and the layer with FP8 E4M3 codes.  `reference` is a
 plain device copy's rate, the achievable HBM bandwidth on the device.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 INT8_MFMA_PEAK_TOPS = 5000.0    # dense
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense
 DECODE_M = (1, 4, 8, 16, 32)
 GROUP = 128
 METRIC = "W4A16/W8A8 GEMM: HBM GB/s (M<=16), TFLOP/s (M>=512), % of MI355X peak"
@@ -305,6 +306,7 @@ def measure_extra(torch, ql, workloads, dev, log):
     xh, gamma, wf = workloads.smoothquant_inputs()
     s, gs, wsm = ql.smooth(xh, gamma, wf)
     wq, wsc = ql.w8a8_quant_weight(wsm)
+    wq8, wsc8 = ql.fp8_quant_weight(wsm)
     del wf, wsm
     xd = torch.from_numpy(xh).to(dev)
     gd = torch.from_numpy(gs).to(dev)
@@ -361,6 +363,26 @@ def measure_extra(torch, ql, workloads, dev, log):
     out.append({"name": "w8a8_gemm_bias_residual", "m": m, "n": nn, "k": kk, "us": round(us_e, 2),
                 "TOP/s": round(ops / (us_e * 1e-6) / 1e12, 1),
                 "frac_mfma_int8": round(ops / (us_e * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)})
+
+    # the same layer with FP8 E4M3 codes
+    del wqs, ge, ga, gp
+    log("[bench] extra: FP8 QRMSNorm + GEMM M=2048")
+    xq8 = torch.empty((m, kk), dtype=torch.uint8, device=dev)
+    ql.fp8_quant_rmsnorm(xd, gd, 1e-6, xq=xq8, x_scale=xsc)
+    g8n = capture(torch, [lambda: ql.fp8_quant_rmsnorm(xd, gd, 1e-6, xq=xq8, x_scale=xsc)] * 8)
+    us_8n = time_graph(torch, g8n, reps) * 1e3 / 8
+    nb = m * kk * 2 + kk * 2 + m * kk + m * 4
+    out.append({"name": "fp8_quant_rmsnorm", "m": m, "k": kk, "us": round(us_8n, 2),
+                "GB/s": round(nb / (us_8n * 1e-6) / 1e9, 1),
+                "frac_hbm": round(nb / (us_8n * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    w8s = [torch.from_numpy(wq8).to(dev) for _ in range(copies)]
+    w8sc = torch.from_numpy(wsc8).to(dev)
+    ql.fp8_gemm(xq8, xsc, w8s[0], w8sc, out=yy)
+    g8 = capture(torch, [(lambda w8=w8: ql.fp8_gemm(xq8, xsc, w8, w8sc, out=yy)) for w8 in w8s])
+    us_8 = time_graph(torch, g8, reps) * 1e3 / copies
+    out.append({"name": "fp8_gemm", "m": m, "n": nn, "k": kk, "us": round(us_8, 2),
+                "TFLOP/s": round(ops / (us_8 * 1e-6) / 1e12, 1),
+                "frac_mfma_fp8": round(ops / (us_8 * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)})
     return out
 
 
