@@ -230,30 +230,6 @@ __device__ __forceinline__ uint4 add_h8(uint4 a, uint4 b)
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// fp32 -> OCP FP8 E4M3 ("e4m3fn") code, nearest with ties to even, for
-// |v| <= 448 (larger magnitudes saturate to 448; the quantisers never pass
-// any).  Normal range: round the fp32 pattern to 3 fraction bits by integer
-// addition (ties to even) and rebias the exponent (127 -> 7).  Below 2^-6 the
-// codes are multiples of 2^-9: rint(|v| * 2^9) (exact scaling), where the
-// result 8 is the smallest normal code.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v)
-{
-    const uint32_t b = __builtin_bit_cast(uint32_t, v);
-    const uint32_t sgn = (b >> 24) & 0x80u;
-    const float a = fabsf(v);
-    uint32_t c;
-    if (a >= 448.0f) {
-        c = 0x7Eu;
-    } else if (a < 0x1p-6f) {
-        c = (uint32_t)rintf(a * 512.0f);
-    } else {
-        const uint32_t ab = b & 0x7FFFFFFFu;
-        const uint32_t r = (ab + 0x7FFFFu + ((ab >> 20) & 1u)) & ~0xFFFFFu;
-        c = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
-    }
-    return sgn | c;
-}
-
 // Per-token quantisers, one workgroup per token.  MODE:
 //   kNormQuant    -- QRMSNorm: y = RMSNorm(x) * gamma, then per-token int8
 //   kAddNormQuant -- h = fp16(x + residual) written to h_out (the residual
@@ -406,8 +382,6 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     auto code = [&](float yv) -> uint32_t {
         if (!(scale > 0.0f))
             return 0u;
-        if constexpr (kF8)
-            return f32_to_e4m3(__fdiv_rn(yv, scale));
         const float q0 = yv * rcp;
         float qr = rintf(q0);
         const float half = floorf(q0) + 0.5f;
@@ -415,6 +389,27 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             qr = rintf(__fdiv_rn(yv, scale));
         const int qv = (int)fminf(fmaxf(qr, -127.0f), 127.0f);
         return (uint32_t)qv & 0xFFu;
+    };
+    // FP8: fp32(y / scale), whose e4m3 cast is the code (0 for a zero scale).
+    // q0 = y * RN(1/scale) lies within 4 ulp of fp32(y / scale).  The cast
+    // rounds at the midpoints between codes: fp32 patterns with fraction bits
+    // [19:0] = 0x80000 in the normal range, half-integers of |q| * 2^9 below
+    // 2^-6.  Unless q0 lies within 4 ulp of one, both give the same code; only
+    // those take the correctly rounded division.
+    auto quot8 = [&](float yv) -> float {
+        if (!(scale > 0.0f))
+            return 0.0f;
+        const float q0 = yv * rcp;
+        const float a0 = fabsf(q0);
+        bool near;
+        if (a0 < 0x1p-6f) {
+            const float t = a0 * 512.0f;                     // ulp <= 2^-21
+            near = fabsf(t - floorf(t) - 0.5f) <= 0x1p-19f;
+        } else {
+            const int m20 = (int)(__builtin_bit_cast(uint32_t, q0) & 0xFFFFFu);
+            near = abs(m20 - 0x80000) <= 4;
+        }
+        return __builtin_expect(near, 0) ? __fdiv_rn(yv, scale) : q0;
     };
     uint2* qr = reinterpret_cast<uint2*>(xq + (int64_t)row * K);
 #pragma unroll R
@@ -431,9 +426,20 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             y_of(v, g, yo);
         }
         uint32_t packed[2] = {0u, 0u};
+        if constexpr (kF8) {
+            // e4m3 casts of two quotients per instruction (nearest, ties to
+            // even; no quotient exceeds 448 by more than rounding)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            packed[e >> 2] |= code(yo[e]) << (8 * (e & 3));
+            for (int h = 0; h < 2; ++h) {
+                uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot8(yo[4 * h]), quot8(yo[4 * h + 1]), 0, false);
+                w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot8(yo[4 * h + 2]), quot8(yo[4 * h + 3]), (int)w, true);
+                packed[h] = w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                packed[e >> 2] |= code(yo[e]) << (8 * (e & 3));
+        }
         if (c < nch)
             qr[c] = make_uint2(packed[0], packed[1]);
     }
@@ -474,18 +480,15 @@ __device__ __forceinline__ i16_t mfma_i8_32(i4_t a, i4_t b, i16_t c)
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
-// FP8 E4M3 x E4M3 -> fp32 on the same 16-byte fragments: each half (8 codes
-// per lane) is one MFMA 32x32x16.  A and B are split alike, so the two
-// instructions cover the fragment's 32 k once, in some order of k.
+// FP8 E4M3 x E4M3 -> fp32, MFMA 32x32x64 (format code 0 = E4M3 for both
+// operands, unit E8M0 block scales 127 = 2^0).  A lane's 32 codes are the two
+// 16-byte fragments of consecutive 32-byte k-steps; A and B are built alike,
+// so the instruction covers the 64 k once, in some order of k.
 typedef float f16v_t __attribute__((ext_vector_type(16)));
-__device__ __forceinline__ f16v_t mfma_f8_32(i4_t a, i4_t b, f16v_t c)
+typedef int i8v_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16v_t mfma_f8_64(i8v_t a, i8v_t b, f16v_t c)
 {
-    const long a0 = (long)(uint32_t)a[0] | ((long)(uint32_t)a[1] << 32);
-    const long a1 = (long)(uint32_t)a[2] | ((long)(uint32_t)a[3] << 32);
-    const long b0 = (long)(uint32_t)b[0] | ((long)(uint32_t)b[1] << 32);
-    const long b1 = (long)(uint32_t)b[2] | ((long)(uint32_t)b[3] << 32);
-    c = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, c, 0, 0, 0);
-    return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 __device__ __forceinline__ float acc_f(int v) { return (float)v; }
 __device__ __forceinline__ float acc_f(float v) { return v; }
@@ -895,6 +898,48 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
     for (int s = 0; s < S; ++s)
         issue(s < nk ? s : nk - 1, s);
     ql::stage_barrier<D * (S - 1)>();   // tile 0 landed
+
+    if constexpr (kF8) {
+        // FP8: one 64-k MFMA per pair of 32-byte steps.  fa8 / fb8 hold the
+        // pair's two fragments (even step in the low half); after the pair's
+        // MFMAs the next pair is read into the same registers (the next tile's
+        // first pair after the barrier and refill).
+        i8v_t fa8[FI], fb8[FJ];
+        auto read_pair = [&](int slot, int j) {
+            i4_t a0[FI], b0[FJ], a1[FI], b1[FJ];
+            read_frags(slot, j, a0, b0);
+            read_frags(slot, j + 1, a1, b1);
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+                fa8[i] = i8v_t{a0[i][0], a0[i][1], a0[i][2], a0[i][3], a1[i][0], a1[i][1], a1[i][2], a1[i][3]};
+#pragma unroll
+            for (int jj = 0; jj < FJ; ++jj)
+                fb8[jj] = i8v_t{b0[jj][0], b0[jj][1], b0[jj][2], b0[jj][3], b1[jj][0], b1[jj][1], b1[jj][2],
+                                b1[jj][3]};
+        };
+        read_pair(0, 0);
+        for (int kt = 0, slot = 0; kt < nk; ++kt) {
+            const int next = slot + 1 == S ? 0 : slot + 1;
+#pragma unroll
+            for (int j = 0; j < KS; j += 2) {
+#pragma unroll
+                for (int i = 0; i < FI; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FJ; ++jj)
+                        acc[i][jj] = mfma_f8_64(fb8[jj], fa8[i], acc[i][jj]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + 2 < KS) {
+                    read_pair(slot, j + 2);
+                } else {
+                    ql::stage_barrier<D * (S - 2)>();
+                    issue(kt + S < nk ? kt + S : nk - 1, slot);
+                    read_pair(next, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            slot = next;
+        }
+    } else {
     read_frags(0, 0, fa[0], fb[0]);
 
     // One k-tile per iteration with its KS steps unrolled and no branch
@@ -924,13 +969,11 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
             for (int i = 0; i < FI; ++i)
 #pragma unroll
                 for (int jj = 0; jj < FJ; ++jj)
-                    if constexpr (kF8)
-                        acc[i][jj] = mfma_f8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
-                    else
-                        acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
+                    acc[i][jj] = mfma_i8_32(fb[cur][jj], fa[cur][i], acc[i][jj]);
             __builtin_amdgcn_sched_barrier(0);
         }
         slot = next;
+    }
     }
     ql::stage_barrier<0>();     // drain the trailing reloads before the workgroup exits
 
@@ -1205,7 +1248,7 @@ extern "C" int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_
     if (int rc = check_gemm(xq, wq, y, m, n, k, who))
         return rc;
     if (k % Pipe::BK)
-        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld (the FP8 GEMM needs k % 64 == 0)", who, (long long)k);
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld (the FP8 GEMM needs a multiple of 64)", who, (long long)k);
     if (m == 0 || n == 0)
         return QL_OK;
     if (!x_scale || !w_scale)
