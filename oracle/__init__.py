@@ -57,6 +57,8 @@ def _load():
         "or_quant_fp8": (C.c_int, [_p, _i64, _i64, _p, C.c_float, _p, _p]),
         "or_fp8_quant_weight": (C.c_int, [_p, _i64, _i64, _p, _p]),
         "or_fp8_forward": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
+        "or_kv_quant_int8": (C.c_int, [_p, _i64, C.c_int, _p, _p]),
+        "or_kv_dequant_int8": (C.c_int, [_p, _p, _i64, C.c_int, _p]),
         "or_sumsq_exact": (None, [_p, _i64, _p, _p]),
         "or_ratio_to_f32_parts": (C.c_float, [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int]),
         "or_num_threads": (C.c_int, []),
@@ -396,6 +398,33 @@ def fp8_forward(xq, x_scale, wq, w_scale, rows=None, cols=None):
     _check(lib.or_fp8_forward(_ptr(xq), _ptr(xs), m, _ptr(wq), _ptr(ws), n, k, _ptr(r), nr, _ptr(c), nc, _ptr(y)),
            "fp8_forward")
     return y
+
+
+# ---------------------------------------------------------------- KV cache INT8
+def kv_quant_int8(x, group=128):
+    """Step 12: x fp16 [..., G-multiple] -> (q int8 same shape, scale float32 [groups])."""
+    lib = _load()
+    xb = _bits16(x)
+    if xb.size % group:
+        raise ValueError("size must be a multiple of the group")
+    groups = xb.size // group
+    q = np.empty(xb.shape, np.int8)
+    sc = np.empty(groups, np.float32)
+    _check(lib.or_kv_quant_int8(_ptr(xb), groups, int(group), _ptr(q), _ptr(sc)), "kv_quant_int8")
+    return q, sc
+
+
+def kv_dequant_int8(q, scale, group=128):
+    """Step 12, dequantisation: fp16 bits (uint16) of q * scale, q's shape."""
+    lib = _load()
+    q = _c(q, np.int8)
+    sc = _c(scale, np.float32)
+    groups = q.size // group
+    if q.size % group or sc.size != groups:
+        raise ValueError("q and scale do not match the group")
+    out = np.empty(q.shape, np.uint16)
+    _check(lib.or_kv_dequant_int8(_ptr(q), _ptr(sc), groups, int(group), _ptr(out)), "kv_dequant_int8")
+    return out
 
 
 def num_threads() -> int:

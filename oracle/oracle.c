@@ -53,6 +53,13 @@
  *        channel w_scale = max|W'| / 448, wq = e4m3(W' / w_scale).
  *    11. acc = sum_j e4m3 value of xq * e4m3 value of wq (exact products,
  *        fp64 sum), y = acc * x_scale * w_scale (fp64).
+ *
+ *   KV cache INT8 (FastLLM architecture page, section 5.2: KV cache group
+ *   quantisation between FP16 and INT8, groups of 128):
+ *    12. per group of G consecutive values (a head's vector at G = 128):
+ *        scale = max|x| / 127, q = clamp(rint(x / scale), -127, 127);
+ *        dequantisation x' = fp16(fp32(q * scale)).
+ *
  *   e4m3 (OCP FP8 E4M3, "fn": no infinities): sign, 4 exponent bits with bias
  *   7, 3 fraction bits; exponent field 0 is subnormal (fraction * 2^-9); the
  *   all-ones pattern S.1111.111 is NaN, so the largest finite value is
@@ -745,6 +752,41 @@ int or_fp8_forward(const uint8_t* xq, const float* x_scale, int64_t m, const uin
             y[a * nc + b] = (x_scale && w_scale) ? s * (double)x_scale[i] * (double)w_scale[j] : s;
         }
     }
+    return OR_OK;
+}
+
+/* Step 12: x fp16 [groups * G] -> q int8 [groups * G], scale float32 [groups]
+ * (fp32 divisions; a zero group gets scale 0 and codes 0). */
+int or_kv_quant_int8(const uint16_t* x, int64_t groups, int G, int8_t* q, float* scale)
+{
+    if (G <= 0)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < groups; ++g) {
+        const uint16_t* xg = x + g * G;
+        float amax = 0.0f;
+        for (int j = 0; j < G; ++j)
+            if (fabsf(or_f16_to_f32(xg[j])) > amax)
+                amax = fabsf(or_f16_to_f32(xg[j]));
+        const float sc = amax / 127.0f;
+        scale[g] = sc;
+        for (int j = 0; j < G; ++j)
+            q[g * G + j] = (int8_t)(sc > 0.0f ? clampi((int)rintf(or_f16_to_f32(xg[j]) / sc), -127, 127) : 0);
+    }
+    return OR_OK;
+}
+
+/* Step 12, dequantisation: out fp16 = fp16(fp32(q * scale)), the fp32
+ * product cast to binary16 (two roundings: the product of an 8-bit code and a
+ * 24-bit scale need not be exact in fp32). */
+int or_kv_dequant_int8(const int8_t* q, const float* scale, int64_t groups, int G, uint16_t* out)
+{
+    if (G <= 0)
+        return OR_BAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < groups; ++g)
+        for (int j = 0; j < G; ++j)
+            out[g * G + j] = or_f32_to_f16((float)q[g * G + j] * scale[g]);
     return OR_OK;
 }
 

@@ -606,3 +606,44 @@ def test_fp8_gemm_exact_rationals():
     ws = rng.uniform(0.01, 1, 5).astype(np.float32)
     y = oracle.fp8_forward(xq, xs, wq, ws, rows=np.array([2]), cols=np.array([4, 0]))
     assert y[0, 0] == acc[2, 4] * float(xs[2]) * float(ws[4]) and y[0, 1] == acc[2, 0] * float(xs[2]) * float(ws[0])
+
+
+# --------------------------------------------------------------------------- KV cache INT8
+def test_kv_quant_closed_forms_and_bound():
+    g = 128
+    x = np.zeros((4, g), np.float16)
+    x[0, 17] = -6.5                                          # single nonzero element
+    x[2] = np.float16(0.125)                                 # constant group
+    x[3] = np.linspace(-3, 3, g).astype(np.float16)
+    q, s = oracle.kv_quant_int8(x, g)
+    assert s[0] == np.float32(6.5) / np.float32(127) and q[0, 17] == -127 and np.count_nonzero(q[0]) == 1
+    assert s[1] == 0 and not q[1].any()
+    assert (q[2] == 127).all() and q[3, 0] == -127 and q[3, -1] == 127
+    rng = np.random.default_rng(61)
+    xr = (rng.standard_normal((64, g)) * rng.uniform(1e-3, 30, (64, 1))).astype(np.float16)
+    for group in (32, 64, 128):
+        q, s = oracle.kv_quant_int8(xr, group)
+        qs = q.reshape(-1, group).astype(np.float64)
+        err = np.abs(qs * s[:, None] - xr.reshape(-1, group).astype(np.float64))
+        assert (err <= s[:, None].astype(np.float64) * (0.5 + 1e-5)).all()
+        assert (np.abs(qs).max(axis=1) == 127).all()
+        qn, sn = oracle.kv_quant_int8(-xr, group)
+        assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+        q8, s8 = oracle.kv_quant_int8((xr.astype(np.float32) * 4).astype(np.float16), group)
+        assert np.array_equal(q8, q) and np.array_equal(s8, s * np.float32(4))
+
+
+def test_kv_dequant_is_the_fp32_product_cast():
+    """fp16(fp32(q * scale)) against NumPy's float32 product and float16 cast;
+    subnormal and large results included.  Within half an fp16 ulp (plus the
+    fp32 rounding) of the exact product."""
+    rng = np.random.default_rng(62)
+    q = rng.integers(-127, 128, size=(256, 128), dtype=np.int8)
+    s = (rng.uniform(0.5, 1.0, 256) * np.float32(2.0) ** rng.integers(-30, 9, 256)).astype(np.float32)
+    got = oracle.kv_dequant_int8(q, s, 128)
+    want = (q.astype(np.float32) * s[:, None]).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want)
+    exact = q.astype(np.float64) * s.astype(np.float64)[:, None]
+    val = got.view(np.float16).astype(np.float64)
+    ulp = np.spacing(np.abs(val).astype(np.float16)).astype(np.float64)
+    assert (np.abs(val - exact) <= ulp * (0.5 + 2.0 ** -12)).all()
