@@ -23,7 +23,8 @@ p10 / median / p90 of 100 single launches (event pairs, cold weights).
 `extra` reports the W4A16 prefill GEMM (M=512 fused QKV) and the W8A8 layer
 (QRMSNorm + int8 GEMM, M=2048) against their rooflines, and the steps beside
 it (residual-fused QRMSNorm, per-token quantisation, the GEMM with bias and
-residual) and the layer with FP8 E4M3 codes.  `reference` is a
+residual), the layer with FP8 E4M3 codes, and KV-cache INT8 group
+quantisation and dequantisation.  `reference` is a
 plain device copy's rate, the achievable HBM bandwidth on the device.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
@@ -383,6 +384,30 @@ def measure_extra(torch, ql, workloads, dev, log):
     out.append({"name": "fp8_gemm", "m": m, "n": nn, "k": kk, "us": round(us_8, 2),
                 "TFLOP/s": round(ops / (us_8 * 1e-6) / 1e12, 1),
                 "frac_mfma_fp8": round(ops / (us_8 * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4)})
+    del g8, w8s, g8n
+
+    # KV cache INT8, groups of 128: one LLaMA-7B layer's K and V for 4096
+    # tokens (2 x 4096 x 32 heads x 128), fp16 values of N(0, 1) per head
+    # scaled by U(0.1, 10)
+    log("[bench] extra: KV cache INT8")
+    kv = torch.from_numpy(
+        (rng.standard_normal((2 * 4096 * 32, 128)) * rng.uniform(0.1, 10, (2 * 4096 * 32, 1))).astype(np.float16)
+    ).to(dev)
+    groups = kv.shape[0]
+    kq = torch.empty(kv.shape, dtype=torch.int8, device=dev)
+    ksc = torch.empty((groups,), dtype=torch.float32, device=dev)
+    kout = torch.empty_like(kv)
+    ql.kv_quant_int8(kv, 128, q=kq, scale=ksc)
+    gq = capture(torch, [lambda: ql.kv_quant_int8(kv, 128, q=kq, scale=ksc)] * 8)
+    us_q = time_graph(torch, gq, reps) * 1e3 / 8
+    gd_ = capture(torch, [lambda: ql.kv_dequant_int8(kq, ksc, 128, out=kout)] * 8)
+    us_d = time_graph(torch, gd_, reps) * 1e3 / 8
+    elems = kv.numel()
+    for name, us_ in (("kv_quant_int8", us_q), ("kv_dequant_int8", us_d)):
+        nb = elems * 2 + elems + groups * 4
+        out.append({"name": name, "values": elems, "group": 128, "us": round(us_, 2),
+                    "GB/s": round(nb / (us_ * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(nb / (us_ * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
     return out
 
 

@@ -305,6 +305,31 @@ int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, cons
                 const uint16_t* bias, const uint16_t* residual, uint16_t* y,
                 int64_t m, int64_t n, int64_t k, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* KV cache INT8                                                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * ql_kv_quant_int8 (device).  KV-cache group quantisation between FP16 and
+ * INT8 (FastLLM architecture page, section 5.2: groups of 128).  Per group of
+ * `group` consecutive values (a head's vector of the K or V cache at 128):
+ *   scale[g] = max |x| / 127,  q = clamp(rint(x / scale[g]), -127, 127)
+ * (correctly rounded fp32 divisions; a zero group gets scale 0 and codes 0).
+ *   x fp16 [groups * group] (device); q int8 [groups * group], scale float32
+ *   [groups] (device, written).  group in {32, 64, 128}.  Inputs finite.
+ * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_GROUP, QL_ERR_ALIGN,
+ * QL_ERR_UNSUPPORTED, QL_ERR_HIP.
+ */
+int ql_kv_quant_int8(const uint16_t* x, int8_t* q, float* scale, int64_t groups, int group, void* stream);
+
+/*
+ * ql_kv_dequant_int8 (device).  out = fp16(fp32(q * scale[g])): the fp32
+ * product, cast to fp16 (nearest, ties to even).
+ *   q int8 [groups * group], scale float32 [groups] (device); out fp16
+ *   [groups * group] (device, written).  Errors: as ql_kv_quant_int8.
+ */
+int ql_kv_dequant_int8(const int8_t* q, const float* scale, uint16_t* out, int64_t groups, int group,
+                       void* stream);
+
 /* ql_w8a8_gemm_i32 (device).  The same int8 MFMA main loop writing the raw
  * int32 accumulator acc [m, n] instead of the fp16 epilogue. */
 int ql_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int32_t* acc,

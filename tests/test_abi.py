@@ -180,3 +180,13 @@ def test_fp8_validation():
     ws = np.zeros(2, np.float32)
     w[1, 3] = np.inf
     assert LIB.ql_fp8_quant_weight(w.ctypes.data, 2, 8, wq.ctypes.data, ws.ctypes.data) == E["QL_ERR_VALUE"]
+
+
+def test_kv_int8_validation():
+    E = CODES
+    for f in (LIB.ql_kv_quant_int8, LIB.ql_kv_dequant_int8):
+        assert f(FAKE, FAKE, FAKE, 4, 48, DEF) == E["QL_ERR_GROUP"]
+        assert f(FAKE, FAKE, FAKE, -1, 128, DEF) == E["QL_ERR_SHAPE"]
+        assert f(FAKE, None, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
+        assert f(FAKE, FAKE, MIS, 4, 128, DEF) == E["QL_ERR_ALIGN"]
+        assert f(None, None, None, 0, 128, DEF) == E["QL_OK"]

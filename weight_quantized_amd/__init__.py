@@ -44,6 +44,8 @@ EXPORTS = {
     "ql_w8a8_quant_per_token": (_i, [_p, _p, _p, _i64, _i64, _p]),
     "ql_w8a8_gemm_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "ql_w8a8_gemm_i32": (_i, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "ql_kv_quant_int8": (_i, [_p, _p, _p, _i64, _i, _p]),
+    "ql_kv_dequant_int8": (_i, [_p, _p, _p, _i64, _i, _p]),
     "ql_fp8_quant_weight": (_i, [_p, _i64, _i64, _p, _p]),
     "ql_fp8_quant_rmsnorm": (_i, [_p, _p, C.c_float, _p, _p, _i64, _i64, _p]),
     "ql_fp8_quant_per_token": (_i, [_p, _p, _p, _i64, _i64, _p]),
@@ -386,6 +388,35 @@ def fp8_gemm(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
                             bias.data_ptr() if bias is not None else None,
                             residual.data_ptr() if residual is not None else None, out.data_ptr(), m, n, k,
                             _stream(xq)))
+    return out
+
+
+def kv_quant_int8(x, group: int = 128, q=None, scale=None):
+    """KV-cache INT8 groups: (q int8, x's shape; scale float32 [x.numel() // group])."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    if x.numel() % group:
+        raise ValueError("x's size must be a multiple of the group")
+    groups = x.numel() // group
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((groups,), dtype=torch.float32, device=x.device)
+    _check(_lib.ql_kv_quant_int8(x.data_ptr(), q.data_ptr(), scale.data_ptr(), groups, int(group), _stream(x)))
+    return q, scale
+
+
+def kv_dequant_int8(q, scale, group: int = 128, out=None):
+    """fp16 values of KV-cache INT8 groups, q's shape."""
+    torch = _torch()
+    q = _dev(q, torch.int8, "q")
+    scale = _dev(scale, torch.float32, "scale")
+    if q.numel() % group or scale.numel() != q.numel() // group:
+        raise ValueError("q and scale do not match the group")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
+    _check(_lib.ql_kv_dequant_int8(q.data_ptr(), scale.data_ptr(), out.data_ptr(), q.numel() // group, int(group),
+                                   _stream(q)))
     return out
 
 

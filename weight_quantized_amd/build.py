@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libqlinear.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["w4a16.hip", "w8a8.hip"]
+HIP_SOURCES = ["w4a16.hip", "w8a8.hip", "kv_int8.hip"]
 HOST_SOURCES = ["status.cpp", "host_quant.cpp"]
 
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
