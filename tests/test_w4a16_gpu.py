@@ -183,6 +183,27 @@ def test_gemm_empty(ql):
     assert y.shape == (0, 64)
 
 
+# Single-row launches take the resident-activation decode kernel: K split into
+# slices of up to eight 256-blocks whose last block is ragged (4224 = 16 x 256
+# + 128; 4160 = 16 x 256 + 64), a ragged last column block, every group size.
+@pytest.mark.parametrize("k", [4224, 4160])
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_decode_single_row(ql, k, group):
+    if k % group:
+        pytest.skip("k must be a multiple of the group")
+    n = 1100
+    rng = np.random.default_rng(k + group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, 1, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y1 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group)
+    assert rel_err(y1.cpu().numpy(), ref) <= TOL
+
+
 def test_decode_deterministic_and_workspace_left_zero(ql):
     m, n, k, group = 16, 4096, 4096, 128
     rng = np.random.default_rng(4)

@@ -571,6 +571,316 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 }
 
 // ---------------------------------------------------------------------------
+// decode with resident activations: m <= MT (16 or 32)
+//
+// Workgroup = 4 waves; wave w owns one tile of 16 output channels, so a
+// workgroup covers 64 channels and one K slice of KS <= NB x 256.  The slice's
+// activation rows [0, m) are copied into LDS once, by direct global->LDS loads,
+// alongside the scale and zero-point tables; the weight pieces stream through
+// a register ring of P blocks per wave.  Two barriers (one after the copies,
+// one after each chunk has been reordered in place for the dequantiser) are
+// all the synchronisation: the waves then consume their blocks independently,
+// with no per-block barrier or activation staging.
+//
+// Lanes and MFMAs are laid out as in w4a16_decode_kernel (lane l: channel
+// l % 16, quarter q = l / 16; pieces [4q, 4q+4) and [16+4q, 16+4q+4) of each
+// 32-word block row; interleaved dequantisation).  Activation chunk c (16
+// bytes) of row m is stored at chunk c ^ xswz(m) within its 32-chunk block; a
+// row holds KS / 8 chunks.  Rows >= m are not stored; chunks past the slice's
+// end (a ragged last block) are zeroed in LDS.
+// ---------------------------------------------------------------------------
+// Loads the compiler does not track, for a register ring that must stay in
+// flight across the barrier that publishes LDS: a 16-byte buffer load into
+// registers, a 4-byte and a 16-byte buffer load into LDS (at M0 + 4 or 16 x
+// lane), and a wait whose register operands keep each ring entry live, and
+// unread, until its load has landed.  Reads past a buffer's end return zero.
+typedef uint32_t u4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u4v_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    u4v_t v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(r));
+    return v;
+}
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds_base)
+{
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(off), "s"(r), "{m0}"(lds_base) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void ring_wait(u4v_t& a, u4v_t& b)
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+// the same for a count known only after unrolling (even, at most 30)
+__device__ __forceinline__ void ring_wait_n(int n, u4v_t& a, u4v_t& b)
+{
+    switch (n) {
+    case 0: ring_wait<0>(a, b); break;
+    case 2: ring_wait<2>(a, b); break;
+    case 4: ring_wait<4>(a, b); break;
+    case 6: ring_wait<6>(a, b); break;
+    case 8: ring_wait<8>(a, b); break;
+    case 10: ring_wait<10>(a, b); break;
+    case 12: ring_wait<12>(a, b); break;
+    case 14: ring_wait<14>(a, b); break;
+    case 16: ring_wait<16>(a, b); break;
+    case 18: ring_wait<18>(a, b); break;
+    case 20: ring_wait<20>(a, b); break;
+    case 22: ring_wait<22>(a, b); break;
+    case 24: ring_wait<24>(a, b); break;
+    case 26: ring_wait<26>(a, b); break;
+    case 28: ring_wait<28>(a, b); break;
+    default: ring_wait<30>(a, b); break;
+    }
+}
+
+template <int MT, int NB, int P, bool POST>
+__global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
+    const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
+    uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
+{
+    static_assert(NB >= 1 && NB <= 16 && P >= 1 && P <= NB, "the ring waits cover up to 16 blocks");
+    constexpr int TW = 64;
+    constexpr int MTI = MT / 16;
+    constexpr int NJ = POST ? 1 : (MTI >= 4 ? 1 : 4 / MTI);   // accumulator chains
+    // Scale and zero-point tables of the workgroup's channels and slice, as
+    // in DecodeTables (per channel SD scale dwords from the dword holding its
+    // first group, then per channel ZD zero words), each table padded to whole
+    // 256-entry batches: a slice of up to NB blocks has at most 8 NB groups,
+    // so SB and ZB batches hold 64 (4 NB + 1) and 64 (NB + 2) entries.
+    constexpr int SB = NB + 1, ZB = (NB + 5) / 4;
+    constexpr int kZOff = SB * 256;               // first dword of the zero table
+    constexpr int kActOff = (SB + ZB) * 1024;     // byte offset of the activations
+    // a 16-byte element type aligns the dynamic region (placed after the
+    // static s_last) for the 16-byte fragment reads and direct loads
+    extern __shared__ uint4 ra_lds[];
+    uint32_t* const tab = reinterpret_cast<uint32_t*>(ra_lds);
+    __shared__ int s_last;
+
+    const int k0 = blockIdx.y * KS;
+    const int kend = min(K, k0 + KS);
+    const int nch = (kend - k0) >> 3;             // valid chunks of the slice
+    const int nb = (kend - k0 + 255) >> 8;        // blocks of this slice (<= NB)
+    const int mrows = M < MT ? M : MT;
+    const int CR = KS >> 3;                       // chunks per stored activation row
+    const int gs = KS >> lg;                      // groups per slice
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int q = lane >> 4, r16 = lane & 15;
+    const int n0 = blockIdx.x * TW;
+    const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
+    const int g0 = k0 >> lg;
+    const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)tab;
+
+    // 1. requests, oldest first, all direct to LDS except the weights: the
+    //    tables (entries clamped into the tensors, so every value is finite),
+    //    the activations, then the first P blocks of weights (blocks past the
+    //    slice re-read block nb - 1, so 2 P loads always follow the others)
+    {
+        const uint32_t sbytes = ((uint32_t)N * (uint32_t)NG * 2u + 3u) & ~3u;
+        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(sc, sbytes);
+        const __amdgpu_buffer_rsrc_t rzr = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
+        const int stot = TW * SD, ztot = TW * ZD;
+        for (int u = 0; u * 256 < stot; ++u) {
+            const int e = min(u * 256 + tid, stot - 1);
+            const int rr = e / SD, col = e - rr * SD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t dw = min(((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col, sbytes / 4u - 1u);
+            buf_dma4(rsc, dw * 4u, (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(u * 256 + wave * 64) * 4u));
+        }
+        for (int u = 0; u * 256 < ztot; ++u) {
+            const int e = min(u * 256 + tid, ztot - 1);
+            const int rr = e / ZD, col = e - rr * ZD;
+            const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
+            const uint32_t wd = min(row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col,
+                                    (uint32_t)N * (uint32_t)ZW - 1u);
+            buf_dma4(rzr, wd * 4u,
+                     (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kZOff + u * 256 + wave * 64) * 4u));
+        }
+    }
+    {
+        const int total = mrows * CR;
+        const int ninst = (total + 255) >> 8;     // direct loads per wave
+        for (int i = 0; i < ninst; ++i) {
+            const int pos = min((i * 4 + wave) * 64 + lane, total - 1);
+            const int m = pos / CR, cpos = pos - m * CR;
+            const int c = min(cpos ^ xswz(m), nch - 1);
+            const uint32_t off = (uint32_t)(m * K + k0 + 8 * c) * 2u;
+            ql::dma16s(x, off,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)kActOff +
+                                                                 (uint32_t)((i * 4 + wave) * 1024)));
+        }
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
+    const int nrow = min(n0 + wave * 16 + r16, N - 1);
+    const uint32_t ow = (uint32_t)nrow * (uint32_t)KW * 4u + (uint32_t)(k0 + 32 * q) / 2u;
+    u4v_t ring[P][2];
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+        const uint32_t bw = ow + (uint32_t)min(b, nb - 1) * 128u;
+        ring[b][0] = buf_load16(rw, bw);
+        ring[b][1] = buf_load16(rw, bw + 64u);
+    }
+    // 2. wait for everything but the weights and publish the tables and the
+    //    activations; a slice whose last block is ragged then zeroes the chunks
+    //    past its end (copied from clamped addresses) before any wave reads them
+    ql::stage_barrier<2 * P>();
+    // 3. each activation chunk, once: reorder its eight values for the
+    //    interleaved dequantiser (permute_x8), or clear it if it lies past the
+    //    slice's end (a ragged last block, copied from clamped addresses)
+    {
+        uint4* xw = ra_lds + kActOff / 16;
+        const int used = mrows * CR;
+        for (int e = tid; e < used; e += 256) {
+            const int m = e / CR, cpos = e - m * CR;
+            const int c = (cpos & ~31) + ((cpos & 31) ^ xswz(m));   // logical chunk stored here
+            xw[e] = c < nch ? ql::permute_x8(xw[e]) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+    }
+
+    // 4. the slice's blocks, in arrival order
+    const uint4* xs = ra_lds + kActOff / 16;
+    // Rows >= m read row m - 1: an MFMA output row depends on its own A row
+    // only, and output rows >= m are never stored.
+    int arow[MTI][4], hoff[MTI];
+#pragma unroll
+    for (int i = 0; i < MTI; ++i) {
+        const int m = i * 16 + r16;
+        const int mm = m < mrows ? m : mrows - 1;
+        const int f = xswz(mm);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            arow[i][jj] = mm * CR + ((4 * q + jj) ^ (f & 15)) + (f & 16);
+        hoff[i] = (f & 16) ? -16 : 16;
+    }
+    const int glane = (32 * q) >> lg;
+    const int gmax = gs - 1;
+    const int trow = wave * 16 + r16;
+    const int spar = (int)(((uint32_t)min(n0 + trow, N - 1) * (uint32_t)NG + (uint32_t)g0) & 1u);
+    const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + trow * SD);
+    const uint32_t* zrow = tab + kZOff + trow * ZD;
+    f4_t acc[MTI][NJ];
+#pragma unroll
+    for (int i = 0; i < MTI; ++i)
+#pragma unroll
+        for (int c = 0; c < NJ; ++c)
+            acc[i][c] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        constexpr int kLast = NB - 1;
+        u4v_t(&rs)[2] = ring[b % P];
+        ring_wait_n(2 * ((b + P - 1 <= kLast ? b + P - 1 : kLast) - b), rs[0], rs[1]);
+        if (b >= nb) {
+            if (b + P < NB) {
+                const uint32_t bw = ow + (uint32_t)(nb - 1) * 128u;
+                rs[0] = buf_load16(rw, bw);
+                rs[1] = buf_load16(rw, bw + 64u);
+            }
+            continue;
+        }
+        uint4 af[8][MTI];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < MTI; ++i)
+                af[j][i] = xs[32 * b + arow[i][j & 3] + (j >> 2) * hoff[i]];
+        const int ga = min(((256 * b) >> lg) + glane, gmax);
+        const int gb = min(((256 * b + 128) >> lg) + glane, gmax);
+        const uint32_t za_ = (zrow[((g0 + ga) >> 3) - (g0 >> 3)] >> (4 * ((g0 + ga) & 7))) & 0xFu;
+        const uint32_t zb_ = (zrow[((g0 + gb) >> 3) - (g0 >> 3)] >> (4 * ((g0 + gb) & 7))) & 0xFu;
+        const uint32_t s16a = srow[spar + ga], s16b = srow[spar + gb];
+        const ql::zb_t za = ql::make_zb(za_), zc = ql::make_zb(zb_);
+        const u4v_t w0 = rs[0], w1 = rs[1];
+        const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        // the slot's next block, once its words are read
+        if (b + P < NB) {
+            const uint32_t bw = ow + (uint32_t)min(b + P, nb - 1) * 128u;
+            rs[0] = buf_load16(rw, bw);
+            rs[1] = buf_load16(rw, bw + 64u);
+        }
+        ql::zb_t zb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            zb[j] = j < 4 ? za : zc;
+        h8_t bw[8];
+        if constexpr (POST) {
+            h2_t d[8][4];
+            ql::dequant_words_qz<8>(words, zb, d);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                bw[j] = __builtin_bit_cast(h8_t, make_uint4(ql::h2u(d[j][0]), ql::h2u(d[j][1]), ql::h2u(d[j][2]),
+                                                            ql::h2u(d[j][3])));
+            const float sa = f16_bits_to_f32(s16a), sb = f16_bits_to_f32(s16b);
+#pragma unroll
+            for (int i = 0; i < MTI; ++i) {
+                f4_t da = f4_t{0.f, 0.f, 0.f, 0.f}, db = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    da = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[j], da);
+                    db = mfma16x16x32(__builtin_bit_cast(h8_t, af[4 + j][i]), bw[4 + j], db);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][0][r] = __builtin_fmaf(sb, db[r], __builtin_fmaf(sa, da[r], acc[i][0][r]));
+            }
+        } else {
+            h2_t s2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                s2[j] = ql::scale2(j < 4 ? s16a : s16b);
+            ql::dequant_words<8>(words, zb, s2, bw);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < MTI; ++i)
+                    acc[i][j % NJ] = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[j], acc[i][j % NJ]);
+        }
+    }
+    f4_t res[MTI];
+#pragma unroll
+    for (int i = 0; i < MTI; ++i) {
+        if constexpr (NJ == 4)
+            res[i] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+        else if constexpr (NJ == 2)
+            res[i] = acc[i][0] + acc[i][1];
+        else
+            res[i] = acc[i][0];
+    }
+
+    const int S = gridDim.y;
+    const int ncol = n0 + wave * 16 + r16;
+    if (S == 1) {
+#pragma unroll
+        for (int i = 0; i < MTI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = i * 16 + 4 * q + r;
+                if (m < M && ncol < N)
+                    y[(int64_t)m * N + ncol] = f32_to_f16_bits(res[i][r]);
+            }
+        return;
+    }
+    // 5. split-K: this slice's partial tile with agent-scope stores, then the
+    //    arrival and the last arrival's reduction
+    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)M * TW;
+#pragma unroll
+    for (int i = 0; i < MTI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = i * 16 + 4 * q + r;
+            if (m < M)
+                __hip_atomic_store(&tile[m * TW + wave * 16 + r16], res[i][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    splitk_finish<TW>(part, cnt, y, M, N, n0, &s_last);
+}
+
+// ---------------------------------------------------------------------------
 // GEMM (m > 32): block tile BM x BN, K advanced in tiles of 64, 4 waves as
 // 2 x 2 (wave tile BM/2 x BN/2), MFMA f32 16x16x32 f16.
 //
@@ -1059,14 +1369,16 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 // host side
 // ---------------------------------------------------------------------------
 struct DecodePlan {
+    bool ra;    // resident-activation kernel (else the streamed one)
     int mt;     // 16 or 32
     int r;      // 16-channel tiles per wave (the workgroup has 4 waves)
-    int p;      // blocks in flight per wave
+    int p;      // blocks in flight per wave (resident kernel: most blocks per slice)
     bool post;  // group scale applied to the fp32 MFMA result (128-channel groups)
     int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
     size_t lds_bytes;   // dynamic LDS bytes
+    size_t act_off;     // resident kernel: byte offset of the activations in LDS
     size_t part_offset, part_bytes;
 };
 
@@ -1112,6 +1424,56 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     return p;
 }
 
+// Resident-activation plan (single-row launches): a slice holds at most
+// kRaBlocks blocks of 256 k and at most kRaActBytes of activation rows;
+// kRaRing blocks of weights are in flight per wave.  Measured on the LLaMA-7B
+// MLP decode shapes (G = 128): at m = 1 it beats the streamed kernel (fused
+// gate/up 13.6 against 15.5 us, down 10.4 against 10.6 us); from m = 4 on the
+// streamed kernel is as fast or faster (it splits K less and stages smaller
+// activation slices), so only m = 1 takes this path.
+constexpr int kRaBlocks = 8, kRaRing = 2;
+constexpr int64_t kRaActBytes = 65536;
+constexpr int64_t kRaMaxM = 1;
+
+DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
+{
+    DecodePlan p{};
+    p.ra = true;
+    p.mt = 16;
+    p.r = 1;
+    p.p = kRaBlocks;
+    p.post = group == 128;
+    p.nblk = (int)((n + 63) / 64);
+    const int64_t kblocks = (k + 255) / 256;
+    const int64_t mrows = std::min<int64_t>(m, p.mt);
+    int64_t sblocks = std::min<int64_t>(std::min<int64_t>(p.p, std::max<int64_t>(1, kRaActBytes / (mrows * 512))),
+                                        kblocks);
+    const int64_t slices = (kblocks + sblocks - 1) / sblocks;
+    sblocks = (kblocks + slices - 1) / slices;
+    p.ks = (int)(sblocks * 256);
+    p.slices = (int)((k + p.ks - 1) / p.ks);
+    // tables padded to whole batches (see the kernel), then the activation rows
+    // in whole 4 KiB rounds of direct loads
+    const size_t tables = (size_t)((p.p + 1) + (p.p + 5) / 4) * 1024;
+    const size_t act = (size_t)((mrows * sblocks * 32 + 255) / 256) * 4096;
+    p.act_off = tables;
+    p.lds_bytes = tables + act;
+    p.part_offset = kCounterBytes;
+    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * 64 * sizeof(float) : 0;
+    return p;
+}
+
+// Kernel choice by m (measured on the MLP decode shapes).
+DecodePlan decode_plan_auto(int64_t m, int64_t n, int64_t k, int group)
+{
+    if (m <= kRaMaxM) {
+        DecodePlan p = decode_plan_ra(m, n, k, group);
+        if (ql::lds_fits(p.lds_bytes))
+            return p;
+    }
+    return decode_plan(m, n, k, group);
+}
+
 size_t decode_workspace(const DecodePlan& p) { return p.slices > 1 ? p.part_offset + p.part_bytes : 0; }
 
 int check_common(const void* qweight, const void* scales, const void* qzeros, int64_t n, int64_t k, int group,
@@ -1151,9 +1513,32 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
 
 // Exact dispatch on the plan; returns false for a combination that is not
 // instantiated.
+template <int MT, int NB, int P, bool POST>
+void launch_decode_ra_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
+                        const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
+{
+    uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
+    float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
+    hipLaunchKernelGGL((w4a16_decode_ra_kernel<MT, NB, P, POST>), dim3(p.nblk, p.slices), dim3(256), p.lds_bytes, st,
+                       x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+}
+
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                    const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
+    if (p.ra) {
+#define QL_DECODE_RA_CASE(MT_, NB_, P_)                                                          \
+    if (p.mt == MT_ && p.p == NB_) {                                                             \
+        if (p.post)                                                                              \
+            launch_decode_ra_t<MT_, NB_, P_, true>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
+        else                                                                                     \
+            launch_decode_ra_t<MT_, NB_, P_, false>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
+        return true;                                                                             \
+    }
+        QL_DECODE_RA_CASE(16, kRaBlocks, kRaRing)
+#undef QL_DECODE_RA_CASE
+        return false;
+    }
 
 #define QL_DECODE_CASE(MT_, R_, P_)                                                          \
     if (p.mt == MT_ && p.r == R_ && p.p == P_) {                                             \
@@ -1175,7 +1560,7 @@ extern "C" size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int 
     (void)group;
     if (m <= 0 || n <= 0 || k <= 0 || m > 32)
         return 0;
-    return decode_workspace(decode_plan(m, n, k, group));
+    return decode_workspace(decode_plan_auto(m, n, k, group));
 }
 
 extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
@@ -1209,7 +1594,7 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     const int mi = (int)m, ni = (int)n, ki = (int)k;
 
     if (path == QL_PATH_DECODE) {
-        DecodePlan p = decode_plan(m, n, k, group);
+        DecodePlan p = decode_plan_auto(m, n, k, group);
         if (p.slices > 1 && p.nblk > kMaxDecodeBlocks)
             QL_FAIL(QL_ERR_UNSUPPORTED, "%s: n=%lld exceeds the decode path's %d column blocks", who, (long long)n,
                     kMaxDecodeBlocks);
