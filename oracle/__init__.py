@@ -59,6 +59,9 @@ def _load():
         "or_fp8_forward": (C.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i64, _p, _i64, _p]),
         "or_kv_quant_int8": (C.c_int, [_p, _i64, C.c_int, _p, _p]),
         "or_kv_dequant_int8": (C.c_int, [_p, _p, _i64, C.c_int, _p]),
+        "or_f64_to_f16": (C.c_uint16, [C.c_double]),
+        "or_awq_scales": (None, [_p, _p, _i64, C.c_double, _p]),
+        "or_awq_search": (C.c_int, [_p, _i64, _p, _i64, _i64, C.c_int, C.c_int, C.c_int, _p, _p, _p]),
         "or_sumsq_exact": (None, [_p, _i64, _p, _p]),
         "or_ratio_to_f32_parts": (C.c_float, [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int]),
         "or_num_threads": (C.c_int, []),
@@ -425,6 +428,38 @@ def kv_dequant_int8(q, scale, group=128):
     out = np.empty(q.shape, np.uint16)
     _check(lib.or_kv_dequant_int8(_ptr(q), _ptr(sc), groups, int(group), _ptr(out)), "kv_dequant_int8")
     return out
+
+
+# ---------------------------------------------------------------- AWQ scale search
+def f64_to_f16(v):
+    """binary16 bits of a float64 value, rounded once to nearest even."""
+    return int(_load().or_f64_to_f16(float(v)))
+
+
+def awq_scales(a, b, alpha):
+    """Step 14's smoothing vector s float32 [k] from the column maxima a, b."""
+    lib = _load()
+    a = _c(a, np.float32)
+    b = _c(b, np.float32)
+    s = np.empty(a.size, np.float32)
+    lib.or_awq_scales(_ptr(a), _ptr(b), a.size, float(alpha), _ptr(s))
+    return s
+
+
+def awq_search(x, w, group, grid=20, quant=True):
+    """Steps 13-15: (err float64 [grid], best int, s_best float32 [k]) for
+    calibration tokens x (fp16 [t, k]) and weights w (float32 [n, k])."""
+    lib = _load()
+    x = _bits16(x)
+    w = _c(w, np.float32)
+    t, k = x.shape
+    n = w.shape[0]
+    err = np.empty(int(grid), np.float64)
+    best = np.zeros(1, np.int32)
+    s = np.empty(k, np.float32)
+    _check(lib.or_awq_search(_ptr(x), t, _ptr(w), n, k, int(group), int(grid), int(bool(quant)), _ptr(err),
+                             _ptr(best), _ptr(s)), "awq_search")
+    return err, int(best[0]), s
 
 
 def num_threads() -> int:

@@ -66,6 +66,22 @@
  *   1.75 * 2^8 = 448.  The cast rounds to nearest, ties to even; magnitudes
  *   above 464 (halfway to the next step) become NaN.
  *
+ *   AWQ scale search (LMDeploy walkthrough, section 2: AWQ samples typical
+ *   inputs and picks the scales that minimise the error of the product with
+ *   those activations, not of the weights; LMDeploy W8A8 guide, source
+ *   analysis of the smoothing: coefficient act_scales^alpha /
+ *   w_scales^(1 - alpha), with per-layer ratios found in calibration
+ *   replacing the fixed alpha when the scale search is on):
+ *    13. a_j = max_t |x[t,j]| over the calibration tokens, b_j = max_r |w[r,j]|.
+ *    14. for alpha = i / grid, i = 0 .. grid-1:
+ *        s_j = exp(alpha ln a_j - (1 - alpha) ln b_j) in fp64, rounded to
+ *        fp32 (s_j = 1 where a_j or b_j is zero); W' = W diag(s) (fp32),
+ *        quantised and dequantised to fp16 by steps 1-4 and 7;
+ *        x' = fp16(fp32(x) / s_j);  y = fp16 of the fp64 sum x' wd16^T
+ *        (the precision the device GEMM delivers its output in);
+ *        err_i = sum over (t, r) of (y - yref)^2, yref = x W^T in fp64.
+ *    15. the chosen ratio is the first i with the smallest err_i.
+ *
  * Rounding: rintf under the default environment (nearest, ties to even).
  * Built with -ffp-contract=off so every fp32 operation rounds on its own.
  */
@@ -178,6 +194,33 @@ uint16_t or_f32_to_f16(float x)
     float m = rintf(ldexpf(a, 10 - ex));   /* significand in [1024, 2048] */
     if (m == 2048.0f) {
         m = 1024.0f;
+        ex += 1;
+    }
+    if (ex + 15 >= 31)
+        return sign | 0x7c00;
+    return sign | (uint16_t)(((ex + 15) << 10) | ((int)m - 1024));
+}
+
+/* the same rounding from a binary64 value (scaling by powers of two is exact,
+ * so the one rint is the only rounding) */
+uint16_t or_f64_to_f16(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7e00;
+    if (a >= 65520.0)
+        return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        double m = rint(ldexp(a, 24));
+        return sign | (uint16_t)m;
+    }
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;
+    double m = rint(ldexp(a, 10 - ex));
+    if (m == 2048.0) {
+        m = 1024.0;
         ex += 1;
     }
     if (ex + 15 >= 31)
@@ -806,4 +849,99 @@ float or_ratio_to_f32_parts(uint64_t num_hi, uint64_t num_lo, uint64_t den, int 
 {
     unsigned __int128 num = ((unsigned __int128)num_hi << 64) | num_lo;
     return or_ratio_to_f32(num, den, e2);
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* AWQ scale search                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Step 14's smoothing vector for one ratio. */
+void or_awq_scales(const float* a, const float* b, int64_t k, double alpha, float* s)
+{
+    for (int64_t j = 0; j < k; ++j)
+        s[j] = (a[j] == 0.0f || b[j] == 0.0f)
+                   ? 1.0f
+                   : (float)exp(alpha * log((double)a[j]) - (1.0 - alpha) * log((double)b[j]));
+}
+
+/*
+ * Steps 13-15.  x fp16 [t, k] (calibration tokens), w float32 [n, k].  Outputs:
+ * err float64 [grid], *best, s_best float32 [k] (the smoothing vector of the
+ * chosen ratio).  quant = 0 replaces the int4 round trip of W' by its plain
+ * fp16 rounding (a lossless stand-in the tests use).
+ */
+int or_awq_search(const uint16_t* x, int64_t t, const float* w, int64_t n, int64_t k, int G, int grid, int quant,
+                  double* err, int* best, float* s_best)
+{
+    if (t <= 0 || n <= 0 || k <= 0 || G <= 0 || k % G || grid <= 0)
+        return OR_BAD;
+    const int64_t ng = k / G;
+    float* a = (float*)calloc((size_t)k, sizeof(float));
+    float* b = (float*)calloc((size_t)k, sizeof(float));
+    float* s = (float*)malloc((size_t)k * sizeof(float));
+    float* ws = (float*)malloc((size_t)(n * k) * sizeof(float));
+    uint8_t* q = (uint8_t*)malloc((size_t)(n * k));
+    uint8_t* z = (uint8_t*)malloc((size_t)(n * ng));
+    uint16_t* sc = (uint16_t*)malloc((size_t)(n * ng) * sizeof(uint16_t));
+    uint16_t* wd16 = (uint16_t*)malloc((size_t)(n * k) * sizeof(uint16_t));
+    uint16_t* xs = (uint16_t*)malloc((size_t)(t * k) * sizeof(uint16_t));
+    double* yref = (double*)malloc((size_t)(t * n) * sizeof(double));
+    if (!a || !b || !s || !ws || !q || !z || !sc || !wd16 || !xs || !yref) {
+        free(a); free(b); free(s); free(ws); free(q); free(z); free(sc); free(wd16); free(xs); free(yref);
+        return OR_BAD;
+    }
+    for (int64_t j = 0; j < k; ++j) {
+        for (int64_t i = 0; i < t; ++i) {
+            float v = fabsf(or_f16_to_f32(x[i * k + j]));
+            if (v > a[j]) a[j] = v;
+        }
+        for (int64_t r = 0; r < n; ++r) {
+            float v = fabsf(w[r * k + j]);
+            if (v > b[j]) b[j] = v;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t i = 0; i < t; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j)
+                acc += (double)or_f16_to_f32(x[i * k + j]) * (double)w[r * k + j];
+            yref[i * n + r] = acc;
+        }
+    int bi = 0;
+    for (int g = 0; g < grid; ++g) {
+        or_awq_scales(a, b, k, (double)g / (double)grid, s);
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t j = 0; j < k; ++j)
+                ws[r * k + j] = w[r * k + j] * s[j];
+        if (quant) {
+            or_awq_quantize(ws, n, k, G, q, z, sc);
+            or_awq_dequant(q, z, sc, n, k, G, NULL, wd16);
+        } else {
+            for (int64_t e = 0; e < n * k; ++e)
+                wd16[e] = or_f32_to_f16(ws[e]);
+        }
+        for (int64_t i = 0; i < t; ++i)
+            for (int64_t j = 0; j < k; ++j)
+                xs[i * k + j] = or_f32_to_f16(or_f16_to_f32(x[i * k + j]) / s[j]);
+        double e2 = 0.0;
+#pragma omp parallel for schedule(static) reduction(+ : e2)
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t i = 0; i < t; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < k; ++j)
+                    acc += (double)or_f16_to_f32(xs[i * k + j]) * (double)or_f16_to_f32(wd16[r * k + j]);
+                double d = (double)or_f16_to_f32(or_f64_to_f16(acc)) - yref[i * n + r];
+                e2 += d * d;
+            }
+        err[g] = e2;
+        if (e2 < err[bi])
+            bi = g;
+    }
+    or_awq_scales(a, b, k, (double)bi / (double)grid, s_best);
+    *best = bi;
+    free(a); free(b); free(s); free(ws); free(q); free(z); free(sc); free(wd16); free(xs); free(yref);
+    return OR_OK;
 }

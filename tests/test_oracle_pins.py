@@ -647,3 +647,95 @@ def test_kv_dequant_is_the_fp32_product_cast():
     val = got.view(np.float16).astype(np.float64)
     ulp = np.spacing(np.abs(val).astype(np.float16)).astype(np.float64)
     assert (np.abs(val - exact) <= ulp * (0.5 + 2.0 ** -12)).all()
+
+
+# --------------------------------------------------------------------------- AWQ scale search
+def test_f64_to_f16_rounds_once():
+    """binary64 -> binary16 against NumPy's direct conversion (which rounds
+    the double once), on random magnitudes across the range and on exact
+    midpoints between neighbouring binary16 values (ties go to even)."""
+    rng = np.random.default_rng(70)
+    v = rng.standard_normal(4000) * 2.0 ** rng.integers(-26, 17, 4000)
+    h = np.arange(0, 0x7BFF, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (h[:-1] + h[1:]) / 2
+    for vals in (v, mids, -mids[::97]):
+        got = np.array([oracle.f64_to_f16(a) for a in vals], np.uint16)
+        assert np.array_equal(got, vals.astype(np.float16).view(np.uint16))
+
+
+def test_awq_scales_closed_forms():
+    """act^alpha / w^(1 - alpha) at the ends and the middle of the grid: 1/b,
+    sqrt(a/b) and a, within 2 ulp (the fp64 exp/log route rounds once to
+    fp32); columns with a zero maximum keep s = 1."""
+    rng = np.random.default_rng(71)
+    a = (rng.uniform(0.01, 3000.0, 512)).astype(np.float32)
+    b = (rng.uniform(1e-4, 0.5, 512)).astype(np.float32)
+    a[:3] = [0.0, 5.0, 0.0]
+    b[:3] = [0.2, 0.0, 0.0]
+
+    def close(x, y):
+        return np.all(np.abs(x.astype(np.float64) - y) <= 2 * np.spacing(np.float32(y)).astype(np.float64))
+
+    with np.errstate(divide="ignore", invalid="ignore"):
+        forms = ((0.0, 1.0 / b.astype(np.float64)), (0.5, np.sqrt(a.astype(np.float64) / b)),
+                 (1.0, a.astype(np.float64)))
+    for alpha, want in forms:
+        s = oracle.awq_scales(a, b, alpha)
+        assert (s[:3] == 1.0).all()
+        assert close(s[3:], want[3:])
+
+
+def _awq_brute(x, w, group, grid):
+    """The search re-derived with NumPy for a tiny case: column maxima,
+    x' = fp16(fp32(x) / s), an fp64 matmul rounded once to fp16, squared
+    error against the fp64 product of the original operands."""
+    xf = x.astype(np.float32)
+    a = np.abs(xf).max(axis=0)
+    b = np.abs(w).max(axis=0)
+    yref = xf.astype(np.float64) @ w.astype(np.float64).T
+    errs = []
+    for i in range(grid):
+        s = oracle.awq_scales(a, b, i / grid)
+        q, z, sc = oracle.awq_quantize(w * s[None, :], group)
+        _, wd16 = oracle.awq_dequant(q, z, sc, group)
+        xs = (xf / s[None, :]).astype(np.float16).astype(np.float64)
+        y = (xs @ wd16.astype(np.float64).T).astype(np.float16).astype(np.float64)
+        errs.append(float(((y - yref) ** 2).sum()))
+    return np.array(errs)
+
+
+def test_awq_search_brute_force():
+    rng = np.random.default_rng(72)
+    for t, n, k, group, grid in ((2, 3, 64, 32, 4), (3, 5, 128, 64, 6), (4, 2, 256, 128, 5)):
+        x = rng.standard_normal((t, k)).astype(np.float32)
+        x[:, rng.choice(k, 2, replace=False)] *= 25
+        x = x.astype(np.float16)
+        w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+        err, best, s = oracle.awq_search(x, w, group, grid)
+        want = _awq_brute(x, w, group, grid)
+        assert np.allclose(err, want, rtol=1e-9, atol=0)
+        assert best == int(np.argmin(want))
+        a = np.abs(x.astype(np.float32)).max(axis=0)
+        b = np.abs(w).max(axis=0)
+        assert np.array_equal(s, oracle.awq_scales(a, b, best / grid))
+
+
+def test_awq_search_lossless_round_trip():
+    """Without the int4 round trip, (x / s) (W diag(s))^T reproduces x W^T for
+    every ratio up to the fp16 roundings of x', W' and y (a scaling applied
+    in the wrong direction, or to the wrong axis, fails by orders of
+    magnitude); the int4 search's errors are far above that floor and its
+    choice is the smallest of them."""
+    rng = np.random.default_rng(73)
+    t, n, k, group = 16, 64, 256, 64
+    x = rng.standard_normal((t, k)).astype(np.float32)
+    x[:, rng.choice(k, 3, replace=False)] *= 30
+    x = x.astype(np.float16)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    yref = x.astype(np.float64) @ w.astype(np.float64).T
+    total = float((yref ** 2).sum())
+    err0, _, _ = oracle.awq_search(x, w, group, 10, quant=False)
+    assert (err0 / total <= 1e-5).all()
+    err, best, _ = oracle.awq_search(x, w, group, 10)
+    assert (err / total >= 1e-4).all()
+    assert err[best] == err.min() and best == int(np.argmin(err))
