@@ -408,6 +408,18 @@ def measure_extra(torch, ql, workloads, dev, log):
         out.append({"name": name, "values": elems, "group": 128, "us": round(us_, 2),
                     "GB/s": round(nb / (us_ * 1e-6) / 1e9, 1),
                     "frac_hbm": round(nb / (us_ * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+
+    # AWQ ratio search, offline: q_proj weights, 128 calibration tokens of the
+    # prefill recipe, 20 ratios; host grid, one device GEMM per candidate
+    log("[bench] extra: AWQ ratio search (q_proj, 128 tokens, 20 ratios)")
+    wq_ = workloads.config_weight("q_proj")
+    xc = workloads.config_activations("qkv", 128, wq_.shape[1])
+    t0 = time.perf_counter()
+    err, best, _, _ = ql.awq_search(xc, wq_, 128, 20)
+    secs = time.perf_counter() - t0
+    out.append({"name": "awq_search", "t": 128, "n": int(wq_.shape[0]), "k": int(wq_.shape[1]), "group": 128,
+                "grid": 20, "s": round(secs, 3), "best_ratio": best / 20,
+                "err_vs_ratio_0.5": round(float(err[best] / err[10]), 4)})
     return out
 
 

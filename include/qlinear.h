@@ -140,6 +140,46 @@ int ql_w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32
                      uint16_t* w16, uint8_t* q_u8, int64_t n, int64_t k, int group,
                      void* stream);
 
+/*
+ * ql_awq_search (host, using the device).  Activation-aware choice of the
+ * per-input-channel smoothing applied before the int4 quantisation: AWQ
+ * picks the scales from sampled activations so that the product's error, not
+ * the weights', is smallest (LMDeploy walkthrough, section 2), and the
+ * smoothing coefficient is act_scales^alpha / w_scales^(1 - alpha) with the
+ * ratio alpha searched per layer in calibration (LMDeploy W8A8 guide, source
+ * analysis of the smoothing).  With a_j = max_t |x[t, j]|, b_j = max_r |w[r, j]|,
+ * for alpha = i / grid, i = 0 .. grid-1:
+ *   s_j  = exp(alpha ln a_j - (1 - alpha) ln b_j) in fp64, rounded to fp32
+ *          (1 where a_j or b_j is 0)
+ *   W'   = W diag(s), packed by ql_awq_pack;  x' = fp16(fp32(x) / s)
+ *   y    = ql_w4a16_gemm(x', W') on the device (fp16)
+ *   err_i = sum over (t, r) of (y - x w^T)^2, the reference in fp64
+ * and the chosen ratio is the first i with the smallest err_i.
+ *   x        fp16 [t, k] calibration tokens          (host)
+ *   w        float32 [n, k]                          (host)
+ *   grid     number of ratios, 1 .. 1000
+ *   workspace, workspace_bytes   device scratch of at least
+ *            ql_awq_search_workspace_bytes(t, n, k, group) bytes, 16-byte
+ *            aligned, zero-filled before its first use (it holds the GEMM's
+ *            split-K counters, which every call leaves zero)
+ *   stream   hipStream_t (NULL = default); the call synchronises it
+ *   err      float64 [grid]    (host, written)
+ *   best     chosen index      (host, written)
+ *   s_best   float32 [k]       (host, written): the chosen smoothing vector;
+ *            the layer then computes (x / s_best) W'^T
+ *   qweight, scales, qzeros   (host, written; all NULL to skip): the chosen
+ *            W' packed as by ql_awq_pack
+ * Errors: QL_ERR_NULL, QL_ERR_GROUP, QL_ERR_SHAPE (t, n, k <= 0, k % group,
+ * grid out of range), QL_ERR_UNSUPPORTED (t*k or t*n >= 2^30, n*k >= 2^32),
+ * QL_ERR_WORKSPACE, QL_ERR_ALIGN, QL_ERR_VALUE (non-finite weight, or a
+ * smoothed group whose scale leaves fp16), QL_ERR_HIP, and those of
+ * ql_w4a16_gemm.
+ */
+size_t ql_awq_search_workspace_bytes(int64_t t, int64_t n, int64_t k, int group);
+int ql_awq_search(const uint16_t* x, int64_t t, const float* w, int64_t n, int64_t k, int group, int grid,
+                  void* workspace, size_t workspace_bytes, void* stream, double* err, int* best,
+                  float* s_best, int32_t* qweight, uint16_t* scales, int32_t* qzeros);
+
 /* ------------------------------------------------------------------------ */
 /* W8A8 (SmoothQuant)                                                        */
 /* ------------------------------------------------------------------------ */

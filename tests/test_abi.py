@@ -190,3 +190,33 @@ def test_kv_int8_validation():
         assert f(FAKE, None, FAKE, 4, 128, DEF) == E["QL_ERR_NULL"]
         assert f(FAKE, FAKE, MIS, 4, 128, DEF) == E["QL_ERR_ALIGN"]
         assert f(None, None, None, 0, 128, DEF) == E["QL_OK"]
+
+
+def test_awq_search_validation():
+    E = CODES
+    f = LIB.ql_awq_search
+    t, n, k, g = 4, 64, 256, 64
+    need = LIB.ql_awq_search_workspace_bytes(t, n, k, g)
+    assert need > 0
+    assert LIB.ql_awq_search_workspace_bytes(t, n, 100, g) == 0
+    assert LIB.ql_awq_search_workspace_bytes(0, n, k, g) == 0
+    assert LIB.ql_awq_search_workspace_bytes(t, n, k, 48) == 0
+    err = np.zeros(8)
+    best = np.zeros(1, np.int32)
+    s = np.zeros(k, np.float32)
+    P = (err.ctypes.data, best.ctypes.data, s.ctypes.data, None, None, None)
+
+    def call(x=FAKE, tt=t, w=FAKE, nn=n, kk=k, gg=g, grid=8, ws=FAKE, wsb=need, tail=P):
+        return f(x, tt, w, nn, kk, gg, grid, ws, wsb, DEF, *tail)
+
+    assert call(x=None) == E["QL_ERR_NULL"]
+    assert call(ws=None) == E["QL_ERR_NULL"]
+    assert call(tail=(None,) + P[1:]) == E["QL_ERR_NULL"]
+    assert call(gg=48) == E["QL_ERR_GROUP"]
+    assert call(kk=100) == E["QL_ERR_SHAPE"]
+    assert call(tt=0) == E["QL_ERR_SHAPE"]
+    assert call(grid=0) == E["QL_ERR_SHAPE"]
+    assert call(grid=1001) == E["QL_ERR_SHAPE"]
+    assert call(tt=1 << 20, kk=4096) == E["QL_ERR_UNSUPPORTED"]
+    assert call(wsb=need - 1) == E["QL_ERR_WORKSPACE"]
+    assert call(ws=MIS) == E["QL_ERR_ALIGN"]

@@ -32,6 +32,8 @@ _p, _i64, _sz, _i = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
 # name -> (restype, argtypes); mirrors include/qlinear.h
 EXPORTS = {
     "ql_awq_pack": (_i, [_p, _i64, _i64, _i, _p, _p, _p]),
+    "ql_awq_search_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
+    "ql_awq_search": (_i, [_p, _i64, _p, _i64, _i64, _i, _i, _p, _sz, _p, _p, _p, _p, _p, _p, _p]),
     "ql_w4a16_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
     "ql_w4a16_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p]),
     "ql_w4a16_gemm_path": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p, _i]),
@@ -120,6 +122,40 @@ def awq_pack(w, group: int):
     qz = np.empty((n, (k // g + 7) // 8), np.int32)
     _check(_lib.ql_awq_pack(w.ctypes.data, n, k, int(group), qw.ctypes.data, sc.ctypes.data, qz.ctypes.data))
     return qw, sc.view(np.float16), qz
+
+
+def awq_search(x, w, group: int, grid: int = 20, device=None):
+    """AWQ ratio search over calibration tokens x (fp16 [t, k], host) for
+    weights w (float32 [n, k], host), each candidate scored with the device
+    GEMM.  Returns (err float64 [grid], best int, s float32 [k],
+    (qweight, scales, qzeros) of the chosen smoothed weights)."""
+    torch = _torch()
+    x = _f16_bits(x)
+    w = _np(w, np.float32)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x [t, k] and w [n, k] must share k")
+    t, k = x.shape
+    n = w.shape[0]
+    g = max(int(group), 1)
+    dev = torch.device("cuda:0") if device is None else torch.device(device)
+    need = awq_search_workspace_bytes(t, n, k, group)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    err = np.empty(max(int(grid), 1), np.float64)
+    best = np.zeros(1, np.int32)
+    s = np.empty(k, np.float32)
+    qw = np.empty((n, k // 8), np.int32)
+    sc = np.empty((n, k // g), np.uint16)
+    qz = np.empty((n, (k // g + 7) // 8), np.int32)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        _check(_lib.ql_awq_search(x.ctypes.data, t, w.ctypes.data, n, k, int(group), int(grid), ws.data_ptr(),
+                                  ws.numel(), stream, err.ctypes.data, best.ctypes.data, s.ctypes.data,
+                                  qw.ctypes.data, sc.ctypes.data, qz.ctypes.data))
+    return err[:int(grid)], int(best[0]), s, (qw, sc.view(np.float16), qz)
+
+
+def awq_search_workspace_bytes(t: int, n: int, k: int, group: int) -> int:
+    return int(_lib.ql_awq_search_workspace_bytes(t, n, k, int(group)))
 
 
 def smooth(x, gamma, w):

@@ -28,7 +28,7 @@ HOST_SOURCES = ["status.cpp", "host_quant.cpp"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC]
-HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-mf16c", "-Wall", "-Wextra",
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-mf16c", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
               "-ffp-contract=off", "-I", INCLUDE, "-I", CSRC, f"-I{ROCM}/include"]
 
 
