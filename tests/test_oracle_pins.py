@@ -660,7 +660,9 @@ def test_f64_to_f16_rounds_once():
     mids = (h[:-1] + h[1:]) / 2
     for vals in (v, mids, -mids[::97]):
         got = np.array([oracle.f64_to_f16(a) for a in vals], np.uint16)
-        assert np.array_equal(got, vals.astype(np.float16).view(np.uint16))
+        with np.errstate(over="ignore"):          # values past 65520 become inf on both sides
+            want = vals.astype(np.float16).view(np.uint16)
+        assert np.array_equal(got, want)
 
 
 def test_awq_scales_closed_forms():

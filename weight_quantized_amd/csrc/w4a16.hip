@@ -3,6 +3,8 @@
 //   w4a16_dequant_kernel  -- writes the shared dequantisation routine's output
 //   w4a16_decode_kernel   -- m <= 32: split-K GEMV on MFMA, weights streamed
 //                            from HBM once, dequantised in registers
+//   w4a16_decode_ra_kernel -- the same GEMV for single-row launches, with the
+//                            activations and tables resident in LDS
 //   w4a16_gemm_kernel     -- any m: LDS-tiled fp16 MFMA GEMM
 //
 // Weight format (LMDeploy walkthrough, section 2; AUQ page, section 5.4):
@@ -571,7 +573,8 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 }
 
 // ---------------------------------------------------------------------------
-// decode with resident activations: m <= MT (16 or 32)
+// decode with resident activations: m <= MT (written for 16 or 32 rows;
+// single-row launches use it, see the host plan)
 //
 // Workgroup = 4 waves; wave w owns one tile of 16 output channels, so a
 // workgroup covers 64 channels and one K slice of KS <= NB x 256.  The slice's
@@ -591,9 +594,9 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 // ---------------------------------------------------------------------------
 // Loads the compiler does not track, for a register ring that must stay in
 // flight across the barrier that publishes LDS: a 16-byte buffer load into
-// registers, a 4-byte and a 16-byte buffer load into LDS (at M0 + 4 or 16 x
-// lane), and a wait whose register operands keep each ring entry live, and
-// unread, until its load has landed.  Reads past a buffer's end return zero.
+// registers, a 4-byte buffer load into LDS (at M0 + 4 x lane), and a wait
+// whose register operands keep each ring entry live, and unread, until its
+// load has landed.  Reads past a buffer's end return zero.
 typedef uint32_t u4v_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u4v_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
@@ -725,8 +728,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
         ring[b][1] = buf_load16(rw, bw + 64u);
     }
     // 2. wait for everything but the weights and publish the tables and the
-    //    activations; a slice whose last block is ragged then zeroes the chunks
-    //    past its end (copied from clamped addresses) before any wave reads them
+    //    activations
     ql::stage_barrier<2 * P>();
     // 3. each activation chunk, once: reorder its eight values for the
     //    interleaved dequantiser (permute_x8), or clear it if it lies past the
