@@ -127,16 +127,20 @@ __device__ __forceinline__ void dequant_words_natural(const uint32_t (&w)[N], co
 }
 
 // Eight consecutive fp16 activations (as four 32-bit pairs) -> the order
-// (0,4)(1,5)(2,6)(3,7) that matches dequant_words.
-__device__ __forceinline__ uint4 permute_x8(uint4 v)
+// (0,4)(1,5)(2,6)(3,7) that matches dequant_words: one v_perm_b32 per output
+// dword, selecting two bytes from each of two input dwords.  With the
+// selectors sel_lo = kPermLo, sel_hi = kPermHi it reorders; with kPermZero
+// (selector byte 0x0C reads as 0x00) it writes zeros instead, so a masked
+// chunk costs no extra instruction.
+constexpr uint32_t kPermLo = 0x05040100u;     // [a.b0, a.b1, b.b0, b.b1] of perm(b, a)
+constexpr uint32_t kPermHi = 0x07060302u;     // [a.b2, a.b3, b.b2, b.b3]
+constexpr uint32_t kPermZero = 0x0C0C0C0Cu;
+__device__ __forceinline__ uint4 permute_x8_sel(uint4 v, uint32_t sel_lo, uint32_t sel_hi)
 {
-    uint4 p;
-    p.x = (v.x & 0xFFFFu) | (v.z << 16);
-    p.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-    p.z = (v.y & 0xFFFFu) | (v.w << 16);
-    p.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    return p;
+    return make_uint4(__builtin_amdgcn_perm(v.z, v.x, sel_lo), __builtin_amdgcn_perm(v.z, v.x, sel_hi),
+                      __builtin_amdgcn_perm(v.w, v.y, sel_lo), __builtin_amdgcn_perm(v.w, v.y, sel_hi));
 }
+__device__ __forceinline__ uint4 permute_x8(uint4 v) { return permute_x8_sel(v, kPermLo, kPermHi); }
 
 // Zero point of group g of one row: nibble g%8 of word g/8.
 __device__ __forceinline__ uint32_t zero_of(const uint32_t* qz_row, int g)

@@ -350,11 +350,18 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
             v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(e * 2u), 0, 0));
         }
     };
+    // rows past m and chunks past the slice's end are stored as zeros (the
+    // permute's zero selectors), without a branch
+    int xlim[XPT];
+#pragma unroll
+    for (int u = 0; u < XPT; ++u)
+        xlim[u] = xok[u] ? nch : 0;
     auto x_store = [&](int j, const uint4 (&v)[XPT]) {
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
-            const bool ok = xok[u] && j * 32 + xcc[u] < nch;
-            xs[j & 1][xdst[u]] = ok ? ql::permute_x8(v[u]) : make_uint4(0u, 0u, 0u, 0u);
+            const bool ok = j * 32 + xcc[u] < xlim[u];
+            xs[j & 1][xdst[u]] =
+                ql::permute_x8_sel(v[u], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
         }
     };
 
@@ -739,7 +746,8 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
         for (int e = tid; e < used; e += 256) {
             const int m = e / CR, cpos = e - m * CR;
             const int c = (cpos & ~31) + ((cpos & 31) ^ xswz(m));   // logical chunk stored here
-            xw[e] = c < nch ? ql::permute_x8(xw[e]) : make_uint4(0u, 0u, 0u, 0u);
+            const bool ok = c < nch;
+            xw[e] = ql::permute_x8_sel(xw[e], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
         }
         __syncthreads();
     }
