@@ -58,3 +58,44 @@ def test_awq_search_improves_on_the_fixed_ratio():
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     err, best, _, _ = ql.awq_search(x, w, group, grid)
     assert err[best] == err.min() and err[best] <= err[10]
+
+
+def test_awq_search_full_size_q_proj():
+    """The bench's search at full size (q_proj 4096 x 4096, 128 calibration
+    tokens, 20 ratios): the oracle's full grid would take about a minute, so
+    what is checked is unique and cheap: the chosen smoothing vector and the
+    packed weights bit-exact against the oracle's quantiser of W diag(s), all
+    errors finite, and the choice the smallest of them."""
+    w = workloads.config_weight("q_proj")
+    x = workloads.config_activations("qkv", 128, w.shape[1])
+    grid = 20
+    err, best, s, (qw, sc, qz) = ql.awq_search(x, w, 128, grid)
+    assert np.isfinite(err).all() and (err > 0).all()
+    assert best == int(np.argmin(err)) and err[best] <= err[grid // 2]
+    a = np.abs(x.astype(np.float32)).max(axis=0)
+    b = np.abs(w).max(axis=0)
+    assert np.array_equal(s, oracle.awq_scales(a, b, best / grid))
+    q, z, osc = oracle.awq_quantize(w * s[None, :], 128)
+    oqw, oqz = oracle.awq_pack(q, z, 128)
+    assert np.array_equal(qw, oqw) and np.array_equal(sc.view(np.uint16), osc) and np.array_equal(qz, oqz)
+
+
+@pytest.mark.parametrize("grid", [1, 3])
+def test_awq_search_zero_columns(grid):
+    """A calibration column that is all zero and a weight column that is all
+    zero keep s = 1 (nothing to balance); a one-point grid is the ratio 0."""
+    rng = np.random.default_rng(90 + grid)
+    t, n, k, group = 12, 96, 256, 32
+    x = calibration(rng, t, k)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x[:, 5] = 0
+    w[:, 9] = 0
+    err, best, s, (qw, sc, qz) = ql.awq_search(x, w, group, grid)
+    oerr, obest, os_ = oracle.awq_search(x, w, group, grid)
+    assert s[5] == 1.0 and s[9] == 1.0
+    assert np.allclose(err, oerr, rtol=RTOL, atol=0)
+    assert best == obest or oerr[best] <= oerr[obest] * (1 + RTOL)
+    if best == obest:
+        assert np.array_equal(s, os_)
+    if grid == 1:
+        assert best == 0
