@@ -204,6 +204,25 @@ def test_decode_single_row(ql, k, group):
     assert rel_err(y1.cpu().numpy(), ref) <= TOL
 
 
+# 9-32 rows on a wide N take six-wave workgroups (96 channels) when that keeps
+# every CU at one workgroup: a ragged last workgroup (20000 = 208 x 96 + 32)
+# and a ragged K, compared on sampled output channels including the tail.
+@pytest.mark.parametrize("m,k,group", [(12, 2176, 128), (24, 2080, 32), (32, 2176, 64)])
+def test_decode_six_wave_workgroups(ql, m, k, group):
+    n = 20000
+    rng = np.random.default_rng(m * 3 + k)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y1 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    rows = np.unique(np.concatenate([sample_rows(n, 3), np.arange(n - 40, n), np.arange(0, 40)]))
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
+    assert rel_err(y1.cpu().numpy()[:, rows], ref) <= TOL
+
+
 def test_decode_deterministic_and_workspace_left_zero(ql):
     m, n, k, group = 16, 4096, 4096, 128
     rng = np.random.default_rng(4)

@@ -102,9 +102,10 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 // ---------------------------------------------------------------------------
 // decode: m <= MT (16 or 32)
 //
-// Workgroup = 4 waves; wave w owns R tiles of 16 output channels, so a
-// workgroup covers TW = 64 R channels and one K slice of KS (a multiple of
-// 256; one slice when K is not split).  K advances in blocks of 256.  Per
+// Workgroup = T waves (4, or 6 where that keeps every CU at one workgroup);
+// wave w owns R tiles of 16 output channels, so a workgroup covers
+// TW = 16 T R channels and one K slice of KS (a multiple of 256; one slice
+// when K is not split).  K advances in blocks of 256.  Per
 // block each wave streams its rows' weights through a P-deep register ring,
 // and the workgroup streams the block's activations (rows < m) through a
 // two-slot LDS ring: the threads load block b + P's activations together with
@@ -156,12 +157,14 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t s16)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)s16);
 }
 
-// Workgroups per CU the register budget is held to: three for one 16-row
-// tile (a 1376-wave launch stays resident in one round), two for 32 rows.
-template <int MT, int R>
+// Workgroups per CU the register budget is held to: three four-wave
+// workgroups for one 16-row tile (a 1376-wave launch stays resident in one
+// round), two for 32 rows; as many T-wave workgroups as fit the same waves.
+template <int MT, int R, int T = 4>
 constexpr int decode_wg_per_cu()
 {
-    return R > 1 ? 1 : (MT == 16 ? 3 : 2);
+    constexpr int waves = 4 * (R > 1 ? 1 : (MT == 16 ? 3 : 2));
+    return waves / T > 0 ? waves / T : 1;
 }
 
 // Scale and zero-point tables of TW channels [n0, n0 + TW) for the groups
@@ -169,13 +172,14 @@ constexpr int decode_wg_per_cu()
 // scales starting at the even element at or below its first group (the dword
 // holding it), then per channel ZD words of zero points.  (The scales are read
 // in 4-byte units, up to the 4-byte boundary at or after their end.)  load()
-// requests a batch of SB scale dwords and ZB zero words per thread; store_all()
+// requests a batch of SB scale dwords and ZB zero words per thread (NT
+// threads); store_all()
 // writes it to LDS, then loads and writes any further batches.  Threads past
 // the end rewrite the last entry with its own value, so no load has a
 // conditional use the compiler could sink it into; each table has its own loop,
 // since a per-lane choice of buffer resource would make the compiler loop over
 // the distinct resources.
-template <int TW, int SB, int ZB>
+template <int TW, int SB, int ZB, int NT = 256>
 struct DecodeTables {
     __amdgpu_buffer_rsrc_t rsc, rzr;
     int n0, N, NG, ZW, g0, SD, ZD, stot, ztot;
@@ -197,7 +201,7 @@ struct DecodeTables {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
-            const int e = min(e0 + u * 256 + tid, stot - 1);
+            const int e = min(e0 + u * NT + tid, stot - 1);
             const int rr = e / SD, col = e - rr * SD;
             const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
             const uint32_t dw = ((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col;
@@ -205,7 +209,7 @@ struct DecodeTables {
         }
 #pragma unroll
         for (int u = 0; u < ZB; ++u) {
-            const int e = min(z0 + u * 256 + tid, ztot - 1);
+            const int e = min(z0 + u * NT + tid, ztot - 1);
             const int rr = e / ZD, col = e - rr * ZD;
             const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
             const uint32_t wd = row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col;
@@ -217,16 +221,16 @@ struct DecodeTables {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int u = 0; u < SB; ++u)
-            tab[min(e0 + u * 256 + tid, stot - 1)] = sv[u];
+            tab[min(e0 + u * NT + tid, stot - 1)] = sv[u];
 #pragma unroll
         for (int u = 0; u < ZB; ++u)
-            tab[stot + min(z0 + u * 256 + tid, ztot - 1)] = zv[u];
+            tab[stot + min(z0 + u * NT + tid, ztot - 1)] = zv[u];
     }
     // the first batch was requested by load(0, 0)
     __device__ __forceinline__ void store_all(uint32_t* tab)
     {
         store(tab, 0, 0);
-        for (int e0 = SB * 256, z0 = ZB * 256; e0 < stot || z0 < ztot; e0 += SB * 256, z0 += ZB * 256) {
+        for (int e0 = SB * NT, z0 = ZB * NT; e0 < stot || z0 < ztot; e0 += SB * NT, z0 += ZB * NT) {
             load(e0, z0);
             store(tab, e0, z0);
         }
@@ -299,16 +303,17 @@ __device__ __forceinline__ void splitk_finish(float* __restrict__ part, uint32_t
         __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int R, int P, bool POST>
-__global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode_kernel(
+template <int MT, int R, int P, bool POST, int T = 4>
+__global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
     uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
 {
-    constexpr int T = 4;
+    constexpr int NT = 64 * T;                     // threads
     constexpr int TW = 16 * T * R;                 // channels per workgroup
     constexpr int MTI = MT / 16;                   // MFMA row tiles
-    constexpr int XPT = MT / 8;                    // activation chunks per thread and block
+    constexpr int XC = MT * 32;                    // activation chunks per block
+    constexpr int XPT = (XC + NT - 1) / NT;        // ... per thread
     constexpr int NJ = POST ? 1 : (R * MTI >= 4 ? 1 : 4 / (R * MTI));   // accumulator chains
     constexpr int NW = 8 * R;                      // words per lane and block
     __shared__ uint4 xs[2][MT * 32];               // activation ring: two 256-k blocks
@@ -330,13 +335,16 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
     const int n0 = blockIdx.x * TW;
     const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
 
-    // activation chunks of this thread: chunk tid + 256 u of a block is chunk
-    // (tid + 256 u) % 32 of row (tid + 256 u) / 32
+    // activation chunks of this thread: chunk tid + NT u of a block is chunk
+    // (tid + NT u) % 32 of row (tid + NT u) / 32; with NT not dividing the
+    // block's chunks, a thread's last chunk may not exist (xhas)
     int xsrc[XPT], xdst[XPT], xcc[XPT];
-    bool xok[XPT];
+    bool xok[XPT], xhas[XPT];
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
-        const int c = tid + 256 * u, m = c >> 5, cc = c & 31;
+        const int craw = tid + NT * u;
+        xhas[u] = craw < XC;
+        const int c = xhas[u] ? craw : XC - 1, m = c >> 5, cc = c & 31;
         xok[u] = m < mrows;
         xcc[u] = cc;
         xsrc[u] = (m < mrows ? m : mrows - 1) * K + k0;   // element offset of the row's slice
@@ -360,14 +368,15 @@ __global__ __launch_bounds__(256, (decode_wg_per_cu<MT, R>())) void w4a16_decode
 #pragma unroll
         for (int u = 0; u < XPT; ++u) {
             const bool ok = j * 32 + xcc[u] < xlim[u];
-            xs[j & 1][xdst[u]] =
-                ql::permute_x8_sel(v[u], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
+            if (XC % NT == 0 || xhas[u])
+                xs[j & 1][xdst[u]] =
+                    ql::permute_x8_sel(v[u], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
         }
     };
 
     // scale and zero-point tables of this workgroup's channels and slice
     const int g0 = k0 >> lg;
-    DecodeTables<TW, 6 * R, 2 * R> tb(sc, qz, n0, N, NG, ZW, g0, gs);
+    DecodeTables<TW, 6 * R, 2 * R, NT> tb(sc, qz, n0, N, NG, ZW, g0, gs);
 
     // weights: block b of this lane's tile t, two 16-byte pieces
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
@@ -1381,7 +1390,8 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 struct DecodePlan {
     bool ra;    // resident-activation kernel (else the streamed one)
     int mt;     // 16 or 32
-    int r;      // 16-channel tiles per wave (the workgroup has 4 waves)
+    int t;      // waves per workgroup (streamed kernel: 4 or 6)
+    int r;      // 16-channel tiles per wave
     int p;      // blocks in flight per wave (resident kernel: most blocks per slice)
     bool post;  // group scale applied to the fp32 MFMA result (128-channel groups)
     int ks;     // k per slice (multiple of 256)
@@ -1400,12 +1410,13 @@ constexpr size_t kCounterBytes = 32768;
 constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
 constexpr int kDecodeWaveMin = 1024;             // 4 streaming waves per CU (MI355X: 256 CUs)
 constexpr int kDecodeWaveTarget = 2048;          // 8 streaming waves per CU
+constexpr bool kDecodeWide = true;               // six-wave workgroups where they avoid doubled CUs
 
 // Dynamic LDS of the decode kernel: the scale and zero-point tables.
-size_t decode_tables(int64_t sblocks, int r, int group)
+size_t decode_tables(int64_t sblocks, int64_t channels, int group)
 {
     const int64_t gs = sblocks * 256 / group;
-    return (size_t)(64 * r) * (size_t)((gs >> 1) + 1 + (gs >> 3) + 2) * 4;
+    return (size_t)channels * (size_t)((gs >> 1) + 1 + (gs >> 3) + 2) * 4;
 }
 // Tile and split choice (measured on the MLP decode shapes).  K is split
 // until the launch has ~8 streaming waves per CU, except that from 9 rows on
@@ -1418,15 +1429,23 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     p.p = 2;
     p.r = 1;
     p.post = group == 128;
-    const int64_t tw = 64 * p.r;
+    p.t = 4;
+    const int64_t cus = ql::cu_count();
+    // From 9 rows on, a launch not split along K whose four-wave column
+    // blocks would put two workgroups on some CUs, while six-wave ones fit
+    // one per CU, takes six-wave workgroups: the busiest CU then holds six
+    // channel tiles instead of eight.
+    if (kDecodeWide && m > 8 && cus > 0 && (n + 63) / 64 > cus && (n + 95) / 96 <= cus && (n + 63) / 64 * 4 >= kDecodeWaveMin)
+        p.t = 6;
+    const int64_t tw = 16 * p.t * p.r;
     p.nblk = (int)((n + tw - 1) / tw);
     const int64_t kblocks = (k + 255) / 256;
-    const int64_t waves = (int64_t)p.nblk * 4;
-    const int64_t target = (m > 8 && waves >= kDecodeWaveMin) ? waves : kDecodeWaveTarget;
+    const int64_t waves = (int64_t)p.nblk * p.t;
+    const int64_t target = (m > 8 && (waves >= kDecodeWaveMin || p.t == 6)) ? waves : kDecodeWaveTarget;
     int64_t slices = std::min<int64_t>((target + waves - 1) / waves, kblocks);
     const int64_t sblocks = (kblocks + slices - 1) / slices;
     p.ks = (int)(sblocks * 256);
-    p.lds_bytes = decode_tables(sblocks, p.r, group);
+    p.lds_bytes = decode_tables(sblocks, tw, group);
     p.slices = (int)((k + p.ks - 1) / p.ks);
     p.part_offset = kCounterBytes;
     // partial tiles [slices][nblk][m][64 r] fp32
@@ -1450,6 +1469,7 @@ DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
     DecodePlan p{};
     p.ra = true;
     p.mt = 16;
+    p.t = 4;
     p.r = 1;
     p.p = kRaBlocks;
     p.post = group == 128;
@@ -1464,7 +1484,7 @@ DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
     p.slices = (int)((k + p.ks - 1) / p.ks);
     // tables padded to whole batches (see the kernel), then the activation rows
     // in whole 4 KiB rounds of direct loads
-    const size_t tables = (size_t)((p.p + 1) + (p.p + 5) / 4) * 1024;
+    const size_t tables = (size_t)((p.p + 1) + (p.p + 5) / 4) * 1024;     // kernel's batch layout
     const size_t act = (size_t)((mrows * sblocks * 32 + 255) / 256) * 4096;
     p.act_off = tables;
     p.lds_bytes = tables + act;
@@ -1511,14 +1531,14 @@ int launch_status(const char* who)
     return QL_OK;
 }
 
-template <int MT, int R, int P, bool POST>
+template <int MT, int R, int P, bool POST, int T>
 void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                      const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST>), dim3(p.nblk, p.slices), dim3(256), p.lds_bytes, st, x,
-                       qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+    hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST, T>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes,
+                       st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
 }
 
 // Exact dispatch on the plan; returns false for a combination that is not
@@ -1550,15 +1570,15 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
         return false;
     }
 
-#define QL_DECODE_CASE(MT_, R_, P_)                                                          \
-    if (p.mt == MT_ && p.r == R_ && p.p == P_) {                                             \
-        if (p.post)                                                                          \
-            launch_decode_t<MT_, R_, P_, true>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
-        else                                                                                 \
-            launch_decode_t<MT_, R_, P_, false>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
-        return true;                                                                         \
+#define QL_DECODE_CASE(MT_, R_, P_, T_)                                                          \
+    if (p.mt == MT_ && p.r == R_ && p.p == P_ && p.t == T_) {                                    \
+        if (p.post)                                                                              \
+            launch_decode_t<MT_, R_, P_, true, T_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
+        else                                                                                     \
+            launch_decode_t<MT_, R_, P_, false, T_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
+        return true;                                                                             \
     }
-    QL_DECODE_CASE(16, 1, 2) QL_DECODE_CASE(32, 1, 2) QL_DECODE_CASE(16, 2, 2) QL_DECODE_CASE(32, 2, 2)
+    QL_DECODE_CASE(16, 1, 2, 4) QL_DECODE_CASE(32, 1, 2, 4) QL_DECODE_CASE(16, 1, 2, 6) QL_DECODE_CASE(32, 1, 2, 6)
 #undef QL_DECODE_CASE
     return false;
 }
@@ -1622,7 +1642,7 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
             QL_FAIL(QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
         const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
         if (!launch_decode(p, xw, qw, scales, qz, y, workspace, mi, ni, ki, lg, st))
-            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d r=%d p=%d", who, p.mt, p.r, p.p);
+            QL_FAIL(QL_ERR_UNSUPPORTED, "%s: no decode kernel for mt=%d r=%d p=%d t=%d", who, p.mt, p.r, p.p, p.t);
         return launch_status(who);
     }
     const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
