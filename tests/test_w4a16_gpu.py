@@ -205,11 +205,12 @@ def test_decode_single_row(ql, k, group):
 
 
 # 9-32 rows on a wide N take six-wave workgroups (96 channels) when that keeps
-# every CU at one workgroup: a ragged last workgroup (20000 = 208 x 96 + 32)
-# and a ragged K, compared on sampled output channels including the tail.
-@pytest.mark.parametrize("m,k,group", [(12, 2176, 128), (24, 2080, 32), (32, 2176, 64)])
-def test_decode_six_wave_workgroups(ql, m, k, group):
-    n = 20000
+# every CU at one workgroup: a ragged last workgroup (20000 = 208 x 96 + 32;
+# 20001 also ends inside a 16-channel tile) and a ragged K, compared on sampled
+# output channels including the tail.
+@pytest.mark.parametrize("m,k,group,n", [(12, 2176, 128, 20000), (24, 2080, 32, 20000), (32, 2176, 64, 20000),
+                                         (20, 2176, 128, 20001)])
+def test_decode_six_wave_workgroups(ql, m, k, group, n):
     rng = np.random.default_rng(m * 3 + k)
     w = workloads.weight(rng, n, k)
     x = workloads.activations(rng, m, k)
