@@ -887,8 +887,10 @@ int or_awq_search(const uint16_t* x, int64_t t, const float* w, int64_t n, int64
     uint16_t* wd16 = (uint16_t*)malloc((size_t)(n * k) * sizeof(uint16_t));
     uint16_t* xs = (uint16_t*)malloc((size_t)(t * k) * sizeof(uint16_t));
     double* yref = (double*)malloc((size_t)(t * n) * sizeof(double));
-    if (!a || !b || !s || !ws || !q || !z || !sc || !wd16 || !xs || !yref) {
+    double* erow = (double*)malloc((size_t)n * sizeof(double));
+    if (!a || !b || !s || !ws || !q || !z || !sc || !wd16 || !xs || !yref || !erow) {
         free(a); free(b); free(s); free(ws); free(q); free(z); free(sc); free(wd16); free(xs); free(yref);
+        free(erow);
         return OR_BAD;
     }
     for (int64_t j = 0; j < k; ++j) {
@@ -926,22 +928,29 @@ int or_awq_search(const uint16_t* x, int64_t t, const float* w, int64_t n, int64
         for (int64_t i = 0; i < t; ++i)
             for (int64_t j = 0; j < k; ++j)
                 xs[i * k + j] = or_f32_to_f16(or_f16_to_f32(x[i * k + j]) / s[j]);
-        double e2 = 0.0;
-#pragma omp parallel for schedule(static) reduction(+ : e2)
-        for (int64_t r = 0; r < n; ++r)
+        /* squared error per output channel, then the channels summed in
+           order: the total does not depend on the thread count */
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < n; ++r) {
+            double er = 0.0;
             for (int64_t i = 0; i < t; ++i) {
                 double acc = 0.0;
                 for (int64_t j = 0; j < k; ++j)
                     acc += (double)or_f16_to_f32(xs[i * k + j]) * (double)or_f16_to_f32(wd16[r * k + j]);
                 double d = (double)or_f16_to_f32(or_f64_to_f16(acc)) - yref[i * n + r];
-                e2 += d * d;
+                er += d * d;
             }
+            erow[r] = er;
+        }
+        double e2 = 0.0;
+        for (int64_t r = 0; r < n; ++r)
+            e2 += erow[r];
         err[g] = e2;
         if (e2 < err[bi])
             bi = g;
     }
     or_awq_scales(a, b, k, (double)bi / (double)grid, s_best);
     *best = bi;
-    free(a); free(b); free(s); free(ws); free(q); free(z); free(sc); free(wd16); free(xs); free(yref);
+    free(a); free(b); free(s); free(ws); free(q); free(z); free(sc); free(wd16); free(xs); free(yref); free(erow);
     return OR_OK;
 }

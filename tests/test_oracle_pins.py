@@ -741,3 +741,31 @@ def test_awq_search_lossless_round_trip():
     err, best, _ = oracle.awq_search(x, w, group, 10)
     assert (err / total >= 1e-4).all()
     assert err[best] == err.min() and best == int(np.argmin(err))
+
+
+def test_awq_search_independent_of_thread_count():
+    """The search's error sums do not depend on how many threads run the
+    oracle: per-channel partial sums are added in channel order, so runs with
+    1 and 3 OpenMP threads give bit-identical errors and the same choice."""
+    import json
+    import subprocess
+    import sys
+
+    code = (
+        "import json, numpy as np, oracle\n"
+        "rng = np.random.default_rng(74)\n"
+        "x = rng.standard_normal((6, 256)).astype(np.float32)\n"
+        "x[:, rng.choice(256, 3, replace=False)] *= 30\n"
+        "x = x.astype(np.float16)\n"
+        "w = (rng.standard_normal((37, 256)) * 0.02).astype(np.float32)\n"
+        "err, best, _ = oracle.awq_search(x, w, 64, 8)\n"
+        "print(json.dumps({'err': [float(e).hex() for e in err], 'best': best}))\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    runs = []
+    for threads in (1, 3):
+        env = dict(os.environ, OMP_NUM_THREADS=str(threads), PYTHONPATH=root)
+        out = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, check=True, capture_output=True,
+                             text=True).stdout
+        runs.append(json.loads(out.strip().splitlines()[-1]))
+    assert runs[0] == runs[1]
