@@ -28,9 +28,11 @@
  *     only enqueues work on `stream` (a hipStream_t, NULL = the null stream)
  *     and returns without synchronising.  Execution faults surface at the
  *     caller's next synchronisation.
- *   - The caller owns every buffer.  The library never allocates or frees
- *     memory and keeps no state between calls, except a thread-local error
- *     message.
+ *   - The caller owns every buffer.  The device entry points never allocate
+ *     or free memory and keep no state between calls, except a thread-local
+ *     error message and per-device attributes queried once (compute units,
+ *     LDS size).  The host helpers (ql_awq_pack, ql_awq_search, ...) use
+ *     temporary host memory of their own while they run.
  *   - Return value: QL_OK (0) or a negative QL_ERR_* code.  On any error
  *     nothing is launched and no output is written; ql_last_error() gives a
  *     human-readable reason on the calling thread.
@@ -98,12 +100,28 @@ int ql_awq_pack(const float* w, int64_t n, int64_t k, int group,
 size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
 
 /*
- * ql_w4a16_gemm (device).  y[m, n] = x[m, k] * dequant(W)^T with
- *   dequant(W)[r, c] = fp16((q[r, c] - z[r, c/group]) * s[r, c/group])
- * (one rounding of an exact product; the value ql_w4a16_dequant returns),
- * fp16 x fp16 products accumulated in fp32, y rounded once to fp16.
- * The dequantisation happens in registers; packed weights are streamed from
- * HBM once per call for m <= 32.
+ * ql_w4a16_gemm (device).  The W4A16 linear layer of the LMDeploy
+ * walkthrough, section 2 (int4 weights in groups along k, each group with its
+ * own fp16 scale and an asymmetric uint4 zero point), dequantised as the AUQ
+ * page, section 3.3, states it (int4 value times scale, with the zero point):
+ *   y[m, n] = sum_c x[m, c] * (q[n, c] - z[n, g]) * s[n, g],  g = c / group
+ * with fp32 accumulation and y rounded once to fp16.  The arithmetic of the
+ * weight factor depends on the kernel that runs:
+ *   - group 32 or 64, and any group with m > 32: each weight is formed as
+ *     w16 = fp16((q - z) * s), one rounding of the exact product (the value
+ *     ql_w4a16_dequant returns), and the exact fp16 x fp16 products x * w16
+ *     are summed in fp32.
+ *   - group 128 with m <= 32 (the decode kernels): the exact integers q - z
+ *     multiply the activations (exact products), each 32-term partial sum
+ *     within one group is formed in fp32 by the matrix cores, then multiplied
+ *     by s and added to the fp32 accumulator in one fused multiply-add; w16
+ *     is never formed.  Per
+ *     term this differs from the first form only by w16's rounding, at most
+ *     2^-11 of the weight, and a single nonzero activation (x = e_c) still
+ *     gives y = w16[:, c] bit for bit, since (q - z) * s is exact in fp32.
+ * The summation order is unspecified but fixed: repeating a call on the same
+ * inputs gives the same bits.  Packed weights are streamed from HBM once per
+ * call for m <= 32 and dequantised in registers.
  *   x        fp16 [m, k]            (device)
  *   qweight, scales, qzeros         as written by ql_awq_pack (device)
  *   y        fp16 [m, n]            (device, written)

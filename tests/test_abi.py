@@ -220,3 +220,25 @@ def test_awq_search_validation():
     assert call(tt=1 << 20, kk=4096) == E["QL_ERR_UNSUPPORTED"]
     assert call(wsb=need - 1) == E["QL_ERR_WORKSPACE"]
     assert call(ws=MIS) == E["QL_ERR_ALIGN"]
+
+
+def test_binding_shape_helpers():
+    """The binding's operand checks (host logic, no device): packed weights
+    must have the layout ql_awq_pack writes for the layer's (n, k, group)."""
+    import torch
+
+    n, k, g = 64, 512, 128
+    qw = torch.zeros((n, k // 8), dtype=torch.int32)
+    sc = torch.zeros((n, k // g), dtype=torch.float16)
+    qz = torch.zeros((n, 1), dtype=torch.int32)
+    ql._w4_operands(qw, sc, qz, n, k, g)
+    for bad in ((qw[:, :-1], sc, qz), (qw, sc[:, :-1], qz), (qw, sc, torch.zeros((n, 2), dtype=torch.int32)),
+                (qw[:-1], sc, qz)):
+        with pytest.raises(ValueError):
+            ql._w4_operands(*bad, n, k, g)
+    with pytest.raises(ValueError):
+        ql._w4_operands(qw, sc, qz, n, k, 48)
+    with pytest.raises(ValueError):
+        ql._w4_operands(qw, sc, qz, n, 500, g)
+    with pytest.raises(ValueError):
+        ql._shape(torch.zeros(3), (4,), "t")

@@ -77,7 +77,7 @@ def test_fp8_gemm_parity(ql, m, n, k):
     # codes of realistic size: quantised N(0,1) data, so sums cancel as in a layer
     xq, xs = oracle.quant_fp8(rng.standard_normal((m, k)).astype(np.float16))
     wq, ws = oracle.fp8_quant_weight((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
-    rows = np.unique(np.concatenate([np.arange(0, m, max(1, m // 64)), [m - 1]]))
+    rows = np.arange(m)
     bias = (rng.standard_normal(n) * 0.5).astype(np.float16)
     res = (rng.standard_normal((m, n)) * 0.5).astype(np.float16)
     ref = oracle.fp8_forward(xq, xs, wq, ws, rows=rows)
@@ -107,7 +107,7 @@ def test_fp8_gemm_extreme_codes(ql):
 
 def test_fp8_smoothquant_layer(ql):
     """The SmoothQuant workload through FP8: smoothing, per-channel FP8
-    weights, FP8 QRMSNorm, FP8 GEMM; checked on sampled rows."""
+    weights, FP8 QRMSNorm, FP8 GEMM; checked on every output."""
     x, gamma, w = workloads.smoothquant_inputs()
     s, gs, wsm = ql.smooth(x, gamma, w)
     wq, wsc = ql.fp8_quant_weight(wsm)
@@ -116,6 +116,7 @@ def test_fp8_smoothquant_layer(ql):
     torch.cuda.synchronize()
     oq, osc = oracle.quant_fp8(x, gs, 1e-6)
     assert np.array_equal(xq.cpu().numpy(), oq) and np.array_equal(xs.cpu().numpy(), osc)
-    rows = np.arange(0, x.shape[0], 97)
-    ref = oracle.fp8_forward(oq, osc, wq, wsc, rows=rows)
-    assert rel_err(y.cpu().numpy()[rows], ref) <= TOL
+    ref = oracle.fp8_forward(oq, osc, wq, wsc)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= TOL

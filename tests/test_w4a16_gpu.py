@@ -37,6 +37,34 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got.astype(np.float64) - ref)) / (den if den > 0 else 1.0))
 
 
+def oracle_weights64(qw, sc, qz, group):
+    """The oracle's dequantised weights fp16((q - z) s), as float64."""
+    q, z = oracle.awq_unpack(qw, qz, group)
+    _, wd16 = oracle.awq_dequant(q, z, sc, group)
+    del q
+    return wd16.astype(np.float64)
+
+
+def oracle_all_channels(x, qw, sc, qz, group, wd64=None):
+    """The oracle on every output channel: its unpacking and dequantisation,
+    then the fp64 contraction by numpy's matmul, which the oracle pins hold
+    equal to the oracle's own fp64 loop to 1e-12 (that loop, an element at a
+    time, would take minutes at these sizes).  Tests also check sampled
+    channels against the loop itself."""
+    if wd64 is None:
+        wd64 = oracle_weights64(qw, sc, qz, group)
+    return x.astype(np.float64) @ wd64.T
+
+
+def full_and_sampled(got, x, qw, sc, qz, group, rows, wd64=None):
+    """(error over every channel, error over the sampled channels against the
+    oracle's own contraction)."""
+    ref = oracle_all_channels(x, qw, sc, qz, group, wd64)
+    ref_rows = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
+    assert np.max(np.abs(ref[:, rows] - ref_rows)) <= 1e-9 * max(np.max(np.abs(ref_rows)), 1e-30)
+    return rel_err(got, ref), rel_err(got[:, rows], ref_rows)
+
+
 def sample_rows(n, seed=0, count=16):
     rng = np.random.default_rng(seed)
     mid = rng.choice(np.arange(16, n - 16), size=min(count, max(n - 32, 0)), replace=False) if n > 32 else []
@@ -129,10 +157,10 @@ def test_gemm_eight_wave_ring(ql, group):
     y = ql.w4a16_gemm(dev(x), *d, group, path=2)
     torch.cuda.synchronize()
     rows = sample_rows(n, group)
-    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
     got = y.cpu().numpy()
     assert np.isfinite(got).all()
-    assert rel_err(got[:, rows], ref) <= TOL
+    full, sampled = full_and_sampled(got, x, qw, sc, qz, group, rows)
+    assert full <= TOL and sampled <= TOL
 
 
 # The 32-row decode kernel with 17 to 32 rows: 18 column blocks of 64
@@ -154,9 +182,14 @@ def test_decode_17_to_32_rows(ql, m, group):
     assert rel_err(y1.cpu().numpy(), ref) <= TOL
 
 
+# With 128-channel groups the decode kernels multiply the exact integers
+# q - z and scale each group's fp32 partial sum; with one nonzero activation
+# that partial is exactly q - z and its product with s is exact in fp32, so
+# every path must still return the dequantised fp16 weight bit for bit.
+@pytest.mark.parametrize("group", [64, 128])
 @pytest.mark.parametrize("path", [1, 2])
-def test_gemm_closed_forms(ql, path):
-    k, group, n = 1024, 64, 96
+def test_gemm_closed_forms(ql, path, group):
+    k, n = 1024, 96
     rng = np.random.default_rng(9)
     w = workloads.weight(rng, n, k)
     (qw, sc, qz), d = pack_dev(ql, w, group)
@@ -175,6 +208,35 @@ def test_gemm_closed_forms(ql, path):
     assert not y2.any()
 
 
+# One-hot rows through each decode kernel at 128-channel groups: the
+# single-row kernel (m = 1), the 16-row kernel, the 32-row kernel (m = 24) and
+# six-wave workgroups (9-32 rows, N above 64 channels per CU), with K split
+# into slices where the plan splits it.
+@pytest.mark.parametrize("m,n,k", [(1, 1100, 4224), (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512),
+                                   (32, 20000, 512)])
+def test_decode_one_hot_bit_exact_group128(ql, m, n, k):
+    group = 128
+    rng = np.random.default_rng(m + n + k)
+    w = workloads.weight(rng, n, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    w16 = ql.w4a16_dequant(*d, group).cpu().numpy()
+    cols = rng.choice(k, size=m, replace=False)
+    cols[0] = k - 1
+    x = np.zeros((m, k), np.float16)
+    x[np.arange(m), cols] = 1.0
+    y = ql.w4a16_gemm(dev(x), *d, group, path=1).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), w16[:, cols].T.copy().view(np.uint16))
+    # a power-of-two activation scales the exact product by that power (equal
+    # values: where the weight is 0 the sum of zero products may be +0 or -0)
+    x2 = np.zeros((m, k), np.float16)
+    x2[np.arange(m), cols] = -2.0
+    y2 = ql.w4a16_gemm(dev(x2), *d, group, path=1).cpu().numpy()
+    want = (w16[:, cols].T.astype(np.float32) * np.float32(-2.0)).astype(np.float16)
+    assert np.array_equal(y2, want)
+    nz = want != 0
+    assert np.array_equal(y2[nz].view(np.uint16), want[nz].view(np.uint16))
+
+
 def test_gemm_empty(ql):
     qw = torch.zeros((64, 16), dtype=torch.int32, device="cuda:0")
     sc = torch.zeros((64, 1), dtype=torch.float16, device="cuda:0")
@@ -186,11 +248,8 @@ def test_gemm_empty(ql):
 # Single-row launches take the resident-activation decode kernel: K split into
 # slices of up to eight 256-blocks whose last block is ragged (4224 = 16 x 256
 # + 128; 4160 = 16 x 256 + 64), a ragged last column block, every group size.
-@pytest.mark.parametrize("k", [4224, 4160])
-@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("k,group", [(4224, 32), (4224, 64), (4224, 128), (4160, 32), (4160, 64)])
 def test_decode_single_row(ql, k, group):
-    if k % group:
-        pytest.skip("k must be a multiple of the group")
     n = 1100
     rng = np.random.default_rng(k + group)
     w = workloads.weight(rng, n, k)
@@ -220,8 +279,8 @@ def test_decode_six_wave_workgroups(ql, m, k, group, n):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     rows = np.unique(np.concatenate([sample_rows(n, 3), np.arange(n - 40, n), np.arange(0, 40)]))
-    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
-    assert rel_err(y1.cpu().numpy()[:, rows], ref) <= TOL
+    full, sampled = full_and_sampled(y1.cpu().numpy(), x, qw, sc, qz, group, rows)
+    assert full <= TOL and sampled <= TOL
 
 
 def test_decode_deterministic_and_workspace_left_zero(ql):
@@ -297,36 +356,54 @@ def test_decode_graph_replays_match_eager(ql):
 
 
 # ------------------------------------------------------------------ full-size configurations
+# Every configuration at its full size, compared on every output channel
+# (the oracle's dequantised weights and an fp64 contraction) and on sampled
+# channels against the oracle's own fp64 loop.
+_PACKED = {}
+
+
+def _packed(ql, name, group, seed=0):
+    """Packed weights (host and device) and the oracle's dequantised weights
+    of one configuration, kept for the tests that follow with the same one."""
+    key = (name, group, seed)
+    if key not in _PACKED:
+        _PACKED.clear()
+        w = workloads.config_weight(name, seed=seed)
+        host, d = pack_dev(ql, w, group)
+        _PACKED[key] = (host, d, w.shape, oracle_weights64(*host, group))
+    return _PACKED[key]
+
+
 def _config_case(ql, name, m, group, seed=0, rows_seed=0):
-    w = workloads.config_weight(name, seed=seed)
-    n, k = w.shape
+    (qw, sc, qz), d, (n, k), wd64 = _packed(ql, name, group, seed)
     x = workloads.config_activations(name, m, k, seed=seed)
-    (qw, sc, qz), d = pack_dev(ql, w, group)
     y = ql.w4a16_gemm(dev(x), *d, group)
     torch.cuda.synchronize()
-    rows = sample_rows(n, rows_seed)
-    ref = oracle.w4a16_forward(x, qw, sc, qz, group, rows=rows)
-    got = y.cpu().numpy()[:, rows]
-    assert np.isfinite(y.cpu().numpy()).all()
-    return rel_err(got, ref)
+    got = y.cpu().numpy()
+    assert np.isfinite(got).all()
+    return full_and_sampled(got, x, qw, sc, qz, group, sample_rows(n, rows_seed), wd64)
 
 
 def test_config_q_proj_m1(ql):
-    assert _config_case(ql, "q_proj", 1, 128) <= TOL
+    full, sampled = _config_case(ql, "q_proj", 1, 128)
+    assert full <= TOL and sampled <= TOL
 
 
 @pytest.mark.parametrize("m", [1, 4, 8, 16, 32])
 @pytest.mark.parametrize("name", ["gate_up", "down"])
 def test_config_llama7b_mlp_decode(ql, name, m):
-    assert _config_case(ql, name, m, 128) <= TOL
+    full, sampled = _config_case(ql, name, m, 128)
+    assert full <= TOL and sampled <= TOL
 
 
 def test_config_qkv_prefill(ql):
-    assert _config_case(ql, "qkv", 512, 64) <= TOL
+    full, sampled = _config_case(ql, "qkv", 512, 64)
+    assert full <= TOL and sampled <= TOL
 
 
+@pytest.mark.parametrize("m", [1, 8, 64, 256, 1024])
+@pytest.mark.parametrize("group", [128, 32])
 @pytest.mark.parametrize("name", ["13b_up", "13b_down"])
-@pytest.mark.parametrize("m,group", [(1, 128), (8, 128), (64, 128), (256, 128), (1024, 128),
-                                     (1, 32), (64, 32), (1024, 32)])
 def test_config_llama13b_sweep(ql, name, m, group):
-    assert _config_case(ql, name, m, group) <= TOL
+    full, sampled = _config_case(ql, name, m, group)
+    assert full <= TOL and sampled <= TOL

@@ -104,7 +104,7 @@ def test_gemm_fp16_parity_small(ql, m, n, k):
 
 def test_config_smoothquant_pipeline(ql):
     """Full W8A8 workload: host smoothing and int8 weights, GPU QRMSNorm and
-    int8 GEMM, against the oracle's own pipeline on sampled outputs."""
+    int8 GEMM, against the oracle's own pipeline on every output."""
     x, gamma, w = workloads.smoothquant_inputs()
     s, gs, wsm = ql.smooth(x, gamma, w)
     wq, wsc = ql.w8a8_quant_weight(wsm)
@@ -120,15 +120,11 @@ def test_config_smoothquant_pipeline(ql):
     torch.cuda.synchronize()
     assert np.array_equal(xq.cpu().numpy(), oxq)
     assert np.array_equal(xs.cpu().numpy(), oxs)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([np.arange(8), np.arange(2040, 2048), rng.choice(2048, 24, replace=False)]))
-    cols = np.unique(np.concatenate([np.arange(8), np.arange(11000, 11008), rng.choice(11008, 40, replace=False)]))
-    oacc = oracle.int8_gemm(oxq, owq, rows=rows, cols=cols)
-    assert np.array_equal(acc.cpu().numpy()[np.ix_(rows, cols)].astype(np.int64), oacc)
-    oy = oracle.w8a8_forward(oxq, oxs, owq, owsc, rows=rows, cols=cols)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), oracle.int8_gemm(oxq, owq))
+    oy = oracle.w8a8_forward(oxq, oxs, owq, owsc)
     got = y.cpu().numpy()
     assert np.isfinite(got).all()
-    assert rel_err(got[np.ix_(rows, cols)], oy) <= TOL
+    assert rel_err(got, oy) <= TOL
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 128, 4096), (300, 260, 1040), (2048, 512, 4096)])
@@ -153,7 +149,7 @@ def test_gemm_fp16_epilogue_rounding(ql, m, n, k):
 # 256 x 256 ring with 128-byte k-tiles: whole tiles, ragged m and n inside it,
 # n % 8 != 0 (no LDS-staged epilogue) and n % 4 != 0 (element stores).  The
 # int32 accumulator and the fp16 epilogue (with bias and residual) are checked
-# bit for bit on sampled rows.
+# bit for bit on every output.
 @pytest.mark.parametrize("m,n,k", [(2048, 8192, 512), (2000, 8100, 384), (2048, 8098, 256)])
 def test_gemm_big_tiles(ql, m, n, k):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -167,7 +163,7 @@ def test_gemm_big_tiles(ql, m, n, k):
     ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
     bias = (rng.standard_normal(n) * 4).astype(np.float16)
     res = (rng.standard_normal((m, n)) * 4).astype(np.float16)
-    rows = np.unique(np.concatenate([np.arange(0, m, 37), [m - 1, m - 2, 255, 256]]))
+    rows = np.arange(m)
     acc = ql.w8a8_gemm_i32(dev(xq), dev(wq))
     y = ql.w8a8_gemm_ex(dev(xq), dev(xs), dev(wq), dev(ws), bias=dev(bias), residual=dev(res))
     torch.cuda.synchronize()

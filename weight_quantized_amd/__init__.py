@@ -207,6 +207,50 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor t has exactly `shape`."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _same_device(ref, *ts):
+    for name, t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _mat(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t
+
+
+def _out(out, shape, dtype, like, name="out"):
+    """A caller-supplied output checked against (shape, dtype, device), or a
+    new one."""
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _dev(out, dtype, name)
+    _shape(out, shape, name)
+    _same_device(like, (name, out))
+    return out
+
+
+def _w4_operands(qweight, scales, qzeros, n, k, group):
+    """Check the packed-weight tensors of an [n, k] layer against the layout
+    ql_awq_pack writes."""
+    g = int(group)
+    if g not in (32, 64, 128):
+        raise ValueError(f"group {g} not in (32, 64, 128)")
+    if k % g:
+        raise ValueError(f"k={k} is not a multiple of the group {g}")
+    _shape(qweight, (n, k // 8), "qweight")
+    _shape(scales, (n, k // g), "scales")
+    _shape(qzeros, (n, (k // g + 7) // 8), "qzeros")
+
+
 def w4a16_workspace_bytes(m: int, n: int, k: int, group: int) -> int:
     return int(_lib.ql_w4a16_workspace_bytes(m, n, k, group))
 
@@ -215,10 +259,20 @@ _workspaces = {}
 
 
 def _workspace(device, nbytes):
-    """A zero-filled workspace per device, grown on demand.  The kernels leave
-    its counter area zero after every call, so it is reused as is."""
+    """A zero-filled split-K workspace per (device, stream), grown on demand.
+    The kernels leave its counter area zero after every call, so it is reused
+    as is.  Calls on one stream run in order and may share it; calls on
+    different streams may run concurrently and so each stream has its own.
+    It is allocated while its stream is current, so when a larger one
+    replaces it the caching allocator hands the old memory out again only to
+    work ordered after the kernels already queued on that stream.  Under
+    graph capture nothing is allocated: pass `workspace` explicitly there."""
     torch = _torch()
-    key = (device.type, device.index)
+    if torch.cuda.is_current_stream_capturing():
+        raise ValueError("w4a16_gemm under graph capture needs an explicit zero-filled workspace "
+                         f"of at least {nbytes} bytes")
+    stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -233,16 +287,17 @@ def w4a16_gemm(x, qweight, scales, qzeros, group: int, out=None, workspace=None,
     qweight = _dev(qweight, torch.int32, "qweight")
     scales = _dev(scales, torch.float16, "scales")
     qzeros = _dev(qzeros, torch.int32, "qzeros")
-    m, k = x.shape
-    n = qweight.shape[0]
-    if qweight.shape[1] * 8 != k:
-        raise ValueError("qweight does not match x's k")
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=x.device)
-    out = _dev(out, torch.float16, "out")
+    m, k = _mat(x, "x").shape
+    n = _mat(qweight, "qweight").shape[0]
+    _w4_operands(qweight, scales, qzeros, n, k, group)
+    _same_device(x, ("qweight", qweight), ("scales", scales), ("qzeros", qzeros))
+    out = _out(out, (m, n), torch.float16, x)
     need = w4a16_workspace_bytes(m, n, k, group) if path != PATH_GEMM else 0
     if workspace is None:
         workspace = _workspace(x.device, need) if need else None
+    else:
+        _dev(workspace, torch.uint8, "workspace")
+        _same_device(x, ("workspace", workspace))
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.ql_w4a16_gemm_path(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
@@ -256,7 +311,9 @@ def w4a16_dequant(qweight, scales, qzeros, group: int, with_codes: bool = False)
     qweight = _dev(qweight, torch.int32, "qweight")
     scales = _dev(scales, torch.float16, "scales")
     qzeros = _dev(qzeros, torch.int32, "qzeros")
-    n, k = qweight.shape[0], qweight.shape[1] * 8
+    n, k = _mat(qweight, "qweight").shape[0], qweight.shape[1] * 8
+    _w4_operands(qweight, scales, qzeros, n, k, group)
+    _same_device(qweight, ("scales", scales), ("qzeros", qzeros))
     w16 = torch.empty((n, k), dtype=torch.float16, device=qweight.device)
     q8 = torch.empty((n, k), dtype=torch.uint8, device=qweight.device) if with_codes else None
     _check(_lib.ql_w4a16_dequant(qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(), w16.data_ptr(),
@@ -264,16 +321,27 @@ def w4a16_dequant(qweight, scales, qzeros, group: int, with_codes: bool = False)
     return (w16, q8) if with_codes else w16
 
 
+def _token_outputs(x, xq, x_scale, code_dtype):
+    torch = _torch()
+    m, k = x.shape
+    return (_out(xq, (m, k), code_dtype, x, "xq"), _out(x_scale, (m,), torch.float32, x, "x_scale"))
+
+
+def _gamma(gamma, x):
+    torch = _torch()
+    gamma = _dev(gamma, torch.float16, "gamma")
+    _shape(gamma, (x.shape[1],), "gamma")
+    _same_device(x, ("gamma", gamma))
+    return gamma
+
+
 def w8a8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
     """QRMSNorm: (xq int8 [m, k], x_scale float32 [m])."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x")
-    gamma = _dev(gamma, torch.float16, "gamma")
+    x = _mat(_dev(x, torch.float16, "x"), "x")
+    gamma = _gamma(gamma, x)
     m, k = x.shape
-    if xq is None:
-        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
-    if x_scale is None:
-        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    xq, x_scale = _token_outputs(x, xq, x_scale, torch.int8)
     _check(_lib.ql_w8a8_quant_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), xq.data_ptr(),
                                       x_scale.data_ptr(), m, k, _stream(x)))
     return xq, x_scale
@@ -284,21 +352,14 @@ def w8a8_add_quant_rmsnorm(x, residual, gamma, eps: float = 1e-6, h_out=None, xq
     (pass h_out=residual, or x, to update in place), then QRMSNorm of h.
     Returns (h, xq int8 [m, k], x_scale float32 [m])."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x")
+    x = _mat(_dev(x, torch.float16, "x"), "x")
     residual = _dev(residual, torch.float16, "residual")
-    gamma = _dev(gamma, torch.float16, "gamma")
-    if residual.shape != x.shape:
-        raise ValueError("residual must have x's shape")
+    _shape(residual, x.shape, "residual")
+    _same_device(x, ("residual", residual))
+    gamma = _gamma(gamma, x)
     m, k = x.shape
-    if h_out is None:
-        h_out = torch.empty_like(x)
-    h_out = _dev(h_out, torch.float16, "h_out")
-    if h_out.shape != x.shape:
-        raise ValueError("h_out must have x's shape")
-    if xq is None:
-        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
-    if x_scale is None:
-        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    h_out = _out(h_out, (m, k), torch.float16, x, "h_out")
+    xq, x_scale = _token_outputs(x, xq, x_scale, torch.int8)
     _check(_lib.ql_w8a8_add_quant_rmsnorm(x.data_ptr(), residual.data_ptr(), gamma.data_ptr(), float(eps),
                                           h_out.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
     return h_out, xq, x_scale
@@ -308,37 +369,51 @@ def w8a8_quant_per_token(x, xq=None, x_scale=None):
     """Per-token int8 quantisation of a plain activation: (xq int8 [m, k],
     x_scale float32 [m]) with x_scale = max|x| / 127."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x")
+    x = _mat(_dev(x, torch.float16, "x"), "x")
     m, k = x.shape
-    if xq is None:
-        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
-    if x_scale is None:
-        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    xq, x_scale = _token_outputs(x, xq, x_scale, torch.int8)
     _check(_lib.ql_w8a8_quant_per_token(x.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
     return xq, x_scale
+
+
+def _gemm8_operands(xq, x_scale, wq, w_scale, code_dtype):
+    """Check the 8-bit GEMM operands: xq [m, k], x_scale [m], wq [n, k],
+    w_scale [n], all on one device; returns (m, n, k)."""
+    torch = _torch()
+    _dev(xq, code_dtype, "xq")
+    _dev(wq, code_dtype, "wq")
+    m, k = _mat(xq, "xq").shape
+    n = _mat(wq, "wq").shape[0]
+    _shape(wq, (n, k), "wq")
+    _same_device(xq, ("wq", wq))
+    if x_scale is not None:
+        _dev(x_scale, torch.float32, "x_scale")
+        _shape(x_scale, (m,), "x_scale")
+        _dev(w_scale, torch.float32, "w_scale")
+        _shape(w_scale, (n,), "w_scale")
+        _same_device(xq, ("x_scale", x_scale), ("w_scale", w_scale))
+    return m, n, k
+
+
+def _epilogue_terms(bias, residual, m, n, like):
+    torch = _torch()
+    if bias is not None:
+        bias = _dev(bias, torch.float16, "bias")
+        _shape(bias, (n,), "bias")
+    if residual is not None:
+        residual = _dev(residual, torch.float16, "residual")
+        _shape(residual, (m, n), "residual")
+    _same_device(like, ("bias", bias), ("residual", residual))
+    return bias, residual
 
 
 def w8a8_gemm_ex(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
     """y fp16 [m, n] = fp16((xq @ wq^T) * x_scale * w_scale [+ bias] [+ residual]),
     bias fp16 [n], residual fp16 [m, n]; out may be residual (in place)."""
     torch = _torch()
-    xq = _dev(xq, torch.int8, "xq")
-    wq = _dev(wq, torch.int8, "wq")
-    x_scale = _dev(x_scale, torch.float32, "x_scale")
-    w_scale = _dev(w_scale, torch.float32, "w_scale")
-    m, k = xq.shape
-    n = wq.shape[0]
-    if bias is not None:
-        bias = _dev(bias, torch.float16, "bias")
-        if bias.shape != (n,):
-            raise ValueError("bias must be [n]")
-    if residual is not None:
-        residual = _dev(residual, torch.float16, "residual")
-        if residual.shape != (m, n):
-            raise ValueError("residual must be [m, n]")
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
-    out = _dev(out, torch.float16, "out")
+    m, n, k = _gemm8_operands(xq, x_scale, wq, w_scale, torch.int8)
+    bias, residual = _epilogue_terms(bias, residual, m, n, xq)
+    out = _out(out, (m, n), torch.float16, xq)
     _check(_lib.ql_w8a8_gemm_ex(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
                                 bias.data_ptr() if bias is not None else None,
                                 residual.data_ptr() if residual is not None else None, out.data_ptr(), m, n, k,
@@ -349,14 +424,8 @@ def w8a8_gemm_ex(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
 def w8a8_gemm(xq, x_scale, wq, w_scale, out=None):
     """y fp16 [m, n] = fp16((xq @ wq^T) * x_scale[:, None] * w_scale[None, :])."""
     torch = _torch()
-    xq = _dev(xq, torch.int8, "xq")
-    wq = _dev(wq, torch.int8, "wq")
-    x_scale = _dev(x_scale, torch.float32, "x_scale")
-    w_scale = _dev(w_scale, torch.float32, "w_scale")
-    m, k = xq.shape
-    n = wq.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
+    m, n, k = _gemm8_operands(xq, x_scale, wq, w_scale, torch.int8)
+    out = _out(out, (m, n), torch.float16, xq)
     _check(_lib.ql_w8a8_gemm(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
                              out.data_ptr(), m, n, k, _stream(xq)))
     return out
@@ -375,13 +444,10 @@ def fp8_quant_weight(w):
 def fp8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
     """QRMSNorm with FP8 E4M3 codes: (xq uint8 [m, k], x_scale float32 [m])."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x")
-    gamma = _dev(gamma, torch.float16, "gamma")
+    x = _mat(_dev(x, torch.float16, "x"), "x")
+    gamma = _gamma(gamma, x)
     m, k = x.shape
-    if xq is None:
-        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    if x_scale is None:
-        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    xq, x_scale = _token_outputs(x, xq, x_scale, torch.uint8)
     _check(_lib.ql_fp8_quant_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), xq.data_ptr(),
                                      x_scale.data_ptr(), m, k, _stream(x)))
     return xq, x_scale
@@ -390,12 +456,9 @@ def fp8_quant_rmsnorm(x, gamma, eps: float = 1e-6, xq=None, x_scale=None):
 def fp8_quant_per_token(x, xq=None, x_scale=None):
     """Per-token FP8 E4M3 quantisation: (xq uint8 [m, k], x_scale float32 [m])."""
     torch = _torch()
-    x = _dev(x, torch.float16, "x")
+    x = _mat(_dev(x, torch.float16, "x"), "x")
     m, k = x.shape
-    if xq is None:
-        xq = torch.empty((m, k), dtype=torch.uint8, device=x.device)
-    if x_scale is None:
-        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    xq, x_scale = _token_outputs(x, xq, x_scale, torch.uint8)
     _check(_lib.ql_fp8_quant_per_token(x.data_ptr(), xq.data_ptr(), x_scale.data_ptr(), m, k, _stream(x)))
     return xq, x_scale
 
@@ -403,23 +466,9 @@ def fp8_quant_per_token(x, xq=None, x_scale=None):
 def fp8_gemm(xq, x_scale, wq, w_scale, bias=None, residual=None, out=None):
     """y fp16 [m, n] = fp16(sum(e4m3 xq * e4m3 wq) * x_scale * w_scale [+ bias] [+ residual])."""
     torch = _torch()
-    xq = _dev(xq, torch.uint8, "xq")
-    wq = _dev(wq, torch.uint8, "wq")
-    x_scale = _dev(x_scale, torch.float32, "x_scale")
-    w_scale = _dev(w_scale, torch.float32, "w_scale")
-    m, k = xq.shape
-    n = wq.shape[0]
-    if bias is not None:
-        bias = _dev(bias, torch.float16, "bias")
-        if bias.shape != (n,):
-            raise ValueError("bias must be [n]")
-    if residual is not None:
-        residual = _dev(residual, torch.float16, "residual")
-        if residual.shape != (m, n):
-            raise ValueError("residual must be [m, n]")
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=xq.device)
-    out = _dev(out, torch.float16, "out")
+    m, n, k = _gemm8_operands(xq, x_scale, wq, w_scale, torch.uint8)
+    bias, residual = _epilogue_terms(bias, residual, m, n, xq)
+    out = _out(out, (m, n), torch.float16, xq)
     _check(_lib.ql_fp8_gemm(xq.data_ptr(), x_scale.data_ptr(), wq.data_ptr(), w_scale.data_ptr(),
                             bias.data_ptr() if bias is not None else None,
                             residual.data_ptr() if residual is not None else None, out.data_ptr(), m, n, k,
@@ -431,13 +480,13 @@ def kv_quant_int8(x, group: int = 128, q=None, scale=None):
     """KV-cache INT8 groups: (q int8, x's shape; scale float32 [x.numel() // group])."""
     torch = _torch()
     x = _dev(x, torch.float16, "x")
+    if int(group) not in (32, 64, 128):
+        raise ValueError(f"group {group} not in (32, 64, 128)")
     if x.numel() % group:
         raise ValueError("x's size must be a multiple of the group")
     groups = x.numel() // group
-    if q is None:
-        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
-    if scale is None:
-        scale = torch.empty((groups,), dtype=torch.float32, device=x.device)
+    q = _out(q, tuple(x.shape), torch.int8, x, "q")
+    scale = _out(scale, (groups,), torch.float32, x, "scale")
     _check(_lib.ql_kv_quant_int8(x.data_ptr(), q.data_ptr(), scale.data_ptr(), groups, int(group), _stream(x)))
     return q, scale
 
@@ -447,10 +496,13 @@ def kv_dequant_int8(q, scale, group: int = 128, out=None):
     torch = _torch()
     q = _dev(q, torch.int8, "q")
     scale = _dev(scale, torch.float32, "scale")
-    if q.numel() % group or scale.numel() != q.numel() // group:
-        raise ValueError("q and scale do not match the group")
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.float16, device=q.device)
+    if int(group) not in (32, 64, 128):
+        raise ValueError(f"group {group} not in (32, 64, 128)")
+    if q.numel() % group:
+        raise ValueError("q's size must be a multiple of the group")
+    _shape(scale, (q.numel() // group,), "scale")
+    _same_device(q, ("scale", scale))
+    out = _out(out, tuple(q.shape), torch.float16, q)
     _check(_lib.ql_kv_dequant_int8(q.data_ptr(), scale.data_ptr(), out.data_ptr(), q.numel() // group, int(group),
                                    _stream(q)))
     return out
@@ -459,11 +511,7 @@ def kv_dequant_int8(q, scale, group: int = 128, out=None):
 def w8a8_gemm_i32(xq, wq, out=None):
     """Raw int32 accumulator [m, n] = xq @ wq^T."""
     torch = _torch()
-    xq = _dev(xq, torch.int8, "xq")
-    wq = _dev(wq, torch.int8, "wq")
-    m, k = xq.shape
-    n = wq.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    m, n, k = _gemm8_operands(xq, None, wq, None, torch.int8)
+    out = _out(out, (m, n), torch.int32, xq)
     _check(_lib.ql_w8a8_gemm_i32(xq.data_ptr(), wq.data_ptr(), out.data_ptr(), m, n, k, _stream(xq)))
     return out

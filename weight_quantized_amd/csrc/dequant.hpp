@@ -1,6 +1,10 @@
-// Device dequantisation of packed uint4 weights (gfx950).  The same two
-// routines serve the dequant export and the W4A16 kernels, so the bit-exact
-// check of the export covers the values the kernels contract.
+// Device dequantisation of packed uint4 weights (gfx950).  The same routines
+// serve the dequant export and the W4A16 kernels.  The export writes
+// fp16((q - z) * s), the weights the GEMM kernels and the decode kernels at
+// groups 32 and 64 contract, so its bit-exact check covers those.  The decode
+// kernels at group 128 run only the first two stages (dequant_words_qz: the
+// exact integers q - z) and apply s to the fp32 matrix-core result instead;
+// their one-hot test checks that path bit for bit.
 //
 // A 32-bit word holds codes q0..q7 (code i in bits [4i, 4i+4), consecutive
 // input channels).  OR-ing a nibble into the mantissa of an fp16 constant
