@@ -140,6 +140,29 @@ int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* sca
                   const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k,
                   int group, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ql_w4a16_gemm_noalloc (device).  ql_w4a16_gemm for callers that cannot
+ * allocate device memory -- code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc: the same kernels, results
+ * bit-identical to ql_w4a16_gemm, with the split-K workspace taken from a
+ * scratch array the library holds in device memory instead of an argument.
+ *   Arguments as ql_w4a16_gemm, without the workspace.
+ *   Scratch: 8 MiB per device (a 32 KiB counter region plus partial sums),
+ *   placed when the library's code loads on that device and held until the
+ *   process ends; the first call on a device clears its counters with a
+ *   small kernel on `stream`, and every completed call leaves them zero.
+ *   The call itself allocates nothing (no hipMalloc, no library allocator).
+ *   Every call on a device shares that device's scratch: calls that may
+ *   overlap on one device (other streams, other threads) race and must be
+ *   serialised by the caller.
+ * Errors: as ql_w4a16_gemm; QL_ERR_WORKSPACE when the shape needs more
+ * split-K scratch than the array holds (ql_w4a16_workspace_bytes > 8 MiB);
+ * QL_ERR_HIP if the scratch array's address cannot be obtained.
+ */
+int ql_w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                          const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k, int group,
+                          void* stream);
+
 /* As ql_w4a16_gemm with an explicit kernel choice (QL_PATH_*), for tests and
  * tuning.  QL_PATH_DECODE with m > 32 is QL_ERR_UNSUPPORTED. */
 int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

@@ -37,6 +37,7 @@ EXPORTS = {
     "ql_w4a16_workspace_bytes": (_sz, [_i64, _i64, _i64, _i]),
     "ql_w4a16_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p]),
     "ql_w4a16_gemm_path": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p, _sz, _p, _i]),
+    "ql_w4a16_gemm_noalloc": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i, _p]),
     "ql_w4a16_dequant": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i, _p]),
     "ql_smooth": (_i, [_p, _i64, _p, _p, _i64, _i64, _p, _p, _p]),
     "ql_w8a8_quant_weight": (_i, [_p, _i64, _i64, _p, _p]),
@@ -302,6 +303,26 @@ def w4a16_gemm(x, qweight, scales, qzeros, group: int, out=None, workspace=None,
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib.ql_w4a16_gemm_path(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
                                    out.data_ptr(), m, n, k, int(group), wptr, wbytes, _stream(x), int(path)))
+    return out
+
+
+def w4a16_gemm_noalloc(x, qweight, scales, qzeros, group: int, out):
+    """y fp16 [m, n] = x fp16 [m, k] @ dequant(W)^T into the caller's `out`,
+    with the split-K scratch held by the library (nothing is allocated)."""
+    torch = _torch()
+    x = _dev(x, torch.float16, "x")
+    qweight = _dev(qweight, torch.int32, "qweight")
+    scales = _dev(scales, torch.float16, "scales")
+    qzeros = _dev(qzeros, torch.int32, "qzeros")
+    m, k = _mat(x, "x").shape
+    n = _mat(qweight, "qweight").shape[0]
+    _w4_operands(qweight, scales, qzeros, n, k, group)
+    _same_device(x, ("qweight", qweight), ("scales", scales), ("qzeros", qzeros))
+    if out is None:
+        raise ValueError("w4a16_gemm_noalloc writes into a caller-supplied `out`")
+    out = _out(out, (m, n), torch.float16, x)
+    _check(_lib.ql_w4a16_gemm_noalloc(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+                                      out.data_ptr(), m, n, k, int(group), _stream(x)))
     return out
 
 

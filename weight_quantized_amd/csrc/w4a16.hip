@@ -13,7 +13,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "dequant.hpp"
 #include "lds_dma.hpp"
@@ -1679,6 +1681,93 @@ extern "C" int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
 {
     return ql_w4a16_gemm_path(x, qweight, scales, qzeros, y, m, n, k, group, workspace, workspace_bytes, stream,
                               QL_PATH_AUTO);
+}
+
+// ---------------------------------------------------------------------------
+// ql_w4a16_gemm_noalloc: the same kernels with the split-K workspace in a
+// file-scope device array instead of caller memory.  Each device that runs
+// the library holds its own copy of `scratch` until the process ends.  Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)8 << 20;   // 32 KiB of counters + partial sums
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+__global__ void zero_words_kernel(uint32_t* p, int count)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array; on the first call for a
+// device its counter region is cleared by a small kernel on `st` (ordered
+// before the caller's launch; no memset node, so the call may be captured).
+int scratch_for_current_device(hipStream_t st, void** out, const char* who)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        QL_FAIL(QL_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", who, dev, kMaxDevices);
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) {
+        *out = p;
+        return QL_OK;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            QL_FAIL(QL_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who, dev,
+                    hipGetErrorString(e));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(8), dim3(256), 0, st, static_cast<uint32_t*>(p),
+                           (int)(kCounterBytes / sizeof(uint32_t)));
+        if (int rc = launch_status(who))
+            return rc;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return QL_OK;
+}
+
+}  // namespace
+
+extern "C" int ql_w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                                     const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k,
+                                     int group, void* stream)
+{
+    ql::clear_error();
+    const char* who = "ql_w4a16_gemm_noalloc";
+    if (int rc = check_common(qweight, scales, qzeros, n, k, group, who))
+        return rc;
+    if (m < 0)
+        QL_FAIL(QL_ERR_SHAPE, "%s: m=%lld", who, (long long)m);
+    if (m == 0 || n == 0)
+        return QL_OK;
+    const size_t need = ql_w4a16_workspace_bytes(m, n, k, group);
+    if (need > kScratchBytes)
+        QL_FAIL(QL_ERR_WORKSPACE,
+                "%s: m=%lld n=%lld k=%lld needs %zu bytes of split-K scratch; this entry point holds at most %zu "
+                "(use ql_w4a16_gemm with a workspace)",
+                who, (long long)m, (long long)n, (long long)k, need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        if (!x || !y)
+            QL_FAIL(QL_ERR_NULL, "%s: null pointer", who);
+        if (int rc = scratch_for_current_device(static_cast<hipStream_t>(stream), &ws, who))
+            return rc;
+    }
+    return ql_w4a16_gemm_path(x, qweight, scales, qzeros, y, m, n, k, group, ws, need > 0 ? kScratchBytes : 0,
+                              stream, QL_PATH_AUTO);
 }
 
 extern "C" int ql_w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
