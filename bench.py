@@ -2,11 +2,13 @@
 """Benchmark of the quantized linear layer on one MI355X.
 
 A step is one pass of the W4A16 decode hot path over the LLaMA-7B MLP
-workload: for each batch size M in {1, 4, 8, 16, 32}, the fused gate/up
-projection (K=4096, N=22016) and the down projection (K=11008, N=4096), int4
-weights in groups of 128 (asymmetric uint4 zero points, fp16 scales), fp16
-activations.  Weights are streamed cold: every launch reads one of several
-weight copies that together exceed the 256 MB Infinity Cache.
+workload at the batch sizes the headline metric covers: for each M in
+{1, 4, 8, 16}, the fused gate/up projection (K=4096, N=22016) and the down
+projection (K=11008, N=4096), int4 weights in groups of 128 (asymmetric
+uint4 zero points, fp16 scales), fp16 activations.  The same workload at
+M=32 is timed launch by launch in `detail` but is not part of the step.
+Weights are streamed cold: every launch reads one of several weight copies
+that together exceed the 256 MB Infinity Cache.
 
 Launches are captured in HIP graphs (one graph per step, rotating the weight
 copies), so the timed region measures the GPU rather than Python's launch
@@ -20,11 +22,14 @@ launches on the launch stream.  `traffic` is filled from the committed
 rocprofv3 counter summary when it was taken on the current kernel source.
 `detail` gives every launch of the step its graph-averaged duration and the
 p10 / median / p90 of 100 single launches (event pairs, cold weights).
-`extra` reports the W4A16 prefill GEMM (M=512 fused QKV) and the W8A8 layer
-(QRMSNorm + int8 GEMM, M=2048) against their rooflines, and the steps beside
-it (residual-fused QRMSNorm, per-token quantisation, the GEMM with bias and
-residual), the layer with FP8 E4M3 codes, and KV-cache INT8 group
-quantisation and dequantisation.  `reference` is a
+`extra` reports the LLaMA-7B q_proj GEMV (M=1), the LLaMA-13B MLP sweep
+(M in {1, 8, 64, 256, 1024}, both projections, groups 32 and 128), the W4A16
+prefill GEMM (M=512 fused QKV) and the W8A8 layer (QRMSNorm + int8 GEMM,
+M=2048) against their rooflines, and the steps beside it (residual-fused
+QRMSNorm, per-token quantisation, the GEMM with bias and residual), the
+layer with FP8 E4M3 codes, and KV-cache INT8 group quantisation and
+dequantisation.  Every weight-streaming extra rotates weight copies that
+together exceed the Infinity Cache.  `reference` is a
 plain device copy's rate, the achievable HBM bandwidth on the device.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
@@ -44,8 +49,10 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 INT8_MFMA_PEAK_TOPS = 5000.0    # dense
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense
-DECODE_M = (1, 4, 8, 16, 32)
+DECODE_M = (1, 4, 8, 16)        # the step: the batch sizes of the headline metric (M <= 16)
+DETAIL_M = (1, 4, 8, 16, 32)    # timed launch by launch
 GROUP = 128
+CACHE_BYTES = 256 << 20         # MI355X Infinity Cache
 METRIC = "W4A16/W8A8 GEMM: HBM GB/s (M<=16), TFLOP/s (M>=512), % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 COPY_BYTES = 256 << 20          # calibration copy: reads and writes this many bytes
@@ -64,6 +71,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_records():
+    """Counter-measured HBM bytes per launch, by workload ("gate_up_m16", ...)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    with open(TRAFFIC_FILE) as f:
+        return json.load(f).get("records", {})
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,8 +90,9 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="output channels per launch for the oracle sample (0 = all of them)")
     ap.add_argument("--profile-launch", metavar="SHAPE,M",
-                    help="run one workload for counter collection and exit: gate_up,M or down,M (decode, cold "
-                         "weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM); then a plain "
+                    help="run one workload for counter collection and exit: gate_up,M or down,M or q_proj,1 "
+                         "(decode, cold weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM); "
+                         "then a plain "
                          f"{COPY_BYTES >> 20} MiB device copy of known size that calibrates the byte counters")
     ap.add_argument("--profile-reps", type=int, default=12)
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -173,12 +189,13 @@ def main():
         sets[name] = [base] + [[t.clone() for t in base] for _ in range(args.copies - 1)]
         del w
     xs = {(name, m): torch.from_numpy(workloads.config_activations(name, m, shapes[name][1])).to(dev)
-          for name in shapes for m in DECODE_M}
+          for name in shapes for m in DETAIL_M}
     ys = {(name, m): torch.empty((m, shapes[name][0]), dtype=torch.float16, device=dev)
-          for name in shapes for m in DECODE_M}
-    need = max(ql.w4a16_workspace_bytes(m, n, k, g) for (n, k, g) in shapes.values() for m in DECODE_M)
+          for name in shapes for m in DETAIL_M}
+    need = max(ql.w4a16_workspace_bytes(m, n, k, g) for (n, k, g) in shapes.values() for m in DETAIL_M)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     launches = [(name, m) for m in DECODE_M for name in ("gate_up", "down")]
+    detail_launches = [(name, m) for m in DETAIL_M for name in ("gate_up", "down")]
     step_bytes = sum(w4a16_bytes(m, *shapes[name]) for name, m in launches)
 
     def launch(name, m, copy):
@@ -187,14 +204,14 @@ def main():
         return lambda: ql.w4a16_gemm(xs[(name, m)], d[0], d[1], d[2], g, out=ys[(name, m)], workspace=ws)
 
     # eager warm-up of every launch (first-call costs stay out of the graphs)
-    for name, m in launches:
+    for name, m in detail_launches:
         launch(name, m, 0)()
     torch.cuda.synchronize()
 
     # ---------------- per-launch durations: graphs of back-to-back launches
     reps = 8
     per = {}
-    for name, m in launches:
+    for name, m in detail_launches:
         g = capture(torch, [launch(name, m, c) for c in range(args.copies)])
         per[(name, m)] = time_graph(torch, g, reps) * 1e3 / args.copies      # us per launch
         del g
@@ -207,7 +224,7 @@ def main():
         for _ in range(12):
             big[1].copy_(big[0])
 
-    for name, m in launches:
+    for name, m in detail_launches:
         pct[(name, m)] = launch_percentiles(torch, [launch(name, m, c) for c in range(100)], blocker)
     del big
     copy_gbs = copy_rate(torch, dev)
@@ -231,30 +248,29 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     detail = []
-    for (name, m) in launches:
+    for (name, m) in detail_launches:
         n, k, g = shapes[name]
         b = w4a16_bytes(m, n, k, g)
         us = per[(name, m)]
         p10, p50, p90 = pct[(name, m)]
-        detail.append({"shape": name, "m": m, "n": n, "k": k, "us": round(us, 2),
+        detail.append({"shape": name, "m": m, "n": n, "k": k, "in_step": m in DECODE_M, "us": round(us, 2),
                        "GB/s": round(b / (us * 1e-6) / 1e9, 1),
                        "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                        "single_launch_us": {"p10": round(p10, 2), "median": round(p50, 2), "p90": round(p90, 2),
                                             "launches": 100}})
+    m32 = [(name, 32) for name in ("gate_up", "down")]
+    m32_bytes = sum(w4a16_bytes(32, *shapes[name]) for name, _ in m32)
+    m32_us = sum(per[key] for key in m32)
     dom = max(launches, key=lambda key: per[key])
     n, k, g = shapes[dom[0]]
     dom_bytes = w4a16_bytes(dom[1], n, k, g)
     achieved = dom_bytes / (per[dom] * 1e-6) / 1e9
-    traffic = None
     src_hash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        if t.get("source_hash") == src_hash and t.get("shape") == f"{dom[0]}_m{dom[1]}":
-            traffic = t.get("bytes_per_launch")
+    rec = traffic_records().get(f"{dom[0]}_m{dom[1]}", {})
+    traffic = rec.get("bytes_per_launch") if rec.get("source_hash") == src_hash else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": f"w4a16_decode_kernel ({dom[0]}, M={dom[1]}, N={n}, K={k})",
+                "kernel": f"W4A16 decode launch ({dom[0]}, M={dom[1]}, N={n}, K={k}, group {g})",
                 "avg_us": round(per[dom], 3), "bytes_per_launch": dom_bytes, "source_hash": src_hash}
 
     extra = []
@@ -271,10 +287,14 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": "W4A16 decode, LLaMA-7B MLP: gate/up K=4096 N=22016 + down K=11008 N=4096, "
-                               "M in {1,4,8,16,32}, group 128, asymmetric uint4, fp16 activations",
+                               "M in {1,4,8,16}, group 128, asymmetric uint4, fp16 activations",
                    "group": GROUP, "m": list(DECODE_M), "cold_weight_copies": args.copies,
                    "bytes_per_step": step_bytes, "launch": "hip graph per step"},
-        "roofline": roofline, "cpu_baseline": cpu, "detail": detail, "extra": extra,
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+        "m32": {"note": "the same MLP workload at M=32, outside the M<=16 metric: gate/up + down, per-launch graphs",
+                "us": round(m32_us, 2), "GB/s": round(m32_bytes / (m32_us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(m32_bytes / (m32_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "extra": extra,
         "reference": {"d2d_copy_GBps": round(copy_gbs, 1),
                       "note": "torch copy_ of 1 GiB on the device, read + write bytes; "
                               "achievable HBM rate on this device (fractions stay against 8 TB/s)"},
@@ -282,15 +302,66 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def cold_copies(nbytes, least=4):
+    """Weight copies whose total exceeds twice the Infinity Cache."""
+    return max(least, -(-2 * CACHE_BYTES // nbytes))
+
+
+def w4a16_entry(torch, ql, x, ds, g, y, ws, reps, name, m, n, k):
+    """Graph-averaged time of launches rotating the weight copies `ds`; GB/s
+    against HBM for M <= 64, TFLOP/s against fp16 MFMA above."""
+    ql.w4a16_gemm(x, *ds[0], g, out=y, workspace=ws)
+    gph = capture(torch, [(lambda d=d: ql.w4a16_gemm(x, *d, g, out=y, workspace=ws)) for d in ds])
+    us = time_graph(torch, gph, reps) * 1e3 / len(ds)
+    del gph
+    b = w4a16_bytes(m, n, k, g)
+    e = {"name": name, "m": m, "n": n, "k": k, "group": g, "us": round(us, 2), "copies": len(ds),
+         "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    if m <= 64:
+        e.update({"bound": "hbm", "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+    else:
+        tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        e.update({"bound": "mfma_fp16", "TFLOP/s": round(tf, 1), "frac_mfma_fp16": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)})
+    return e
+
+
 def measure_extra(torch, ql, workloads, dev, log):
     out = []
     reps = 6
+    # LLaMA-7B q_proj GEMV, M=1, group 128
+    log("[bench] extra: W4A16 q_proj M=1")
+    n, k, g = workloads.C1
+    qw, sc, qz = ql.awq_pack(workloads.config_weight("q_proj"), g)
+    copies = cold_copies(qw.nbytes)
+    ds = [[torch.from_numpy(a).to(dev) for a in (qw, sc, qz)] for _ in range(copies)]
+    x = torch.from_numpy(workloads.config_activations("q_proj", 1, k)).to(dev)
+    y = torch.empty((1, n), dtype=torch.float16, device=dev)
+    ws = torch.zeros(max(ql.w4a16_workspace_bytes(1, n, k, g), 1), dtype=torch.uint8, device=dev)
+    out.append(w4a16_entry(torch, ql, x, ds, g, y, ws, reps, "w4a16_q_proj", 1, n, k))
+    del ds
+    # LLaMA-13B MLP sweep: both projections, groups 128 and 32, M in {1, 8, 64, 256, 1024}
+    for name in ("13b_up", "13b_down"):
+        w = workloads.config_weight(name)
+        n, k = w.shape
+        for g in (128, 32):
+            log(f"[bench] extra: W4A16 LLaMA-13B {name} group {g}")
+            qw, sc, qz = ql.awq_pack(w, g)
+            copies = cold_copies(qw.nbytes)
+            ds = [[torch.from_numpy(a).to(dev) for a in (qw, sc, qz)] for _ in range(copies)]
+            need = max(ql.w4a16_workspace_bytes(m, n, k, g) for m in workloads.C5_M)
+            ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+            for m in workloads.C5_M:
+                x = torch.from_numpy(workloads.config_activations(name, m, k)).to(dev)
+                y = torch.empty((m, n), dtype=torch.float16, device=dev)
+                out.append(w4a16_entry(torch, ql, x, ds, g, y, ws, reps, "w4a16_" + name, m, n, k))
+            del ds, ws
+        del w
     # W4A16 prefill, fused QKV M=512, group 64
     n, k, g = workloads.C3
     w = workloads.config_weight("qkv")
     qw, sc, qz = ql.awq_pack(w, g)
     del w
-    copies = 8
+    copies = cold_copies(qw.nbytes)
     ds = [[torch.from_numpy(a).to(dev) for a in (qw, sc, qz)] for _ in range(copies)]
     x = torch.from_numpy(workloads.config_activations("qkv", 512, k)).to(dev)
     y = torch.empty((512, n), dtype=torch.float16, device=dev)
@@ -311,7 +382,7 @@ def measure_extra(torch, ql, workloads, dev, log):
     del wf, wsm
     xd = torch.from_numpy(xh).to(dev)
     gd = torch.from_numpy(gs).to(dev)
-    copies = 6
+    copies = cold_copies(wq.nbytes)
     wqs = [torch.from_numpy(wq).to(dev) for _ in range(copies)]
     wsd = torch.from_numpy(wsc).to(dev)
     m, kk = xh.shape
@@ -464,8 +535,8 @@ def profile_launch(args):
     torch.cuda.set_device(dev)
     shape, m = args.profile_launch.split(",")
     m = int(m)
-    if shape in ("gate_up", "down"):
-        n, k, g = {"gate_up": workloads.C2_GATEUP, "down": workloads.C2_DOWN}[shape]
+    if shape in ("gate_up", "down", "q_proj"):
+        n, k, g = {"gate_up": workloads.C2_GATEUP, "down": workloads.C2_DOWN, "q_proj": workloads.C1}[shape]
         w = workloads.config_weight(shape)
         qw, sc, qz = ql.awq_pack(w, g)
         del w
@@ -538,7 +609,7 @@ def traffic_summary(fetch_csv, write_csv):
     def median(v):
         return float(np.median(v)) if v else float("nan")
 
-    dec_f, dec_w = pick(fetch, "w4a16_decode_kernel"), pick(write, "w4a16_decode_kernel")
+    dec_f, dec_w = pick(fetch, "w4a16_decode"), pick(write, "w4a16_decode")
     cp_f, cp_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")
     if not (dec_f and dec_w and cp_f and cp_w):
         raise SystemExit("counter files lack the decode kernel or the calibration copy")
@@ -558,13 +629,16 @@ def traffic_summary(fetch_csv, write_csv):
                 meta = json.loads(lines[-1])
             break
     rec = {"source_hash": meta.get("source_hash", kernel_source_hash()), "shape": meta.get("shape"),
+           "kernel": sorted({name for (_, name) in fetch if "w4a16_decode" in name}),
            "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "algorithmic_bytes": meta.get("bytes_per_launch"),
            "fetch_kib_raw": median(dec_f), "write_kib_raw": median(dec_w),
            "copy_fetch_kib_raw": median(cp_f), "copy_write_kib_raw": median(cp_w),
            "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4), "dispatches": len(dec_f)}
+    records = traffic_records()
+    records[rec["shape"]] = rec
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump({"records": records}, f, indent=1)
         f.write("\n")
     alg = rec["algorithmic_bytes"]
     print(f"| launch | {rec['shape']} |\n|---|---|")

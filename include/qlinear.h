@@ -94,8 +94,11 @@ int ql_awq_pack(const float* w, int64_t n, int64_t k, int group,
                 int32_t* qweight, uint16_t* scales, int32_t* qzeros);
 
 /*
- * Bytes of device workspace ql_w4a16_gemm needs for this shape (0 if none).
- * The workspace holds split-K partial sums and per-tile arrival counters.
+ * Bytes of device workspace ql_w4a16_gemm needs for this shape (0 if none),
+ * enough for every kernel path ql_w4a16_gemm_path may take.  The workspace
+ * holds per-tile split-K arrival counters and fp32 partial sums: the decode
+ * kernels (m <= 32) split K when their column blocks alone would leave CUs
+ * idle, and so does the MFMA GEMM when its tiles would.
  */
 size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
 
@@ -147,7 +150,7 @@ int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* sca
  * bit-identical to ql_w4a16_gemm, with the split-K workspace taken from a
  * scratch array the library holds in device memory instead of an argument.
  *   Arguments as ql_w4a16_gemm, without the workspace.
- *   Scratch: 8 MiB per device (a 32 KiB counter region plus partial sums),
+ *   Scratch: 32 MiB per device (a 32 KiB counter region plus partial sums),
  *   placed when the library's code loads on that device and held until the
  *   process ends; the first call on a device clears its counters with a
  *   small kernel on `stream`, and every completed call leaves them zero.
@@ -156,7 +159,7 @@ int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* sca
  *   overlap on one device (other streams, other threads) race and must be
  *   serialised by the caller.
  * Errors: as ql_w4a16_gemm; QL_ERR_WORKSPACE when the shape needs more
- * split-K scratch than the array holds (ql_w4a16_workspace_bytes > 8 MiB);
+ * split-K scratch than the array holds (ql_w4a16_workspace_bytes > 32 MiB);
  * QL_ERR_HIP if the scratch array's address cannot be obtained.
  */
 int ql_w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

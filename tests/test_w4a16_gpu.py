@@ -163,6 +163,31 @@ def test_gemm_eight_wave_ring(ql, group):
     assert full <= TOL and sampled <= TOL
 
 
+# GEMM launches whose tiles would leave CUs idle split K into slices whose
+# partial tiles the last arrival sums in slice order: 64-row tiles (m <= 64)
+# and 128-row tiles, ragged m, n and last slice, every group size; reruns are
+# bit-identical and leave the workspace's counters at zero.
+@pytest.mark.parametrize("m,n,k,group", [(33, 200, 2048, 128), (64, 1000, 4096, 64), (70, 1000, 4096, 32),
+                                         (130, 2000, 3328, 128), (100, 5120, 13824, 32)])
+def test_gemm_split_k(ql, m, n, k, group):
+    need = ql.w4a16_workspace_bytes(m, n, k, group)
+    assert need > 0, "expected a split-K plan"
+    rng = np.random.default_rng(m + n + k + group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k, outlier_channel_frac=0.01)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    y1 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=2)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert not ws[:32768].cpu().numpy().any()
+    got = y1.cpu().numpy()
+    assert np.isfinite(got).all()
+    full, sampled = full_and_sampled(got, x, qw, sc, qz, group, sample_rows(n, 5))
+    assert full <= TOL and sampled <= TOL
+
+
 # The 32-row decode kernel with 17 to 32 rows: 18 column blocks of 64
 # channels with a ragged last one, K split into slices, 128-channel groups
 # (scale after the MFMA) and 32/64-channel groups (scaled fp16 weights);

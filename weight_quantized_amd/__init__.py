@@ -293,7 +293,7 @@ def w4a16_gemm(x, qweight, scales, qzeros, group: int, out=None, workspace=None,
     _w4_operands(qweight, scales, qzeros, n, k, group)
     _same_device(x, ("qweight", qweight), ("scales", scales), ("qzeros", qzeros))
     out = _out(out, (m, n), torch.float16, x)
-    need = w4a16_workspace_bytes(m, n, k, group) if path != PATH_GEMM else 0
+    need = w4a16_workspace_bytes(m, n, k, group)
     if workspace is None:
         workspace = _workspace(x.device, need) if need else None
     else:

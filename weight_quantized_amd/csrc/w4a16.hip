@@ -1104,6 +1104,67 @@ __global__ __launch_bounds__(256) void w4a16_gemm_kernel(const uint16_t* __restr
 // Tiles go to XCDs in groups of GM m-tiles (m fastest within a group), so the
 // 32 workgroups an XCD runs at once share a few activation and weight panels.
 // ---------------------------------------------------------------------------
+// Split-K completion of a GEMM tile, after this thread's agent-scope stores
+// of its part of the tile's fp32 partial sums ([rows][BN] at
+// part[(slice * tiles + tile) * srows * BN], srows = min(M, BM)): wait for
+// them, arrive on the tile's counter, and if this workgroup arrived last, sum
+// the nsl partial tiles in slice order and store y.  As splitk_finish: every
+// cross-workgroup value moves through agent-scope accesses, the last arrival
+// resets the counter, and the order of the sum does not depend on timing.
+template <int BN>
+__device__ __forceinline__ void gemm_splitk_finish(float* __restrict__ part, uint32_t* __restrict__ cnt,
+                                                   uint16_t* __restrict__ y, int M, int N, int m0, int n0, int tile,
+                                                   int tiles, int nsl, int srows, int* s_last)
+{
+    const int tid = threadIdx.x;
+    __builtin_amdgcn_s_waitcnt(0);      // this thread's partial stores have completed
+    __syncthreads();                    // ... and so have every other thread's
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (prev == (uint32_t)(nsl - 1));
+    }
+    __syncthreads();
+    if (!*s_last)
+        return;
+    const uint32_t tile_bytes = (uint32_t)srows * BN * 4u;
+    const uint32_t slice_bytes = (uint32_t)tiles * tile_bytes;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, (uint32_t)nsl * slice_bytes);
+    constexpr int kSc1 = 16;            // cache policy: agent scope (bypasses this CU's L1)
+    const int rows = min(srows, M - m0);
+    for (int v = tid; v < rows * (BN / 4); v += blockDim.x) {
+        const uint32_t off = (uint32_t)tile * tile_bytes + (uint32_t)v * 16u;
+        f4_t sum = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < nsl; s0 += 8) {
+            f4_t pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int sl = min(s0 + u, nsl - 1);
+                pv[u] = __builtin_bit_cast(
+                    f4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, (int)(off + (uint32_t)sl * slice_bytes), 0, kSc1));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < nsl)
+                    sum += pv[u];
+        }
+        const int m = m0 + v / (BN / 4), nn = n0 + (v % (BN / 4)) * 4;
+        uint16_t* yr = y + (int64_t)m * N;
+        if (nn + 3 < N && (N & 3) == 0) {
+            uint2 h;
+            h.x = f32_to_f16_bits(sum[0]) | ((uint32_t)f32_to_f16_bits(sum[1]) << 16);
+            h.y = f32_to_f16_bits(sum[2]) | ((uint32_t)f32_to_f16_bits(sum[3]) << 16);
+            *reinterpret_cast<uint2*>(yr + nn) = h;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (nn + e < N)
+                    yr[nn + e] = f32_to_f16_bits(sum[e]);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int BM_, int BN_, int WM_, int S_, int GM_, int NW_ = 4>
 struct W4PipeCfg {
     static constexpr int BM = BM_, BN = BN_, S = S_, GM = GM_;
@@ -1148,7 +1209,9 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
                                                               const uint32_t* __restrict__ qw,
                                                               const uint16_t* __restrict__ sc,
                                                               const uint32_t* __restrict__ qz,
-                                                              uint16_t* __restrict__ y, int M, int N, int K, int lg)
+                                                              uint16_t* __restrict__ y, int M, int N, int K, int lg,
+                                                              float* __restrict__ part, uint32_t* __restrict__ cnt,
+                                                              int KB, int nsl)
 {
     constexpr int BM = C::BM, BN = C::BN, S = C::S, D = C::D, DA = C::DA, DB = C::DB;
     constexpr int TM = BM / C::WM, TN = BN / C::WN;
@@ -1157,10 +1220,15 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
     static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
     extern __shared__ __attribute__((aligned(1024))) uint8_t pl[];   // S * kStageBytes
 
+    // Work unit u = slice * tiles + tile (split-K: nsl slices of KB blocks of
+    // 128 k; nsl = 1 without), so the units one XCD runs share a K slice of
+    // the activations.
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    const int tile = xcd_tile(blockIdx.x, tm * tn);
-    if (tile >= tm * tn)
+    const int tiles = tm * tn;
+    const int unit = xcd_tile(blockIdx.x, tiles * nsl);
+    if (unit >= tiles * nsl)
         return;
+    const int slice = unit / tiles, tile = unit - slice * tiles;
     const int gsz = C::GM * tn;                        // tiles per group of GM m-tiles
     const int grp = tile / gsz, first = grp * C::GM;
     const int gm = min(tm - first, C::GM);
@@ -1285,7 +1353,9 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
     ql::zb_t zb[2][FJ];
     h2_t s2[2][FJ];
     h8_t bw[2][FJ];
-    const int nk = K / 128;
+    const int kb_lo = slice * KB;                      // this slice's blocks [kb_lo, kb_hi)
+    const int kb_hi = min(K / 128, kb_lo + KB);
+    const int nkl = kb_hi - kb_lo;
     auto word = [](const uint4& w4, int st) { return st == 0 ? w4.x : st == 1 ? w4.y : st == 2 ? w4.z : w4.w; };
     // zero bias and scale of block kb from its table words
     auto set_zs = [&](int kb, int p) {
@@ -1313,11 +1383,11 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        issue(s < nk ? s : nk - 1, s);
-    ql::stage_barrier<D * (S - 1)>();   // block 0 landed
+        issue(kb_lo + (s < nkl ? s : nkl - 1), s);
+    ql::stage_barrier<D * (S - 1)>();   // the slice's first block landed
     read_a(0, 0, fa[0]);
-    read_b(0, 0, fb[0], zr[0], sr[0]);
-    set_zs(0, 0);
+    read_b(0, kb_lo, fb[0], zr[0], sr[0]);
+    set_zs(kb_lo, 0);
     dequant(0, 0, bw[0]);
 
     // One block.  fa[st & 1] / bw[st & 1] hold step st's operands, prepared
@@ -1339,7 +1409,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
                 interleave<FI, FI * FJ, 3>();
             } else {
                 ql::stage_barrier<D * (S - 2)>();
-                issue(min(kb + S, nk - 1), slot);
+                issue(min(kb + S, kb_hi - 1), slot);
                 read_b((u + 1) % S, kb + 1, fb[par ^ 1], zr[par ^ 1], sr[par ^ 1]);
                 read_a((u + 1) % S, 0, fa[cur ^ 1]);
                 mfmas(cur, 0, FI / 2);
@@ -1352,16 +1422,37 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
         }
     };
     int kb0 = 0;
-    for (; kb0 + U <= nk; kb0 += U) {
+    for (; kb0 + U <= nkl; kb0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            block(kb0 + u, u);
+            block(kb_lo + kb0 + u, u);
     }
 #pragma unroll
     for (int u = 0; u < U - 1; ++u)
-        if (kb0 + u < nk)
-            block(kb0 + u, u);
-    ql::stage_barrier<0>();   // drain the trailing reloads before the workgroup exits
+        if (kb0 + u < nkl)
+            block(kb_lo + kb0 + u, u);
+    ql::stage_barrier<0>();   // drain the trailing reloads; the ring's LDS is free from here
+
+    if (nsl > 1) {
+        // this slice's partial tile (rows < M), then the split-K completion;
+        // the first LDS word serves as the workgroup's flag
+        const int srows = M < BM ? M : BM;
+        float* tp = part + ((int64_t)slice * tiles + tile) * (int64_t)srows * BN;
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) {
+                const int ml = wm * TM + i * 16 + r16;
+                const int nl = wn * TN + j * 16 + 4 * q;
+                if (m0 + ml < M)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        __hip_atomic_store(&tp[ml * BN + nl + r], acc[i][j][r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+        gemm_splitk_finish<BN>(part, cnt, y, M, N, m0, n0, tile, tiles, nsl, srows, reinterpret_cast<int*>(pl));
+        return;
+    }
 
     // lane (q, r16) holds y[m][n .. n+3] of fragment (i, j)
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
@@ -1465,6 +1556,9 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
 constexpr int kRaBlocks = 8, kRaRing = 2;
 constexpr int64_t kRaActBytes = 65536;
 constexpr int64_t kRaMaxM = 1;
+// K is split further, up to this many workgroups per CU in all, when the
+// column blocks alone would leave CUs idle (q_proj: 64 column blocks).
+constexpr int64_t kRaWgPerCu = 1;
 
 DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
 {
@@ -1480,7 +1574,10 @@ DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
     const int64_t mrows = std::min<int64_t>(m, p.mt);
     int64_t sblocks = std::min<int64_t>(std::min<int64_t>(p.p, std::max<int64_t>(1, kRaActBytes / (mrows * 512))),
                                         kblocks);
-    const int64_t slices = (kblocks + sblocks - 1) / sblocks;
+    int64_t slices = (kblocks + sblocks - 1) / sblocks;
+    const int64_t cus = ql::cu_count();
+    if (cus > 0)
+        slices = std::min<int64_t>(std::max<int64_t>(slices, kRaWgPerCu * cus / p.nblk), kblocks);
     sblocks = (kblocks + slices - 1) / slices;
     p.ks = (int)(sblocks * 256);
     p.slices = (int)((k + p.ks - 1) / p.ks);
@@ -1507,6 +1604,53 @@ DecodePlan decode_plan_auto(int64_t m, int64_t n, int64_t k, int group)
 }
 
 size_t decode_workspace(const DecodePlan& p) { return p.slices > 1 ? p.part_offset + p.part_bytes : 0; }
+
+// GEMM path (any m): tile shape, ring kernel or register-staged kernel, and
+// the split-K factor.  Launches whose tiles would leave CUs idle (few tiles:
+// small m or small n) split K into nsl slices of kb 128-blocks, so that
+// tiles x nsl fills the CUs; partial tiles are summed by the last arrival as
+// in the decode path.
+constexpr int kGemmMinSliceBlocks = 4;           // no slice shorter than 512 k
+
+struct GemmPlan {
+    bool pipe;      // LDS-ring kernel (else the register-staged kernel)
+    int bm, bn;     // tile
+    bool eight;     // ring kernel with 8 waves (two or more rounds of tiles)
+    int64_t tiles;
+    int nsl, kb;    // split-K slices and 128-blocks per slice (nsl = 1: none)
+    size_t part_offset, part_bytes;
+};
+
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, int group)
+{
+    GemmPlan p{};
+    p.bn = 192;
+    // G = 128 reads scale pairs, which needs an even number of 128-blocks;
+    // the ring kernel addresses its tensors with 32-bit offsets
+    const bool small = m * k * 2 < (1LL << 32) && n * k / 2 < (1LL << 32);
+    p.pipe = k % 128 == 0 && (group != 128 || (k / 128) % 2 == 0) && small;
+    p.bm = (p.pipe && m <= 64) ? 64 : 128;
+    p.tiles = ((n + p.bn - 1) / p.bn) * ((m + p.bm - 1) / p.bm);
+    const int64_t cus = ql::cu_count();
+    p.eight = p.pipe && cus > 0 && p.tiles >= 2 * cus;
+    p.nsl = 1;
+    p.kb = (int)(k / 128);
+    if (p.pipe && cus > 0 && p.tiles < cus) {
+        const int64_t nk = k / 128;
+        const int64_t want = std::min<int64_t>(cus / p.tiles, nk / kGemmMinSliceBlocks);
+        if (want >= 2) {
+            p.kb = (int)((nk + want - 1) / want);
+            p.nsl = (int)((nk + p.kb - 1) / p.kb);
+        }
+    }
+    p.part_offset = kCounterBytes;
+    p.part_bytes = p.nsl > 1 ? (size_t)p.nsl * (size_t)p.tiles * (size_t)std::min<int64_t>(m, p.bm) * (size_t)p.bn *
+                                   sizeof(float)
+                             : 0;
+    return p;
+}
+
+size_t gemm_workspace(const GemmPlan& p) { return p.nsl > 1 ? p.part_offset + p.part_bytes : 0; }
 
 int check_common(const void* qweight, const void* scales, const void* qzeros, int64_t n, int64_t k, int group,
                  const char* who)
@@ -1589,10 +1733,12 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
 
 extern "C" size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group)
 {
-    (void)group;
-    if (m <= 0 || n <= 0 || k <= 0 || m > 32)
+    if (m <= 0 || n <= 0 || k <= 0 || !ql::valid_group(group) || k % group)
         return 0;
-    return decode_workspace(decode_plan_auto(m, n, k, group));
+    const size_t g = gemm_workspace(gemm_plan(m, n, k, group));
+    if (m > 32)
+        return g;
+    return std::max(g, decode_workspace(decode_plan_auto(m, n, k, group)));
 }
 
 extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
@@ -1648,29 +1794,42 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
         return launch_status(who);
     }
     const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
-    // 128 x 192 tiles: M=512, N=12288 gives exactly one tile per CU
-    constexpr int BM = 128, BN = 192;
-    // 4 waves (1 x 4) for launches of one round of tiles; 8 waves (2 x 4, each
-    // weight word dequantised twice, two waves per SIMD) from two rounds on
-    // (M = 2048 fused QKV: 248 us against 260)
-    using Pipe = W4PipeCfg<BM, BN, 1, 3, 4>;
-    using Pipe8 = W4PipeCfg<BM, BN, 2, 3, 4, 8>;
-    const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-    const unsigned grid = (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);   // whole rounds over the XCDs
-    // G = 128 reads scale pairs, which needs an even number of 128-blocks;
-    // the ring kernel addresses its tensors with 32-bit offsets
-    const bool small = m * k * 2 < (1LL << 32) && n * k / 2 < (1LL << 32);
-    const int64_t cus = ql::cu_count();
-    if (k % 128 == 0 && (group != 128 || (k / 128) % 2 == 0) && small && ql::lds_fits(Pipe::kLds)) {
-        if (cus > 0 && tiles >= 2 * cus)
+    // 128 x 192 tiles (M=512, N=12288 gives exactly one tile per CU), 64 x 192
+    // for m <= 64.  4 waves (1 x 4) for launches of one round of tiles; 8
+    // waves (2 x 4, each weight word dequantised twice, two waves per SIMD)
+    // from two rounds on (M = 2048 fused QKV: 248 us against 260)
+    using Pipe = W4PipeCfg<128, 192, 1, 3, 4>;
+    using Pipe8 = W4PipeCfg<128, 192, 2, 3, 4, 8>;
+    using Pipe64 = W4PipeCfg<64, 192, 1, 3, 4>;
+    GemmPlan gp = gemm_plan(m, n, k, group);
+    if (gp.pipe && !ql::lds_fits(gp.eight ? Pipe8::kLds : (gp.bm == 64 ? Pipe64::kLds : Pipe::kLds)))
+        gp = GemmPlan{false, 128, 192, false, ((n + 191) / 192) * ((m + 127) / 128), 1, (int)(k / 128), 0, 0};
+    const size_t need = gemm_workspace(gp);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        QL_FAIL(QL_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !ql::aligned16(workspace))
+        QL_FAIL(QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+    if (gp.part_bytes >= ((size_t)1 << 32))
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: split-K partial sums of %zu bytes (limit 4 GiB)", who, gp.part_bytes);
+    uint32_t* cnt = gp.nsl > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+    float* part = gp.nsl > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gp.part_offset) : nullptr;
+    const int64_t units = gp.tiles * gp.nsl;
+    const unsigned grid = (unsigned)((units + kXcds - 1) / kXcds * kXcds);   // whole rounds over the XCDs
+    if (gp.pipe) {
+        if (gp.eight)
             hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8>), dim3(grid), dim3(Pipe8::NW * 64), (size_t)Pipe8::kLds,
-                               st, xw, qw, scales, qz, y, mi, ni, ki, lg);
+                               st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb, gp.nsl);
+        else if (gp.bm == 64)
+            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe64>), dim3(grid), dim3(Pipe64::NW * 64),
+                               (size_t)Pipe64::kLds, st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb,
+                               gp.nsl);
         else
             hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe>), dim3(grid), dim3(Pipe::NW * 64), (size_t)Pipe::kLds,
-                               st, xw, qw, scales, qz, y, mi, ni, ki, lg);
+                               st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb, gp.nsl);
     }
     else
-        hipLaunchKernelGGL((w4a16_gemm_kernel<BM, BN>), dim3(grid), dim3(256), 0, st, xw, qw, scales, qz, y, mi, ni,
+        hipLaunchKernelGGL((w4a16_gemm_kernel<128, 192>), dim3(grid), dim3(256), 0, st, xw, qw, scales, qz, y, mi, ni,
                            ki, lg);
     return launch_status(who);
 }
@@ -1691,7 +1850,7 @@ extern "C" int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
 // stand-in, not device memory): the device address comes from
 // hipGetSymbolAddress, once per device, and is kept in g_scratch.
 // ---------------------------------------------------------------------------
-constexpr size_t kScratchBytes = (size_t)8 << 20;   // 32 KiB of counters + partial sums
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // 32 KiB of counters + partial sums
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {

@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "weight", "activations", "smoothquant_inputs", "config_weight",
-    "DECODE_M", "C1", "C2_GATEUP", "C2_DOWN", "C3", "C4", "C5_SHAPES",
+    "DECODE_M", "C1", "C2_GATEUP", "C2_DOWN", "C3", "C4", "C5_SHAPES", "C5_M",
 ]
 
 # (N, K, group) of the configurations
@@ -32,6 +32,7 @@ DECODE_M = (1, 4, 8, 16, 32)
 C3 = (12288, 4096, 64)            # LLaMA-7B fused QKV, prefill M=512
 C4 = dict(m=2048, k=4096, n=11008)
 C5_SHAPES = ((13824, 5120), (5120, 13824))   # (N, K) LLaMA-13B MLP up / down
+C5_M = (1, 8, 64, 256, 1024)
 
 
 def weight(rng: np.random.Generator, n: int, k: int, *, base_std: float = 0.02,
