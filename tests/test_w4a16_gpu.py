@@ -234,7 +234,7 @@ def test_gemm_closed_forms(ql, path, group):
 
 
 # One-hot rows through each decode kernel at 128-channel groups: the
-# single-row kernel (m = 1), the 16-row kernel, the 32-row kernel (m = 24) and
+# single-row GEMV kernel (m = 1), the 16-row kernel, the 32-row kernel (m = 24) and
 # six-wave workgroups (9-32 rows, N above 64 channels per CU), with K split
 # into slices where the plan splits it.
 @pytest.mark.parametrize("m,n,k", [(1, 1100, 4224), (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512),
@@ -270,9 +270,10 @@ def test_gemm_empty(ql):
     assert y.shape == (0, 64)
 
 
-# Single-row launches take the resident-activation decode kernel: K split into
-# slices of up to eight 256-blocks whose last block is ragged (4224 = 16 x 256
-# + 128; 4160 = 16 x 256 + 64), a ragged last column block, every group size.
+# Single-row launches take the GEMV kernel (one 16-channel tile per
+# workgroup, K split among its waves and, where the plan says so, across
+# workgroups): a ragged last 256-block (4224 = 16 x 256 + 128; 4160 = 16 x 256
+# + 64), a ragged last tile (1100 = 68 x 16 + 12), every group size.
 @pytest.mark.parametrize("k,group", [(4224, 32), (4224, 64), (4224, 128), (4160, 32), (4160, 64)])
 def test_decode_single_row(ql, k, group):
     n = 1100

@@ -1,11 +1,13 @@
 // W4A16 kernels for gfx950 and their C-ABI entry points.
 //
 //   w4a16_dequant_kernel  -- writes the shared dequantisation routine's output
-//   w4a16_decode_kernel   -- m <= 32: split-K GEMV on MFMA, weights streamed
-//                            from HBM once, dequantised in registers
-//   w4a16_decode_ra_kernel -- the same GEMV for single-row launches, with the
-//                            activations and tables resident in LDS
-//   w4a16_gemm_kernel     -- any m: LDS-tiled fp16 MFMA GEMM
+//   w4a16_decode_kernel   -- 2 <= m <= 32: split-K GEMV on MFMA, weights
+//                            streamed from HBM once, dequantised in registers
+//   w4a16_gemv_kernel     -- m = 1: one 16-channel tile per workgroup, K split
+//                            among its waves, activations and tables in LDS
+//   w4a16_gemm_pipe_kernel -- m > 32: LDS-ring fp16 MFMA GEMM (split-K when
+//                            its tiles would leave CUs idle)
+//   w4a16_gemm_kernel     -- the same for shapes the ring does not cover
 //
 // Weight format (LMDeploy walkthrough, section 2; AUQ page, section 5.4):
 // qweight int32 [n, k/8] with code i of a word at bits [4i, 4i+4), fp16 scales
@@ -322,9 +324,12 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     extern __shared__ uint32_t tab[];              // scale and zero-point tables
     __shared__ int s_last;
 
+    // K slice: blocks [y nkb / S, (y + 1) nkb / S) of the nkb 256-k blocks,
+    // so slices differ by at most one block (KS is the longest)
     const int S = gridDim.y;
-    const int k0 = blockIdx.y * KS;
-    const int kend = min(K, k0 + KS);
+    const int nkb = (K + 255) >> 8;
+    const int k0 = (int)(((int64_t)blockIdx.y * nkb) / S) << 8;
+    const int kend = min(K, (int)(((int64_t)(blockIdx.y + 1) * nkb) / S) << 8);
     const int nch = (kend - k0) >> 3;             // valid chunks of the slice
     const int nb = (kend - k0 + 255) >> 8;        // blocks of this slice
     const int nbp = (nb + P - 1) / P * P;         // blocks streamed, padded to the ring
@@ -590,26 +595,6 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     splitk_finish<TW>(part, cnt, y, M, N, n0, &s_last);
 }
 
-// ---------------------------------------------------------------------------
-// decode with resident activations: m <= MT (written for 16 or 32 rows;
-// single-row launches use it, see the host plan)
-//
-// Workgroup = 4 waves; wave w owns one tile of 16 output channels, so a
-// workgroup covers 64 channels and one K slice of KS <= NB x 256.  The slice's
-// activation rows [0, m) are copied into LDS once, by direct global->LDS loads,
-// alongside the scale and zero-point tables; the weight pieces stream through
-// a register ring of P blocks per wave.  Two barriers (one after the copies,
-// one after each chunk has been reordered in place for the dequantiser) are
-// all the synchronisation: the waves then consume their blocks independently,
-// with no per-block barrier or activation staging.
-//
-// Lanes and MFMAs are laid out as in w4a16_decode_kernel (lane l: channel
-// l % 16, quarter q = l / 16; pieces [4q, 4q+4) and [16+4q, 16+4q+4) of each
-// 32-word block row; interleaved dequantisation).  Activation chunk c (16
-// bytes) of row m is stored at chunk c ^ xswz(m) within its 32-chunk block; a
-// row holds KS / 8 chunks.  Rows >= m are not stored; chunks past the slice's
-// end (a ragged last block) are zeroed in LDS.
-// ---------------------------------------------------------------------------
 // Loads the compiler does not track, for a register ring that must stay in
 // flight across the barrier that publishes LDS: a 16-byte buffer load into
 // registers, a 4-byte buffer load into LDS (at M0 + 4 x lane), and a wait
@@ -655,141 +640,147 @@ __device__ __forceinline__ void ring_wait_n(int n, u4v_t& a, u4v_t& b)
     }
 }
 
-template <int MT, int NB, int P, bool POST>
-__global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
+// ---------------------------------------------------------------------------
+// single-row GEMV (m = 1): one 16-channel tile per workgroup, K split among
+// its KW waves, partial sums added through LDS
+//
+// The decode kernels above give each workgroup several channel tiles and one
+// K slice, and sum the slices across workgroups (split-K: each partial tile
+// is stored, waited for, counted and re-read).  Timestamps of those launches
+// show the weights streaming at the device's copy rate while the blocks are
+// consumed, with the time around that loop -- waiting for the tables and
+// activations with two weight blocks in flight, and the split-K round trips
+// -- costing about as much again.  Here a workgroup owns one tile of 16
+// output channels; wave w streams blocks [w nbs / KW, (w + 1) nbs / KW) of the
+// workgroup's K range, all of them requested (up to P) before the workgroup
+// waits for its tables and activations, and the KW partial sums meet in LDS.
+// Launches whose tiles alone would leave CUs unevenly loaded still split K
+// across workgroups (gridDim.y slices, summed as in the other decode kernels).
+//
+// Lane layout (lane l: channel l % 16, quarter q = l / 16, pieces [4q, 4q+4)
+// and [16+4q, 16+4q+4) of each 32-word block row), MFMAs, interleaved
+// dequantisation and POST scaling: as w4a16_decode_kernel, with one row
+// (every A row reads activation row 0; output rows > 0 are not stored).  LDS: the scale and zero-point tables of the tile's 16 channels for
+// the slice's groups (16 x SD scale dwords from the dword holding the first
+// group, 16 x ZD zero words; both padded to whole 64-entry wave loads), the
+// slice's activation chunks (reordered in place for the interleaved
+// dequantiser, zero past the slice), and KW x 16 floats for the sum.
+// ---------------------------------------------------------------------------
+template <int NB, int P, bool POST, int KW = 4, int P0 = P>
+__global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
+    uint32_t* __restrict__ cnt, int N, int K, int lg, int KS)
 {
     static_assert(NB >= 1 && NB <= 16 && P >= 1 && P <= NB, "the ring waits cover up to 16 blocks");
-    constexpr int TW = 64;
-    constexpr int MTI = MT / 16;
-    constexpr int NJ = POST ? 1 : (MTI >= 4 ? 1 : 4 / MTI);   // accumulator chains
-    // Scale and zero-point tables of the workgroup's channels and slice, as
-    // in DecodeTables (per channel SD scale dwords from the dword holding its
-    // first group, then per channel ZD zero words), each table padded to whole
-    // 256-entry batches: a slice of up to NB blocks has at most 8 NB groups,
-    // so SB and ZB batches hold 64 (4 NB + 1) and 64 (NB + 2) entries.
-    constexpr int SB = NB + 1, ZB = (NB + 5) / 4;
-    constexpr int kZOff = SB * 256;               // first dword of the zero table
-    constexpr int kActOff = (SB + ZB) * 1024;     // byte offset of the activations
-    // a 16-byte element type aligns the dynamic region (placed after the
-    // static s_last) for the 16-byte fragment reads and direct loads
-    extern __shared__ uint4 ra_lds[];
-    uint32_t* const tab = reinterpret_cast<uint32_t*>(ra_lds);
+    constexpr int TW = 16;
+    constexpr int NT = 64 * KW;
+    constexpr int NJ = POST ? 1 : 4;               // accumulator chains
+    extern __shared__ uint4 gv_lds[];              // 16-byte elements: aligned fragment reads
+    uint32_t* const tab = reinterpret_cast<uint32_t*>(gv_lds);
     __shared__ int s_last;
 
-    const int k0 = blockIdx.y * KS;
-    const int kend = min(K, k0 + KS);
-    const int nch = (kend - k0) >> 3;             // valid chunks of the slice
-    const int nb = (kend - k0 + 255) >> 8;        // blocks of this slice (<= NB)
-    const int mrows = M < MT ? M : MT;
-    const int CR = KS >> 3;                       // chunks per stored activation row
-    const int gs = KS >> lg;                      // groups per slice
+    // this workgroup's K range: balanced 256-k blocks of slice blockIdx.y
+    const int nkb = (K + 255) >> 8;
+    const int kb_lo = (int)(((int64_t)blockIdx.y * nkb) / gridDim.y);
+    const int kb_hi = (int)(((int64_t)(blockIdx.y + 1) * nkb) / gridDim.y);
+    const int k0 = kb_lo << 8, kend = min(K, kb_hi << 8);
+    const int nch = (kend - k0) >> 3;             // valid activation chunks
+    const int nbs = kb_hi - kb_lo;
+    const int gs = KS >> lg;                      // groups of the longest slice
+    const int g0 = k0 >> lg;
+    const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
+    const int stot = TW * SD, ztot = TW * ZD;
+    const int spad = (stot + NT - 1) / NT * NT, zpad = (ztot + NT - 1) / NT * NT;   // whole wave loads
+    const int CR = KS >> 3;                       // activation chunks stored
+    const int cpad = (CR + NT - 1) / NT * NT;
+    const uint32_t act_off = (uint32_t)(spad + zpad) * 4u;            // bytes, a multiple of 16
+    const uint32_t red_off = act_off + (uint32_t)cpad * 16u;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int n0 = blockIdx.x * TW;
-    const int KW = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
-    const int g0 = k0 >> lg;
-    const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
+    const int KWD = K >> 3, NG = K >> lg, ZW = (NG + 7) >> 3;
+    const int wb0 = (wave * nbs) / KW, nb = ((wave + 1) * nbs) / KW - wb0;   // this wave's blocks
     const uint32_t lds0 = (uint32_t)(uintptr_t)tab;
 
-    // 1. requests, oldest first, all direct to LDS except the weights: the
-    //    tables (entries clamped into the tensors, so every value is finite),
-    //    the activations, then the first P blocks of weights (blocks past the
-    //    slice re-read block nb - 1, so 2 P loads always follow the others)
+    // 1. requests, oldest first: tables and activations straight to LDS,
+    //    then this wave's first P weight blocks (blocks past its range re-read
+    //    its last block, so 2 P loads always follow the others)
     {
         const uint32_t sbytes = ((uint32_t)N * (uint32_t)NG * 2u + 3u) & ~3u;
         const __amdgpu_buffer_rsrc_t rsc = make_rsrc(sc, sbytes);
         const __amdgpu_buffer_rsrc_t rzr = make_rsrc(qz, (uint32_t)N * (uint32_t)ZW * 4u);
-        const int stot = TW * SD, ztot = TW * ZD;
-        for (int u = 0; u * 256 < stot; ++u) {
-            const int e = min(u * 256 + tid, stot - 1);
+        for (int u = 0; u < spad; u += NT) {
+            const int e = min(u + tid, stot - 1);
             const int rr = e / SD, col = e - rr * SD;
             const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
             const uint32_t dw = min(((row * (uint32_t)NG + (uint32_t)g0) >> 1) + (uint32_t)col, sbytes / 4u - 1u);
-            buf_dma4(rsc, dw * 4u, (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(u * 256 + wave * 64) * 4u));
+            buf_dma4(rsc, dw * 4u, (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(u + wave * 64) * 4u));
         }
-        for (int u = 0; u * 256 < ztot; ++u) {
-            const int e = min(u * 256 + tid, ztot - 1);
+        for (int u = 0; u < zpad; u += NT) {
+            const int e = min(u + tid, ztot - 1);
             const int rr = e / ZD, col = e - rr * ZD;
             const uint32_t row = (uint32_t)min(n0 + rr, N - 1);
             const uint32_t wd = min(row * (uint32_t)ZW + (uint32_t)(g0 >> 3) + (uint32_t)col,
                                     (uint32_t)N * (uint32_t)ZW - 1u);
             buf_dma4(rzr, wd * 4u,
-                     (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(kZOff + u * 256 + wave * 64) * 4u));
+                     (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(spad + u + wave * 64) * 4u));
+        }
+        for (int u = 0; u < cpad; u += NT) {
+            const int c = min(u + tid, nch - 1);
+            ql::dma16s(x, (uint32_t)(k0 + 8 * c) * 2u,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + act_off + (uint32_t)(u + wave * 64) * 16u));
         }
     }
-    {
-        const int total = mrows * CR;
-        const int ninst = (total + 255) >> 8;     // direct loads per wave
-        for (int i = 0; i < ninst; ++i) {
-            const int pos = min((i * 4 + wave) * 64 + lane, total - 1);
-            const int m = pos / CR, cpos = pos - m * CR;
-            const int c = min(cpos ^ xswz(m), nch - 1);
-            const uint32_t off = (uint32_t)(m * K + k0 + 8 * c) * 2u;
-            ql::dma16s(x, off,
-                       (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)kActOff +
-                                                                 (uint32_t)((i * 4 + wave) * 1024)));
-        }
-    }
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KW * 4u);
-    const int nrow = min(n0 + wave * 16 + r16, N - 1);
-    const uint32_t ow = (uint32_t)nrow * (uint32_t)KW * 4u + (uint32_t)(k0 + 32 * q) / 2u;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KWD * 4u);
+    const int nrow = min(n0 + r16, N - 1);
+    const int last = nb > 0 ? nb - 1 : 0;
+    const uint32_t ow = (uint32_t)nrow * (uint32_t)KWD * 4u + (uint32_t)(k0 + 256 * wb0 + 32 * q) / 2u;
     u4v_t ring[P][2];
 #pragma unroll
-    for (int b = 0; b < P; ++b) {
-        const uint32_t bw = ow + (uint32_t)min(b, nb - 1) * 128u;
+    for (int b = 0; b < P0; ++b) {
+        const uint32_t bw = ow + (uint32_t)min(b, last) * 128u;
         ring[b][0] = buf_load16(rw, bw);
         ring[b][1] = buf_load16(rw, bw + 64u);
     }
-    // 2. wait for everything but the weights and publish the tables and the
-    //    activations
-    ql::stage_barrier<2 * P>();
-    // 3. each activation chunk, once: reorder its eight values for the
-    //    interleaved dequantiser (permute_x8), or clear it if it lies past the
-    //    slice's end (a ragged last block, copied from clamped addresses)
+    // 2. wait for everything but those weights and publish the tables and
+    //    the activations (the chunks past the slice's end hold copies of its
+    //    last chunk; the blocks that read them are masked below), then
+    //    request the rest of the ring: issued after the small loads, the
+    //    weight stream does not delay them
+    ql::stage_barrier<2 * P0>();
+#pragma unroll
+    for (int b = P0; b < P; ++b) {
+        const uint32_t bw = ow + (uint32_t)min(b, last) * 128u;
+        ring[b][0] = buf_load16(rw, bw);
+        ring[b][1] = buf_load16(rw, bw + 64u);
+    }
+    // 3. each activation chunk, once: reordered for the interleaved
+    //    dequantiser (13 operations per weight word instead of 16 in natural
+    //    order, which the block loop's issue rate feels), or cleared past the
+    //    slice's end
     {
-        uint4* xw = ra_lds + kActOff / 16;
-        const int used = mrows * CR;
-        for (int e = tid; e < used; e += 256) {
-            const int m = e / CR, cpos = e - m * CR;
-            const int c = (cpos & ~31) + ((cpos & 31) ^ xswz(m));   // logical chunk stored here
-            const bool ok = c < nch;
+        uint4* xw = gv_lds + act_off / 16;
+        for (int e = tid; e < CR; e += NT) {
+            const bool ok = e < nch;
             xw[e] = ql::permute_x8_sel(xw[e], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
         }
         __syncthreads();
     }
 
-    // 4. the slice's blocks, in arrival order
-    const uint4* xs = ra_lds + kActOff / 16;
-    // Rows >= m read row m - 1: an MFMA output row depends on its own A row
-    // only, and output rows >= m are never stored.
-    int arow[MTI][4], hoff[MTI];
-#pragma unroll
-    for (int i = 0; i < MTI; ++i) {
-        const int m = i * 16 + r16;
-        const int mm = m < mrows ? m : mrows - 1;
-        const int f = xswz(mm);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            arow[i][jj] = mm * CR + ((4 * q + jj) ^ (f & 15)) + (f & 16);
-        hoff[i] = (f & 16) ? -16 : 16;
-    }
+    // 4. this wave's blocks
+    const uint4* xs = gv_lds + act_off / 16;
     const int glane = (32 * q) >> lg;
     const int gmax = gs - 1;
-    const int trow = wave * 16 + r16;
-    const int spar = (int)(((uint32_t)min(n0 + trow, N - 1) * (uint32_t)NG + (uint32_t)g0) & 1u);
-    const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + trow * SD);
-    const uint32_t* zrow = tab + kZOff + trow * ZD;
-    f4_t acc[MTI][NJ];
+    const int spar = (int)(((uint32_t)nrow * (uint32_t)NG + (uint32_t)g0) & 1u);
+    const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + r16 * SD);
+    const uint32_t* zrow = tab + spad + r16 * ZD;
+    f4_t acc[NJ];
 #pragma unroll
-    for (int i = 0; i < MTI; ++i)
-#pragma unroll
-        for (int c = 0; c < NJ; ++c)
-            acc[i][c] = f4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NJ; ++c)
+        acc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -798,20 +789,19 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
         ring_wait_n(2 * ((b + P - 1 <= kLast ? b + P - 1 : kLast) - b), rs[0], rs[1]);
         if (b >= nb) {
             if (b + P < NB) {
-                const uint32_t bw = ow + (uint32_t)(nb - 1) * 128u;
+                const uint32_t bw = ow + (uint32_t)last * 128u;
                 rs[0] = buf_load16(rw, bw);
                 rs[1] = buf_load16(rw, bw + 64u);
             }
             continue;
         }
-        uint4 af[8][MTI];
+        const int bb = wb0 + b;                   // block within the slice
+        uint4 af[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < MTI; ++i)
-                af[j][i] = xs[32 * b + arow[i][j & 3] + (j >> 2) * hoff[i]];
-        const int ga = min(((256 * b) >> lg) + glane, gmax);
-        const int gb = min(((256 * b + 128) >> lg) + glane, gmax);
+            af[j] = xs[32 * bb + 16 * (j >> 2) + 4 * q + (j & 3)];
+        const int ga = min(((256 * bb) >> lg) + glane, gmax);
+        const int gb = min(((256 * bb + 128) >> lg) + glane, gmax);
         const uint32_t za_ = (zrow[((g0 + ga) >> 3) - (g0 >> 3)] >> (4 * ((g0 + ga) & 7))) & 0xFu;
         const uint32_t zb_ = (zrow[((g0 + gb) >> 3) - (g0 >> 3)] >> (4 * ((g0 + gb) & 7))) & 0xFu;
         const uint32_t s16a = srow[spar + ga], s16b = srow[spar + gb];
@@ -820,7 +810,7 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
         const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         // the slot's next block, once its words are read
         if (b + P < NB) {
-            const uint32_t bw = ow + (uint32_t)min(b + P, nb - 1) * 128u;
+            const uint32_t bw = ow + (uint32_t)min(b + P, last) * 128u;
             rs[0] = buf_load16(rw, bw);
             rs[1] = buf_load16(rw, bw + 64u);
         }
@@ -837,18 +827,15 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
                 bw[j] = __builtin_bit_cast(h8_t, make_uint4(ql::h2u(d[j][0]), ql::h2u(d[j][1]), ql::h2u(d[j][2]),
                                                             ql::h2u(d[j][3])));
             const float sa = f16_bits_to_f32(s16a), sb = f16_bits_to_f32(s16b);
+            f4_t da = f4_t{0.f, 0.f, 0.f, 0.f}, db = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < MTI; ++i) {
-                f4_t da = f4_t{0.f, 0.f, 0.f, 0.f}, db = f4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    da = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[j], da);
-                    db = mfma16x16x32(__builtin_bit_cast(h8_t, af[4 + j][i]), bw[4 + j], db);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][0][r] = __builtin_fmaf(sb, db[r], __builtin_fmaf(sa, da[r], acc[i][0][r]));
+            for (int j = 0; j < 4; ++j) {
+                da = mfma16x16x32(__builtin_bit_cast(h8_t, af[j]), bw[j], da);
+                db = mfma16x16x32(__builtin_bit_cast(h8_t, af[4 + j]), bw[4 + j], db);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[0][r] = __builtin_fmaf(sb, db[r], __builtin_fmaf(sa, da[r], acc[0][r]));
         } else {
             h2_t s2[8];
 #pragma unroll
@@ -857,48 +844,39 @@ __global__ __launch_bounds__(256, 2) void w4a16_decode_ra_kernel(
             ql::dequant_words<8>(words, zb, s2, bw);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int i = 0; i < MTI; ++i)
-                    acc[i][j % NJ] = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[j], acc[i][j % NJ]);
+                acc[j % NJ] = mfma16x16x32(__builtin_bit_cast(h8_t, af[j]), bw[j], acc[j % NJ]);
         }
     }
-    f4_t res[MTI];
-#pragma unroll
-    for (int i = 0; i < MTI; ++i) {
-        if constexpr (NJ == 4)
-            res[i] = (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
-        else if constexpr (NJ == 2)
-            res[i] = acc[i][0] + acc[i][1];
-        else
-            res[i] = acc[i][0];
-    }
+    f4_t res;
+    if constexpr (NJ == 4)
+        res = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    else
+        res = acc[0];
 
-    const int S = gridDim.y;
-    const int ncol = n0 + wave * 16 + r16;
-    if (S == 1) {
+    // 5. the waves' partial sums of output row 0 (lanes 0-15, element 0) meet
+    //    in LDS and are added in wave order
+    float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(gv_lds) + red_off);
+    if (q == 0)
+        red[wave * TW + r16] = res[0];
+    __syncthreads();
+    float sum = 0.0f;
+    if (tid < TW) {
 #pragma unroll
-        for (int i = 0; i < MTI; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = i * 16 + 4 * q + r;
-                if (m < M && ncol < N)
-                    y[(int64_t)m * N + ncol] = f32_to_f16_bits(res[i][r]);
-            }
+        for (int w = 0; w < KW; ++w)
+            sum += red[w * TW + tid];
+    }
+    const int ncol = n0 + tid;
+    if (gridDim.y == 1) {
+        if (tid < TW && ncol < N)
+            y[ncol] = f32_to_f16_bits(sum);
         return;
     }
-    // 5. split-K: this slice's partial tile with agent-scope stores, then the
+    // 6. split-K across workgroups: this slice's 16 partial sums, then the
     //    arrival and the last arrival's reduction
-    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)M * TW;
-#pragma unroll
-    for (int i = 0; i < MTI; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + 4 * q + r;
-            if (m < M)
-                __hip_atomic_store(&tile[m * TW + wave * 16 + r16], res[i][r], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-    splitk_finish<TW>(part, cnt, y, M, N, n0, &s_last);
+    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)TW;
+    if (tid < TW)
+        __hip_atomic_store(&tile[tid], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    splitk_finish<TW>(part, cnt, y, 1, N, n0, &s_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1165,11 +1143,12 @@ __device__ __forceinline__ void gemm_splitk_finish(float* __restrict__ part, uin
         __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM_, int BN_, int WM_, int S_, int GM_, int NW_ = 4>
+template <int BM_, int BN_, int WM_, int S_, int GM_, int NW_ = 4, int KG_ = 1>
 struct W4PipeCfg {
     static constexpr int BM = BM_, BN = BN_, S = S_, GM = GM_;
     static constexpr int NW = NW_;                     // waves; the first 4 issue the ring loads
-    static constexpr int WM = WM_, WN = NW_ / WM_;     // waves along m and n
+    static constexpr int KG = KG_;                     // wave groups splitting each block's k steps
+    static constexpr int WM = WM_, WN = NW_ / (WM_ * KG_);   // waves along m and n (per group)
     static constexpr int kArow = 256;                  // activation LDS row: 128 fp16
     static constexpr int kBrow = 64;                   // weight LDS row: 16 packed words
     static constexpr int kAbytes = BM * kArow, kBbytes = BN * kBrow;
@@ -1182,8 +1161,8 @@ struct W4PipeCfg {
     static constexpr int DW = (4 * kDwRows + 3) / 4;   // per wave: zero words, scale dwords 0 and 1
     static constexpr int D = DA + DB + DW;
     static_assert(kAbytes % 4096 == 0 && kBbytes % 4096 == 0, "whole 1 KiB loads for every wave");
-    static_assert(WM * WN == NW && (NW == 4 || NW == 8) && BM % (16 * WM) == 0 && BN % (16 * WN) == 0 &&
-                      BN % 64 == 0,
+    static_assert(WM * WN * KG == NW && (NW == 4 || NW == 8) && (KG == 1 || KG == 2) && BM % (16 * WM) == 0 &&
+                      BN % (16 * WN) == 0 && BN % 64 == 0,
                   "4 or 8 waves of 16-row fragments, 64-row tables");
     static_assert(kStageBytes % 256 == 0, "stages keep the 256-byte row bank alignment");
 };
@@ -1203,6 +1182,23 @@ __device__ __forceinline__ void interleave()
     }
 }
 
+
+// The same for MFMAs that each read one A fragment in turn (FJ MFMAs per
+// fragment, then that fragment's refill from LDS), V vector-ALU instructions
+// after each MFMA.
+template <int FI, int FJ, int V>
+__device__ __forceinline__ void interleave_rolling()
+{
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // vector ALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+    }
+}
 
 template <class C>
 __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint16_t* __restrict__ x,
@@ -1237,7 +1233,12 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / C::WN, wn = wave % C::WN;
+    // k group kg takes steps [s0, s0 + NS) of every block; within a group,
+    // wave wl owns sub-tile (wm, wn)
+    constexpr int NS = 4 / C::KG;
+    const int kg = wave / (C::WM * C::WN), wl = wave % (C::WM * C::WN);
+    const int wm = wl / C::WN, wn = wl % C::WN;
+    const int s0 = kg * NS;
     const int q = lane >> 4, r16 = lane & 15;
     const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
     const int NG = K >> lg, ZW = (NG + 7) >> 3;
@@ -1335,7 +1336,14 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const int r = wn * TN + 16 * j + r16;
-            fb[j] = *reinterpret_cast<const uint4*>(base + C::kAbytes + r * C::kBrow + 16 * (q ^ ql::swz64(r)));
+            const uint8_t* wp = base + C::kAbytes + r * C::kBrow + 16 * (q ^ ql::swz64(r));
+            if constexpr (C::KG == 2) {
+                // this group's words 4q + s0 and 4q + s0 + 1 of the chunk
+                const uint2 h = *reinterpret_cast<const uint2*>(wp + 4 * s0);
+                fb[j] = make_uint4(h.x, h.y, 0u, 0u);
+            } else {
+                fb[j] = *reinterpret_cast<const uint4*>(wp);
+            }
             zr[j] = *reinterpret_cast<const uint32_t*>(base + C::kZoff + 4 * r);
             sr[j] = *reinterpret_cast<const uint16_t*>(base + C::kSoff + tbl * 4 * BN + 4 * r + 2 * half);
         }
@@ -1348,7 +1356,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
         for (int j = 0; j < FJ; ++j)
             acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 fa[2][FI], fb[2][FJ];
+    uint4 fa[C::KG == 2 ? 1 : 2][FI], fb[2][FJ];
     uint32_t zr[2][FJ], sr[2][FJ];
     ql::zb_t zb[2][FJ];
     h2_t s2[2][FJ];
@@ -1385,7 +1393,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
     for (int s = 0; s < S; ++s)
         issue(kb_lo + (s < nkl ? s : nkl - 1), s);
     ql::stage_barrier<D * (S - 1)>();   // the slice's first block landed
-    read_a(0, 0, fa[0]);
+    read_a(0, s0, fa[0]);
     read_b(0, kb_lo, fb[0], zr[0], sr[0]);
     set_zs(kb_lo, 0);
     dequant(0, 0, bw[0]);
@@ -1400,10 +1408,10 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
     auto block = [&](int kb, int u) {
         const int slot = u % S, par = u & 1;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < NS; ++st) {
             const int cur = st & 1;
-            if (st < 3) {
-                read_a(slot, st + 1, fa[cur ^ 1]);
+            if (st < NS - 1) {
+                read_a(slot, s0 + st + 1, fa[cur ^ 1]);
                 dequant(par, st + 1, bw[cur ^ 1]);
                 mfmas(cur, 0, FI);
                 interleave<FI, FI * FJ, 3>();
@@ -1411,7 +1419,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
                 ql::stage_barrier<D * (S - 2)>();
                 issue(min(kb + S, kb_hi - 1), slot);
                 read_b((u + 1) % S, kb + 1, fb[par ^ 1], zr[par ^ 1], sr[par ^ 1]);
-                read_a((u + 1) % S, 0, fa[cur ^ 1]);
+                read_a((u + 1) % S, s0, fa[cur ^ 1]);
                 mfmas(cur, 0, FI / 2);
                 set_zs(kb + 1, par ^ 1);
                 dequant(par ^ 1, 0, bw[cur ^ 1]);
@@ -1421,17 +1429,93 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // Two k groups (NS = 2 steps per block and wave): one buffer of A
+    // fragments, each refilled with the next step's fragment right after the
+    // MFMAs that read it, so a wave holds FI fragments instead of 2 FI.
+    auto read_a1 = [&](int slot, int st, int i) -> uint4 {
+        const uint8_t* base = pl + slot * C::kStageBytes;
+        const int r = wm * TM + 16 * i + r16;
+        return *reinterpret_cast<const uint4*>(base + r * C::kArow + 16 * ((4 * q + st) ^ ql::swz256(r)));
+    };
+    auto block_k2 = [&](int kb, int u) {
+        const int slot = u % S, par = u & 1;
+        // step s0: A fragments of step s0 in fa[0], weights in bw[0]
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[i][j] = mfma16x16x32(bw[0][j], __builtin_bit_cast(h8_t, fa[0][i]), acc[i][j]);
+            fa[0][i] = read_a1(slot, s0 + 1, i);
+        }
+        dequant(par, 1, bw[1]);
+        interleave_rolling<FI, FJ, 2>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step s0 + 1: wait for the next block, refill this block's slot, read
+        // the next block's weights and tables, then its step-s0 A fragments
+        ql::stage_barrier<D * (S - 2)>();
+        issue(min(kb + S, kb_hi - 1), slot);
+        read_b((u + 1) % S, kb + 1, fb[par ^ 1], zr[par ^ 1], sr[par ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                acc[i][j] = mfma16x16x32(bw[1][j], __builtin_bit_cast(h8_t, fa[0][i]), acc[i][j]);
+            fa[0][i] = read_a1((u + 1) % S, s0, i);
+        }
+        set_zs(kb + 1, par ^ 1);
+        dequant(par ^ 1, 0, bw[0]);
+        interleave_rolling<FI, FJ, 2>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
     int kb0 = 0;
     for (; kb0 + U <= nkl; kb0 += U) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            block(kb_lo + kb0 + u, u);
+        for (int u = 0; u < U; ++u) {
+            if constexpr (C::KG == 2)
+                block_k2(kb_lo + kb0 + u, u);
+            else
+                block(kb_lo + kb0 + u, u);
+        }
     }
 #pragma unroll
     for (int u = 0; u < U - 1; ++u)
-        if (kb0 + u < nkl)
-            block(kb_lo + kb0 + u, u);
+        if (kb0 + u < nkl) {
+            if constexpr (C::KG == 2)
+                block_k2(kb_lo + kb0 + u, u);
+            else
+                block(kb_lo + kb0 + u, u);
+        }
     ql::stage_barrier<0>();   // drain the trailing reloads; the ring's LDS is free from here
+
+    if constexpr (C::KG == 2) {
+        // group 1 hands its partial sums to group 0 through LDS (lane-major,
+        // 256 bytes per accumulator element and wave); group 0 adds them in
+        // a fixed order and alone stores the tile
+        float* red = reinterpret_cast<float*>(pl);
+        static_assert(C::WM * C::WN * FI * FJ * 4 * 64 * 4 <= C::kLds, "reduction fits in the ring's LDS");
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        red[(((wl * FI + i) * FJ + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[i][j][r] += red[(((wl * FI + i) * FJ + j) * 4 + r) * 64 + lane];
+        }
+        __syncthreads();
+    }
+    const bool storer = kg == 0;
 
     if (nsl > 1) {
         // this slice's partial tile (rows < M), then the split-K completion;
@@ -1444,7 +1528,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
             for (int j = 0; j < FJ; ++j) {
                 const int ml = wm * TM + i * 16 + r16;
                 const int nl = wn * TN + j * 16 + 4 * q;
-                if (m0 + ml < M)
+                if (storer && m0 + ml < M)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         __hip_atomic_store(&tp[ml * BN + nl + r], acc[i][j][r], __ATOMIC_RELAXED,
@@ -1454,6 +1538,8 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
         return;
     }
 
+    if (!storer)
+        return;
     // lane (q, r16) holds y[m][n .. n+3] of fragment (i, j)
     const bool vec = m0 + BM <= M && n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
@@ -1481,17 +1567,16 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 // host side
 // ---------------------------------------------------------------------------
 struct DecodePlan {
-    bool ra;    // resident-activation kernel (else the streamed one)
+    bool gemv;  // single-row GEMV kernel (one 16-channel tile per workgroup; else the streamed one)
     int mt;     // 16 or 32
     int t;      // waves per workgroup (streamed kernel: 4 or 6)
     int r;      // 16-channel tiles per wave
-    int p;      // blocks in flight per wave (resident kernel: most blocks per slice)
+    int p;      // blocks in flight per wave (GEMV kernel: most blocks per wave)
     bool post;  // group scale applied to the fp32 MFMA result (128-channel groups)
     int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
     size_t lds_bytes;   // dynamic LDS bytes
-    size_t act_off;     // resident kernel: byte offset of the activations in LDS
     size_t part_offset, part_bytes;
 };
 
@@ -1536,67 +1621,71 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     const int64_t waves = (int64_t)p.nblk * p.t;
     const int64_t target = (m > 8 && (waves >= kDecodeWaveMin || p.t == 6)) ? waves : kDecodeWaveTarget;
     int64_t slices = std::min<int64_t>((target + waves - 1) / waves, kblocks);
-    const int64_t sblocks = (kblocks + slices - 1) / slices;
+    const int64_t sblocks = (kblocks + slices - 1) / slices;   // the longest balanced slice
     p.ks = (int)(sblocks * 256);
     p.lds_bytes = decode_tables(sblocks, tw, group);
-    p.slices = (int)((k + p.ks - 1) / p.ks);
+    p.slices = (int)slices;
     p.part_offset = kCounterBytes;
     // partial tiles [slices][nblk][m][64 r] fp32
     p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)tw * sizeof(float) : 0;
     return p;
 }
 
-// Resident-activation plan (single-row launches): a slice holds at most
-// kRaBlocks blocks of 256 k and at most kRaActBytes of activation rows;
-// kRaRing blocks of weights are in flight per wave.  Measured on the LLaMA-7B
-// MLP decode shapes (G = 128): at m = 1 it beats the streamed kernel (fused
-// gate/up 13.6 against 15.5 us, down 10.4 against 10.6 us); from m = 4 on the
-// streamed kernel is as fast or faster (it splits K less and stages smaller
-// activation slices), so only m = 1 takes this path.
-constexpr int kRaBlocks = 8, kRaRing = 2;
-constexpr int64_t kRaActBytes = 65536;
-constexpr int64_t kRaMaxM = 1;
-// K is split further, up to this many workgroups per CU in all, when the
-// column blocks alone would leave CUs idle (q_proj: 64 column blocks).
-constexpr int64_t kRaWgPerCu = 1;
+// Single-row GEMV plan: one workgroup of kGemvWaves waves per 16-channel
+// tile; K split across workgroups (sg slices) only where that evens out the
+// load per CU by more than the cross-workgroup sum costs (taken as 15%).
+constexpr int kGemvWaves = 4;
+constexpr int kGemvEarlyBlocks = 2;              // weight blocks requested before the tables and activations land
+constexpr int kGemvMaxWaveBlocks = 16;
+constexpr int64_t kGemvMaxActBytes = 65536;
 
-DecodePlan decode_plan_ra(int64_t m, int64_t n, int64_t k, int group)
+DecodePlan decode_plan_gemv(int64_t n, int64_t k, int group)
 {
     DecodePlan p{};
-    p.ra = true;
+    p.gemv = true;
     p.mt = 16;
-    p.t = 4;
-    p.r = 1;
-    p.p = kRaBlocks;
     p.post = group == 128;
-    p.nblk = (int)((n + 63) / 64);
+    p.nblk = (int)((n + 15) / 16);
     const int64_t kblocks = (k + 255) / 256;
-    const int64_t mrows = std::min<int64_t>(m, p.mt);
-    int64_t sblocks = std::min<int64_t>(std::min<int64_t>(p.p, std::max<int64_t>(1, kRaActBytes / (mrows * 512))),
-                                        kblocks);
-    int64_t slices = (kblocks + sblocks - 1) / sblocks;
+    int64_t sg_min = 1;
+    while ((kblocks + sg_min - 1) / sg_min > (int64_t)kGemvWaves * kGemvMaxWaveBlocks ||
+           (kblocks + sg_min - 1) / sg_min * 512 > kGemvMaxActBytes)
+        ++sg_min;
+    int64_t sg = sg_min;
     const int64_t cus = ql::cu_count();
-    if (cus > 0)
-        slices = std::min<int64_t>(std::max<int64_t>(slices, kRaWgPerCu * cus / p.nblk), kblocks);
-    sblocks = (kblocks + slices - 1) / slices;
+    if (cus > 0) {
+        double best = 1e30;
+        for (int64_t s2 = sg_min; s2 <= std::min<int64_t>(4 * sg_min, kblocks); ++s2) {
+            const double load = (double)((p.nblk * s2 + cus - 1) / cus) / (double)s2 * (s2 > 1 ? 1.15 : 1.0);
+            if (load < best - 1e-9) {
+                best = load;
+                sg = s2;
+            }
+        }
+    }
+    p.slices = (int)sg;
+    const int64_t sblocks = (kblocks + sg - 1) / sg;               // the longest slice
     p.ks = (int)(sblocks * 256);
-    p.slices = (int)((k + p.ks - 1) / p.ks);
-    // tables padded to whole batches (see the kernel), then the activation rows
-    // in whole 4 KiB rounds of direct loads
-    const size_t tables = (size_t)((p.p + 1) + (p.p + 5) / 4) * 1024;     // kernel's batch layout
-    const size_t act = (size_t)((mrows * sblocks * 32 + 255) / 256) * 4096;
-    p.act_off = tables;
-    p.lds_bytes = tables + act;
+    const int64_t wave_blocks = (sblocks + kGemvWaves - 1) / kGemvWaves;
+    p.p = wave_blocks <= 4 ? 4 : (wave_blocks <= 8 ? 8 : 16);      // blocks unrolled per wave
+    // LDS: the kernel's layout (tables padded to whole wave loads, the
+    // activation chunks, the partial sums)
+    const int64_t nt = 64 * kGemvWaves;
+    const int64_t gs = (int64_t)p.ks / group;
+    const int64_t stot = 16 * ((gs >> 1) + 1), ztot = 16 * ((gs >> 3) + 2);
+    const int64_t spad = (stot + nt - 1) / nt * nt, zpad = (ztot + nt - 1) / nt * nt;
+    const int64_t cpad = (p.ks / 8 + nt - 1) / nt * nt;
+    p.lds_bytes = (size_t)((spad + zpad) * 4 + cpad * 16 + kGemvWaves * 16 * 4);
     p.part_offset = kCounterBytes;
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * 64 * sizeof(float) : 0;
+    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * 16 * sizeof(float) : 0;
     return p;
 }
 
 // Kernel choice by m (measured on the MLP decode shapes).
 DecodePlan decode_plan_auto(int64_t m, int64_t n, int64_t k, int group)
 {
-    if (m <= kRaMaxM) {
-        DecodePlan p = decode_plan_ra(m, n, k, group);
+    if (m == 1) {
+        DecodePlan p = decode_plan_gemv(n, k, group);
         if (ql::lds_fits(p.lds_bytes))
             return p;
     }
@@ -1611,6 +1700,7 @@ size_t decode_workspace(const DecodePlan& p) { return p.slices > 1 ? p.part_offs
 // tiles x nsl fills the CUs; partial tiles are summed by the last arrival as
 // in the decode path.
 constexpr int kGemmMinSliceBlocks = 4;           // no slice shorter than 512 k
+constexpr bool kGemmKGroups = true;              // one-round launches: 8 waves in two k groups
 
 struct GemmPlan {
     bool pipe;      // LDS-ring kernel (else the register-staged kernel)
@@ -1632,7 +1722,10 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, int group)
     p.bm = (p.pipe && m <= 64) ? 64 : 128;
     p.tiles = ((n + p.bn - 1) / p.bn) * ((m + p.bm - 1) / p.bm);
     const int64_t cus = ql::cu_count();
-    p.eight = p.pipe && cus > 0 && p.tiles >= 2 * cus;
+    // 8 waves (2 x 4) for 128-row tiles: one wave per SIMD is not enough to
+    // keep the matrix cores fed (13B MLP, M=256: 74 -> 65 us; fused QKV M=512
+    // unchanged at ~63 us)
+    p.eight = p.pipe && p.bm == 128;
     p.nsl = 1;
     p.kb = (int)(k / 128);
     if (p.pipe && cus > 0 && p.tiles < cus) {
@@ -1687,32 +1780,31 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
                        st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
 }
 
-// Exact dispatch on the plan; returns false for a combination that is not
-// instantiated.
-template <int MT, int NB, int P, bool POST>
-void launch_decode_ra_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
-                        const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
+template <int NB, int P, bool POST>
+void launch_gemv_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
+                   const uint32_t* qz, uint16_t* y, void* ws, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_ra_kernel<MT, NB, P, POST>), dim3(p.nblk, p.slices), dim3(256), p.lds_bytes, st,
-                       x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+    hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, kGemvWaves, (kGemvEarlyBlocks < P ? kGemvEarlyBlocks : P)>),
+                       dim3(p.nblk, p.slices), dim3(64 * kGemvWaves),
+                       p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, n, k, lg, p.ks);
 }
 
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                    const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
-    if (p.ra) {
-#define QL_DECODE_RA_CASE(MT_, NB_, P_)                                                          \
-    if (p.mt == MT_ && p.p == NB_) {                                                             \
-        if (p.post)                                                                              \
-            launch_decode_ra_t<MT_, NB_, P_, true>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
-        else                                                                                     \
-            launch_decode_ra_t<MT_, NB_, P_, false>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
-        return true;                                                                             \
+    if (p.gemv) {
+#define QL_GEMV_CASE(NB_, P_)                                                         \
+    if (p.p == NB_) {                                                                 \
+        if (p.post)                                                                   \
+            launch_gemv_t<NB_, P_, true>(p, x, qw, sc, qz, y, ws, n, k, lg, st);      \
+        else                                                                          \
+            launch_gemv_t<NB_, P_, false>(p, x, qw, sc, qz, y, ws, n, k, lg, st);     \
+        return true;                                                                  \
     }
-        QL_DECODE_RA_CASE(16, kRaBlocks, kRaRing)
-#undef QL_DECODE_RA_CASE
+        QL_GEMV_CASE(4, 4) QL_GEMV_CASE(8, 8) QL_GEMV_CASE(16, 8)
+#undef QL_GEMV_CASE
         return false;
     }
 
@@ -1801,6 +1893,9 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     using Pipe = W4PipeCfg<128, 192, 1, 3, 4>;
     using Pipe8 = W4PipeCfg<128, 192, 2, 3, 4, 8>;
     using Pipe64 = W4PipeCfg<64, 192, 1, 3, 4>;
+    // the same tiles with 8 waves in two k groups (two waves per SIMD, each
+    // weight word still dequantised once)
+    using Pipe64K = W4PipeCfg<64, 192, 1, 3, 4, 8, 2>;
     GemmPlan gp = gemm_plan(m, n, k, group);
     if (gp.pipe && !ql::lds_fits(gp.eight ? Pipe8::kLds : (gp.bm == 64 ? Pipe64::kLds : Pipe::kLds)))
         gp = GemmPlan{false, 128, 192, false, ((n + 191) / 192) * ((m + 127) / 128), 1, (int)(k / 128), 0, 0};
@@ -1820,6 +1915,10 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
         if (gp.eight)
             hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8>), dim3(grid), dim3(Pipe8::NW * 64), (size_t)Pipe8::kLds,
                                st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb, gp.nsl);
+        else if (gp.bm == 64 && kGemmKGroups)
+            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe64K>), dim3(grid), dim3(Pipe64K::NW * 64),
+                               (size_t)Pipe64K::kLds, st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb,
+                               gp.nsl);
         else if (gp.bm == 64)
             hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe64>), dim3(grid), dim3(Pipe64::NW * 64),
                                (size_t)Pipe64::kLds, st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb,
