@@ -98,6 +98,9 @@ def parse():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter files of a --profile-launch run "
                          "into the traffic record bench.py reads, and print a summary")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print a markdown table of a rocprofv3 --kernel-trace CSV: calls, average, minimum and "
+                         "maximum duration per kernel and grid")
     return ap.parse_args()
 
 
@@ -157,6 +160,9 @@ def main():
     args = parse()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -516,7 +522,7 @@ def cpu_baseline(host, shapes, launches, rows_opt, log):
         total_bytes += w4a16_bytes(m, n, k, g) * (rows_per / n)
     log(f"[bench] cpu baseline: {total_s:.2f} s for up to {rows_per_opt} channels per launch")
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"one step (10 launches), min({rows_per_opt}, N) evenly spaced output channels per launch, "
+            "sample": f"one step ({len(launches)} launches), min({rows_per_opt}, N) evenly spaced output channels per launch, "
                       f"{total_s:.1f} s of oracle time"}
 
 
@@ -609,7 +615,8 @@ def traffic_summary(fetch_csv, write_csv):
     def median(v):
         return float(np.median(v)) if v else float("nan")
 
-    dec_f, dec_w = pick(fetch, "w4a16_decode"), pick(write, "w4a16_decode")
+    dec_f = pick(fetch, "w4a16_decode") + pick(fetch, "w4a16_gemv")
+    dec_w = pick(write, "w4a16_decode") + pick(write, "w4a16_gemv")
     cp_f, cp_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")
     if not (dec_f and dec_w and cp_f and cp_w):
         raise SystemExit("counter files lack the decode kernel or the calibration copy")
@@ -629,7 +636,7 @@ def traffic_summary(fetch_csv, write_csv):
                 meta = json.loads(lines[-1])
             break
     rec = {"source_hash": meta.get("source_hash", kernel_source_hash()), "shape": meta.get("shape"),
-           "kernel": sorted({name for (_, name) in fetch if "w4a16_decode" in name}),
+           "kernel": sorted({name for (_, name) in fetch if "w4a16_decode" in name or "w4a16_gemv" in name}),
            "bytes_per_launch": round(fetch_b + write_b), "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "algorithmic_bytes": meta.get("bytes_per_launch"),
            "fetch_kib_raw": median(dec_f), "write_kib_raw": median(dec_w),
@@ -649,6 +656,28 @@ def traffic_summary(fetch_csv, write_csv):
     print(f"| decode HBM bytes per launch (fetch + write) | {fetch_b + write_b:,.0f} |")
     if alg:
         print(f"| algorithmic bytes per launch | {alg:,} (traffic / algorithmic = {(fetch_b + write_b) / alg:.3f}) |")
+
+
+def trace_summary(path):
+    """Kernel durations of a rocprofv3 --kernel-trace CSV, grouped by kernel
+    name and grid, largest total time first."""
+    import csv
+    import re
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            name = re.sub(r"\(anonymous namespace\)::", "", name)
+            name = re.sub(r"\(.*$", "", name) if "<" not in name else name[:name.rfind(">") + 1]
+            grid = f"{r['Grid_Size_X']}x{r['Grid_Size_Y']}"
+            lds = next((r[c] for c in ("LDS_Block_Size", "Group_Segment_Size", "Lds_Size") if c in r), "")
+            key = (name, grid, r["Workgroup_Size_X"], lds)
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups.setdefault(key, []).append(dur)
+    print("| kernel | grid (threads) | workgroup | LDS bytes | calls | avg us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (name, grid, wg, lds), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {name} | {grid} | {wg} | {lds} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
 
 
 if __name__ == "__main__":
