@@ -237,8 +237,8 @@ def test_gemm_closed_forms(ql, path, group):
 # single-row GEMV kernel (m = 1), the 16-row kernel, the 32-row kernel (m = 24) and
 # six-wave workgroups (9-32 rows, N above 64 channels per CU), with K split
 # into slices where the plan splits it.
-@pytest.mark.parametrize("m,n,k", [(1, 1100, 4224), (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512),
-                                   (32, 20000, 512)])
+@pytest.mark.parametrize("m,n,k", [(1, 1100, 4224), (2, 1100, 4224), (3, 300, 11008), (3, 5120, 13824),
+                                   (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512), (32, 20000, 512)])
 def test_decode_one_hot_bit_exact_group128(ql, m, n, k):
     group = 128
     rng = np.random.default_rng(m + n + k)
@@ -270,16 +270,22 @@ def test_gemm_empty(ql):
     assert y.shape == (0, 64)
 
 
-# Single-row launches take the GEMV kernel (one 16-channel tile per
+# Launches of 1-3 rows take the GEMV kernel (one 16-channel tile per
 # workgroup, K split among its waves and, where the plan says so, across
 # workgroups): a ragged last 256-block (4224 = 16 x 256 + 128; 4160 = 16 x 256
-# + 64), a ragged last tile (1100 = 68 x 16 + 12), every group size.
-@pytest.mark.parametrize("k,group", [(4224, 32), (4224, 64), (4224, 128), (4160, 32), (4160, 64)])
-def test_decode_single_row(ql, k, group):
-    n = 1100
-    rng = np.random.default_rng(k + group)
+# + 64), a ragged last tile (1100 = 68 x 16 + 12), every group size; K split
+# across workgroups because the activation rows exceed their LDS budget
+# (3 x 20480 fp16) or because the tiles alone load the CUs unevenly (320 tiles
+# for N = 5120).
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("n,k,group", [(1100, 4224, 32), (1100, 4224, 64), (1100, 4224, 128), (1100, 4160, 32),
+                                       (1100, 4160, 64), (600, 20480, 128), (5120, 13824, 32)])
+def test_decode_gemv(ql, m, n, k, group):
+    if k >= 13824:
+        assert ql.w4a16_workspace_bytes(m, n, k, group) > 0, "expected K split across workgroups"
+    rng = np.random.default_rng(k + group + 7 * m)
     w = workloads.weight(rng, n, k)
-    x = workloads.activations(rng, 1, k)
+    x = workloads.activations(rng, m, k)
     (qw, sc, qz), d = pack_dev(ql, w, group)
     y1 = ql.w4a16_gemm(dev(x), *d, group, path=1)
     y2 = ql.w4a16_gemm(dev(x), *d, group, path=1)

@@ -1,9 +1,9 @@
 // W4A16 kernels for gfx950 and their C-ABI entry points.
 //
 //   w4a16_dequant_kernel  -- writes the shared dequantisation routine's output
-//   w4a16_decode_kernel   -- 2 <= m <= 32: split-K GEMV on MFMA, weights
+//   w4a16_decode_kernel   -- 4 <= m <= 32: split-K GEMV on MFMA, weights
 //                            streamed from HBM once, dequantised in registers
-//   w4a16_gemv_kernel     -- m = 1: one 16-channel tile per workgroup, K split
+//   w4a16_gemv_kernel     -- m <= 3: one 16-channel tile per workgroup, K split
 //                            among its waves, activations and tables in LDS
 //   w4a16_gemm_pipe_kernel -- m > 32: LDS-ring fp16 MFMA GEMM (split-K when
 //                            its tiles would leave CUs idle)
@@ -641,8 +641,8 @@ __device__ __forceinline__ void ring_wait_n(int n, u4v_t& a, u4v_t& b)
 }
 
 // ---------------------------------------------------------------------------
-// single-row GEMV (m = 1): one 16-channel tile per workgroup, K split among
-// its KW waves, partial sums added through LDS
+// GEMV (m <= 3): one 16-channel tile per workgroup, K split among its KW
+// waves, partial sums added through LDS
 //
 // The decode kernels above give each workgroup several channel tiles and one
 // K slice, and sum the slices across workgroups (split-K: each partial tile
@@ -659,20 +659,24 @@ __device__ __forceinline__ void ring_wait_n(int n, u4v_t& a, u4v_t& b)
 //
 // Lane layout (lane l: channel l % 16, quarter q = l / 16, pieces [4q, 4q+4)
 // and [16+4q, 16+4q+4) of each 32-word block row), MFMAs, interleaved
-// dequantisation and POST scaling: as w4a16_decode_kernel, with one row
-// (every A row reads activation row 0; output rows > 0 are not stored).  LDS: the scale and zero-point tables of the tile's 16 channels for
-// the slice's groups (16 x SD scale dwords from the dword holding the first
-// group, 16 x ZD zero words; both padded to whole 64-entry wave loads), the
-// slice's activation chunks (reordered in place for the interleaved
-// dequantiser, zero past the slice), and KW x 16 floats for the sum.
+// dequantisation and POST scaling: as w4a16_decode_kernel, with M <= MR rows
+// (A row r reads activation row min(r, M - 1); output rows >= M are not
+// stored; MR = 1 compiles the single-row case without the other rows' work).  LDS: the scale and zero-point tables of the tile's 16 channels
+// for the slice's groups (16 x SD scale dwords from the dword holding the
+// first group, 16 x ZD zero words; both padded to whole 64-entry wave loads),
+// the slice's activation chunks of each row (reordered in place for the
+// interleaved dequantiser, zero past the slice; rows 64 bytes apart in the
+// banks), and KW x MR x 16 floats for the sum.
 // ---------------------------------------------------------------------------
-template <int NB, int P, bool POST, int KW = 4, int P0 = P>
+template <int NB, int P, bool POST, int MR, int KW = 4, int P0 = P>
 __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int N, int K, int lg, int KS)
+    uint32_t* __restrict__ cnt, int m_rows, int N, int K, int lg, int KS)
 {
     static_assert(NB >= 1 && NB <= 16 && P >= 1 && P <= NB, "the ring waits cover up to 16 blocks");
+    static_assert(MR >= 1 && MR <= 4, "up to four rows (lanes 0-15 hold output rows 0-3)");
+    const int M = MR == 1 ? 1 : m_rows;            // 1 <= M <= MR
     constexpr int TW = 16;
     constexpr int NT = 64 * KW;
     constexpr int NJ = POST ? 1 : 4;               // accumulator chains
@@ -692,10 +696,14 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     const int SD = (gs >> 1) + 1, ZD = (gs >> 3) + 2;
     const int stot = TW * SD, ztot = TW * ZD;
     const int spad = (stot + NT - 1) / NT * NT, zpad = (ztot + NT - 1) / NT * NT;   // whole wave loads
-    const int CR = KS >> 3;                       // activation chunks stored
+    const int CR = KS >> 3;                       // activation chunks stored per row
     const int cpad = (CR + NT - 1) / NT * NT;
+    // row stride: whole wave loads plus 4 chunks, so rows sit 64 bytes apart
+    // in the LDS banks and the lanes of different rows reading the same chunk
+    // do not conflict
+    const int CRS = MR == 1 ? cpad : cpad + 4;
     const uint32_t act_off = (uint32_t)(spad + zpad) * 4u;            // bytes, a multiple of 16
-    const uint32_t red_off = act_off + (uint32_t)cpad * 16u;
+    const uint32_t red_off = act_off + (uint32_t)(M * CRS) * 16u;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -728,11 +736,13 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
             buf_dma4(rzr, wd * 4u,
                      (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(spad + u + wave * 64) * 4u));
         }
-        for (int u = 0; u < cpad; u += NT) {
-            const int c = min(u + tid, nch - 1);
-            ql::dma16s(x, (uint32_t)(k0 + 8 * c) * 2u,
-                       (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + act_off + (uint32_t)(u + wave * 64) * 16u));
-        }
+        for (int r = 0; r < M; ++r)
+            for (int u = 0; u < cpad; u += NT) {
+                const int c = min(u + tid, nch - 1);
+                ql::dma16s(x, (uint32_t)(r * K + k0 + 8 * c) * 2u,
+                           (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + act_off +
+                                                                    (uint32_t)(r * CRS + u + wave * 64) * 16u));
+            }
     }
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(qw, (uint32_t)N * (uint32_t)KWD * 4u);
     const int nrow = min(n0 + r16, N - 1);
@@ -762,16 +772,18 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     //    order, which the block loop's issue rate feels), or cleared past the
     //    slice's end
     {
-        uint4* xw = gv_lds + act_off / 16;
-        for (int e = tid; e < CR; e += NT) {
-            const bool ok = e < nch;
-            xw[e] = ql::permute_x8_sel(xw[e], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
+        for (int r = 0; r < M; ++r) {
+            uint4* xw = gv_lds + act_off / 16 + r * CRS;
+            for (int e = tid; e < CR; e += NT) {
+                const bool ok = e < nch;
+                xw[e] = ql::permute_x8_sel(xw[e], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
+            }
         }
         __syncthreads();
     }
 
     // 4. this wave's blocks
-    const uint4* xs = gv_lds + act_off / 16;
+    const uint4* xs = gv_lds + act_off / 16 + min(r16, M - 1) * CRS;   // this lane's A row
     const int glane = (32 * q) >> lg;
     const int gmax = gs - 1;
     const int spar = (int)(((uint32_t)nrow * (uint32_t)NG + (uint32_t)g0) & 1u);
@@ -853,30 +865,35 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     else
         res = acc[0];
 
-    // 5. the waves' partial sums of output row 0 (lanes 0-15, element 0) meet
-    //    in LDS and are added in wave order
+    // 5. the waves' partial tiles of output rows 0 .. M-1 (lanes 0-15 hold
+    //    rows 0-3) meet in LDS and are added in wave order
     float* red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(gv_lds) + red_off);
-    if (q == 0)
-        red[wave * TW + r16] = res[0];
+    if (q == 0) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+            if (r < M)
+                red[(wave * MR + r) * TW + r16] = res[r];
+    }
     __syncthreads();
+    const int rr = tid >> 4, cc = tid & 15;       // output row and channel of this thread
     float sum = 0.0f;
-    if (tid < TW) {
+    if (rr < M) {
 #pragma unroll
         for (int w = 0; w < KW; ++w)
-            sum += red[w * TW + tid];
+            sum += red[(w * MR + rr) * TW + cc];
     }
-    const int ncol = n0 + tid;
+    const int ncol = n0 + cc;
     if (gridDim.y == 1) {
-        if (tid < TW && ncol < N)
-            y[ncol] = f32_to_f16_bits(sum);
+        if (rr < M && ncol < N)
+            y[(int64_t)rr * N + ncol] = f32_to_f16_bits(sum);
         return;
     }
-    // 6. split-K across workgroups: this slice's 16 partial sums, then the
-    //    arrival and the last arrival's reduction
-    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)TW;
-    if (tid < TW)
-        __hip_atomic_store(&tile[tid], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    splitk_finish<TW>(part, cnt, y, 1, N, n0, &s_last);
+    // 6. split-K across workgroups: this slice's M x 16 partial tile, then
+    //    the arrival and the last arrival's reduction
+    float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)(M * TW);
+    if (rr < M)
+        __hip_atomic_store(&tile[rr * TW + cc], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    splitk_finish<TW>(part, cnt, y, M, N, n0, &s_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1567,7 +1584,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 // host side
 // ---------------------------------------------------------------------------
 struct DecodePlan {
-    bool gemv;  // single-row GEMV kernel (one 16-channel tile per workgroup; else the streamed one)
+    bool gemv;  // GEMV kernel, m <= 3 (one 16-channel tile per workgroup; else the streamed one)
     int mt;     // 16 or 32
     int t;      // waves per workgroup (streamed kernel: 4 or 6)
     int r;      // 16-channel tiles per wave
@@ -1631,15 +1648,17 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     return p;
 }
 
-// Single-row GEMV plan: one workgroup of kGemvWaves waves per 16-channel
-// tile; K split across workgroups (sg slices) only where that evens out the
-// load per CU by more than the cross-workgroup sum costs (taken as 15%).
+// GEMV plan (m <= kGemvMaxRows): one workgroup of kGemvWaves waves per
+// 16-channel tile; K split across workgroups (sg slices) only where that
+// evens out the load per CU by more than the cross-workgroup sum costs (taken
+// as 15%), or where the slice's activation rows would not fit their budget.
 constexpr int kGemvWaves = 4;
 constexpr int kGemvEarlyBlocks = 2;              // weight blocks requested before the tables and activations land
 constexpr int kGemvMaxWaveBlocks = 16;
-constexpr int64_t kGemvMaxActBytes = 65536;
+constexpr int64_t kGemvMaxActBytes = 98304;
+constexpr int kGemvMaxRows = 3;
 
-DecodePlan decode_plan_gemv(int64_t n, int64_t k, int group)
+DecodePlan decode_plan_gemv(int64_t m, int64_t n, int64_t k, int group)
 {
     DecodePlan p{};
     p.gemv = true;
@@ -1649,7 +1668,7 @@ DecodePlan decode_plan_gemv(int64_t n, int64_t k, int group)
     const int64_t kblocks = (k + 255) / 256;
     int64_t sg_min = 1;
     while ((kblocks + sg_min - 1) / sg_min > (int64_t)kGemvWaves * kGemvMaxWaveBlocks ||
-           (kblocks + sg_min - 1) / sg_min * 512 > kGemvMaxActBytes)
+           (kblocks + sg_min - 1) / sg_min * 512 * m > kGemvMaxActBytes)
         ++sg_min;
     int64_t sg = sg_min;
     const int64_t cus = ql::cu_count();
@@ -1675,17 +1694,18 @@ DecodePlan decode_plan_gemv(int64_t n, int64_t k, int group)
     const int64_t stot = 16 * ((gs >> 1) + 1), ztot = 16 * ((gs >> 3) + 2);
     const int64_t spad = (stot + nt - 1) / nt * nt, zpad = (ztot + nt - 1) / nt * nt;
     const int64_t cpad = (p.ks / 8 + nt - 1) / nt * nt;
-    p.lds_bytes = (size_t)((spad + zpad) * 4 + cpad * 16 + kGemvWaves * 16 * 4);
+    const int64_t mr = m > 1 ? kGemvMaxRows : 1;
+    p.lds_bytes = (size_t)((spad + zpad) * 4 + m * (cpad + (m > 1 ? 4 : 0)) * 16 + kGemvWaves * mr * 16 * 4);
     p.part_offset = kCounterBytes;
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * 16 * sizeof(float) : 0;
+    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * 16 * sizeof(float) : 0;
     return p;
 }
 
 // Kernel choice by m (measured on the MLP decode shapes).
 DecodePlan decode_plan_auto(int64_t m, int64_t n, int64_t k, int group)
 {
-    if (m == 1) {
-        DecodePlan p = decode_plan_gemv(n, k, group);
+    if (m <= kGemvMaxRows) {
+        DecodePlan p = decode_plan_gemv(m, n, k, group);
         if (ql::lds_fits(p.lds_bytes))
             return p;
     }
@@ -1782,13 +1802,20 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
 
 template <int NB, int P, bool POST>
 void launch_gemv_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
-                   const uint32_t* qz, uint16_t* y, void* ws, int n, int k, int lg, hipStream_t st)
+                   const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
-    hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, kGemvWaves, (kGemvEarlyBlocks < P ? kGemvEarlyBlocks : P)>),
+    constexpr int P0 = kGemvEarlyBlocks < P ? kGemvEarlyBlocks : P;
+    if (m > 1) {
+        hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, kGemvMaxRows, kGemvWaves, P0>),
+                           dim3(p.nblk, p.slices), dim3(64 * kGemvWaves),
+                           p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+        return;
+    }
+    hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, 1, kGemvWaves, P0>),
                        dim3(p.nblk, p.slices), dim3(64 * kGemvWaves),
-                       p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, n, k, lg, p.ks);
+                       p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
 }
 
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
@@ -1798,9 +1825,9 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
 #define QL_GEMV_CASE(NB_, P_)                                                         \
     if (p.p == NB_) {                                                                 \
         if (p.post)                                                                   \
-            launch_gemv_t<NB_, P_, true>(p, x, qw, sc, qz, y, ws, n, k, lg, st);      \
+            launch_gemv_t<NB_, P_, true>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
         else                                                                          \
-            launch_gemv_t<NB_, P_, false>(p, x, qw, sc, qz, y, ws, n, k, lg, st);     \
+            launch_gemv_t<NB_, P_, false>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);  \
         return true;                                                                  \
     }
         QL_GEMV_CASE(4, 4) QL_GEMV_CASE(8, 8) QL_GEMV_CASE(16, 8)
