@@ -205,6 +205,21 @@ __device__ __forceinline__ bool mean_fast(double tot, int K, float* out)
 
 __device__ __forceinline__ float h2f(uint32_t bits16) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16); }
 
+// a * b rounded once to fp32, signed zeros kept, with one of the operands an
+// fp16 half of a 32-bit word (HI: bits 16-31): v_fma_mix_f32 with the addend
+// -0 (the exact product plus -0 is the exact product, whatever its sign).  The
+// compiler turns fma(a, b, -0) back into a conversion and a multiply.
+template <bool HI>
+__device__ __forceinline__ float mul_hf(uint32_t w, float b, float negzero)
+{
+    float d;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(b), "v"(negzero));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(b), "v"(negzero));
+    return d;
+}
+
 constexpr int kNormThreads = 256;
 
 // One workgroup per token; chunks of 8 fp16 (16 bytes) strided over threads.
@@ -213,20 +228,17 @@ constexpr int kNormThreads = 256;
 // absmax and quantisation passes read registers.  CPT == 0: chunks are
 // re-read from memory in each pass (any k).  Chunks past k are zero: they add
 // nothing to the sum of squares or the absmax and are not stored.
-// Eight fp16 pairs -> fp16(a + b) per element.  The fp32 sum of two binary16
-// values rounded to binary16 is their correctly rounded sum (24 >= 2 * 11 + 2
-// significand bits), so this is exact fp16 addition.
+// Eight fp16 pairs -> fp16(a + b) per element: the correctly rounded binary16
+// sum, which is also the fp32 sum rounded to binary16 (24 >= 2 * 11 + 2
+// significand bits, so the double rounding is innocuous).
 __device__ __forceinline__ uint4 add_h8(uint4 a, uint4 b)
 {
+    typedef _Float16 h2v __attribute__((ext_vector_type(2)));
     const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
     uint32_t o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float lo = __fadd_rn(h2f(aw[e] & 0xFFFFu), h2f(bw[e] & 0xFFFFu));
-        const float hi = __fadd_rn(h2f(aw[e] >> 16), h2f(bw[e] >> 16));
-        o[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-    }
+    for (int e = 0; e < 4; ++e)   // one v_pk_add_f16 per pair
+        o[e] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2v, aw[e]) + __builtin_bit_cast(h2v, bw[e]));
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -342,6 +354,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     // y = fp32(fp32(x * r) * gamma) (y = x without the norm); kept per
     // element when the chunks are in registers, recomputed per pass otherwise
     float yk[R][8];
+    const float nz = -0.0f;
     auto y_of = [&](const uint4& v, const uint4& g, float (&yo)[8]) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
@@ -350,8 +363,10 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
                 yo[2 * e] = h2f(w[e] & 0xFFFFu);
                 yo[2 * e + 1] = h2f(w[e] >> 16);
             } else {
-                yo[2 * e] = __fmul_rn(__fmul_rn(h2f(w[e] & 0xFFFFu), r), h2f(gw[e] & 0xFFFFu));
-                yo[2 * e + 1] = __fmul_rn(__fmul_rn(h2f(w[e] >> 16), r), h2f(gw[e] >> 16));
+                // each product rounded once, fp16 operands converted inside
+                // the instruction (the e4m3 codes keep the sign of a zero)
+                yo[2 * e] = mul_hf<false>(gw[e], mul_hf<false>(w[e], r, nz), nz);
+                yo[2 * e + 1] = mul_hf<true>(gw[e], mul_hf<true>(w[e], r, nz), nz);
             }
         }
     };
@@ -374,21 +389,44 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
     if (threadIdx.x == 0)
         x_scale[row] = scale;
 
-    // Code of y: rint(fp32(y / scale)), clamped to +-127.  q0 = y * RN(1/scale)
-    // is within 1.5 ulp of fp32(y / scale) (both < 128 in magnitude, an ulp is
-    // at most 2^-17), so the two round to the same integer unless q0 lies
-    // within 2^-15 of a half-integer; only those take the exact division.
+    // Codes of y: rint(fp32(y / scale)), clamped to +-127.  q0 = y *
+    // RN(1/scale) is within 1.5 ulp of fp32(y / scale) (both < 128 in
+    // magnitude, an ulp is at most 2^-17), so the two round to the same integer
+    // unless q0 lies within 2^-15 of a half-integer, i.e. unless q0 - rint(q0)
+    // (exact) is at least 1/2 - 2^-15 in magnitude; only those take the exact
+    // division.  Eight codes at a time, packed four to a word by byte permutes.
     const float rcp = scale > 0.0f ? __fdiv_rn(1.0f, scale) : 0.0f;
-    auto code = [&](float yv) -> uint32_t {
-        if (!(scale > 0.0f))
-            return 0u;
-        const float q0 = yv * rcp;
-        float qr = rintf(q0);
-        const float half = floorf(q0) + 0.5f;
-        if (__builtin_expect(fabsf(q0 - half) <= 0x1p-15f, 0))
-            qr = rintf(__fdiv_rn(yv, scale));
-        const int qv = (int)fminf(fmaxf(qr, -127.0f), 127.0f);
-        return (uint32_t)qv & 0xFFu;
+    auto codes8 = [&](const float (&yv)[8], uint32_t (&pk)[2]) {
+        if (!(scale > 0.0f)) {
+            pk[0] = pk[1] = 0u;
+            return;
+        }
+        float qf[8];
+        bool near = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float q0 = yv[e] * rcp;
+            qf[e] = rintf(q0);
+            near |= fabsf(q0 - qf[e]) >= 0.5f - 0x1p-15f;
+        }
+        if (__builtin_expect(near, 0)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float q0 = yv[e] * rcp;
+                if (fabsf(q0 - qf[e]) >= 0.5f - 0x1p-15f)
+                    qf[e] = rintf(__fdiv_rn(yv[e], scale));
+            }
+        }
+        uint32_t qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            qv[e] = (uint32_t)(int)fminf(fmaxf(qf[e], -127.0f), 127.0f);
+        // byte 0 of each code: perm selector bytes 0 / 4 pick the low byte of
+        // the second / first operand, 0x0C a zero byte
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            pk[h] = __builtin_amdgcn_perm(qv[4 * h + 1], qv[4 * h], 0x0C0C0400u) |
+                    __builtin_amdgcn_perm(qv[4 * h + 3], qv[4 * h + 2], 0x04000C0Cu);
     };
     // FP8: fp32(y / scale), whose e4m3 cast is the code (0 for a zero scale).
     // q0 = y * RN(1/scale) lies within 4 ulp of fp32(y / scale).  The cast
@@ -436,9 +474,7 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
                 packed[h] = w;
             }
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                packed[e >> 2] |= code(yo[e]) << (8 * (e & 3));
+            codes8(yo, packed);
         }
         if (c < nch)
             qr[c] = make_uint2(packed[0], packed[1]);
