@@ -147,12 +147,50 @@ __device__ __forceinline__ U128 block_sum128(U128 v, U128* sh)
     return t;
 }
 
+// Wave reductions by DPP moves, which stay in the VALU (a shuffle is an LDS
+// round trip per step): within each row of 16 lanes the quad swaps (lane ^ 1,
+// lane ^ 2), the half-row mirror (lane 7 - i of each 8) and the row mirror
+// (lane 15 - i) leave every lane with its row's result; the four rows are
+// then combined through readlane, so every lane gets the wave's result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    return __builtin_bit_cast(double, (uint64_t)dpp<CTRL>((uint32_t)b) | ((uint64_t)dpp<CTRL>((uint32_t)(b >> 32)) << 32));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    return __builtin_bit_cast(double, (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l) |
+                                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l) << 32));
+}
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, __builtin_bit_cast(float, dpp<0xB1>(__builtin_bit_cast(uint32_t, v))));
+    v = fmaxf(v, __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(uint32_t, v))));
+    v = fmaxf(v, __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(uint32_t, v))));
+    v = fmaxf(v, __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(uint32_t, v))));
+    const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+    return fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48)));
+}
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+    v += dpp_f64<0xB1>(v);
+    v += dpp_f64<0x4E>(v);
+    v += dpp_f64<0x141>(v);
+    v += dpp_f64<0x140>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* sh)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, 64));
+    v = wave_max(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0)
         sh[wave] = v;
@@ -167,9 +205,7 @@ __device__ __forceinline__ float block_max(float v, float* sh)
 template <int NT>
 __device__ __forceinline__ double block_sum_f64(double v, double* sh)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        v += __shfl_xor(v, off, 64);
+    v = wave_sum_f64(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0)
         sh[wave] = v;
