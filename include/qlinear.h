@@ -62,8 +62,8 @@ extern "C" {
 #define QL_ERR_HIP (-8)         /* a HIP runtime call or launch failed */
 
 /* W4A16 kernel selection for ql_w4a16_gemm_path */
-#define QL_PATH_AUTO 0          /* by m: decode path for m <= 32, MFMA GEMM above */
-#define QL_PATH_DECODE 1        /* split-K GEMV path, m <= 32 */
+#define QL_PATH_AUTO 0          /* by m: decode path for m <= 64, MFMA GEMM above */
+#define QL_PATH_DECODE 1        /* split-K GEMV path, m <= 64 */
 #define QL_PATH_GEMM 2          /* LDS-tiled fp16 MFMA GEMM, any m */
 
 /* ------------------------------------------------------------------------ */
@@ -97,7 +97,7 @@ int ql_awq_pack(const float* w, int64_t n, int64_t k, int group,
  * Bytes of device workspace ql_w4a16_gemm needs for this shape (0 if none),
  * enough for every kernel path ql_w4a16_gemm_path may take.  The workspace
  * holds per-tile split-K arrival counters and fp32 partial sums: the decode
- * kernels (m <= 32) split K when their column blocks alone would leave CUs
+ * kernels (m <= 64) split K when their column blocks alone would leave CUs
  * idle, and so does the MFMA GEMM when its tiles would.
  */
 size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
@@ -110,11 +110,11 @@ size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
  *   y[m, n] = sum_c x[m, c] * (q[n, c] - z[n, g]) * s[n, g],  g = c / group
  * with fp32 accumulation and y rounded once to fp16.  The arithmetic of the
  * weight factor depends on the kernel that runs:
- *   - group 32 or 64, and any group with m > 32: each weight is formed as
+ *   - group 32 or 64, and any group with m > 64: each weight is formed as
  *     w16 = fp16((q - z) * s), one rounding of the exact product (the value
  *     ql_w4a16_dequant returns), and the exact fp16 x fp16 products x * w16
  *     are summed in fp32.
- *   - group 128 with m <= 32 (the decode kernels): the exact integers q - z
+ *   - group 128 with m <= 64 (the decode kernels): the exact integers q - z
  *     multiply the activations (exact products), each 32-term partial sum
  *     within one group is formed in fp32 by the matrix cores, then multiplied
  *     by s and added to the fp32 accumulator in one fused multiply-add; w16
@@ -124,7 +124,7 @@ size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
  *     gives y = w16[:, c] bit for bit, since (q - z) * s is exact in fp32.
  * The summation order is unspecified but fixed: repeating a call on the same
  * inputs gives the same bits.  Packed weights are streamed from HBM once per
- * call for m <= 32 and dequantised in registers.
+ * call for m <= 64 and dequantised in registers.
  *   x        fp16 [m, k]            (device)
  *   qweight, scales, qzeros         as written by ql_awq_pack (device)
  *   y        fp16 [m, n]            (device, written)
@@ -167,7 +167,7 @@ int ql_w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint1
                           void* stream);
 
 /* As ql_w4a16_gemm with an explicit kernel choice (QL_PATH_*), for tests and
- * tuning.  QL_PATH_DECODE with m > 32 is QL_ERR_UNSUPPORTED. */
+ * tuning.  QL_PATH_DECODE with m > 64 is QL_ERR_UNSUPPORTED. */
 int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                        const int32_t* qzeros, uint16_t* y, int64_t m, int64_t n, int64_t k,
                        int group, void* workspace, size_t workspace_bytes, void* stream,

@@ -72,8 +72,8 @@ def test_w4a16_gemm_validation():
     # misaligned pointers
     assert g(FAKE, MIS, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_ALIGN"]
     assert g(MIS, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 0) == E["QL_ERR_ALIGN"]
-    # decode path with m > 32, unknown path
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 33, 64, 128, 128, None, 0, DEF, 1) == E["QL_ERR_UNSUPPORTED"]
+    # decode path with m > 64, unknown path
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 65, 64, 128, 128, None, 0, DEF, 1) == E["QL_ERR_UNSUPPORTED"]
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 128, 128, None, 0, DEF, 7) == E["QL_ERR_UNSUPPORTED"]
     # split-K shape with missing / short workspace
     need = LIB.ql_w4a16_workspace_bytes(16, 4096, 4096, 128)

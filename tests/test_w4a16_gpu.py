@@ -188,12 +188,13 @@ def test_gemm_split_k(ql, m, n, k, group):
     assert full <= TOL and sampled <= TOL
 
 
-# The 32-row decode kernel with 17 to 32 rows: 18 column blocks of 64
-# channels with a ragged last one, K split into slices, 128-channel groups
-# (scale after the MFMA) and 32/64-channel groups (scaled fp16 weights);
-# deterministic reruns.
-@pytest.mark.parametrize("m,group", [(24, 128), (20, 64), (32, 32)])
-def test_decode_17_to_32_rows(ql, m, group):
+# The 32-row decode kernel with 17 to 32 rows (18 column blocks of 64
+# channels, the last ragged) and the 64-row kernel with 33 to 64 (eight-wave
+# workgroups of 128 channels: 1100 = 8 x 128 + 76), K split into slices,
+# 128-channel groups (scale after the MFMA) and 32/64-channel groups (scaled
+# fp16 weights); deterministic reruns.
+@pytest.mark.parametrize("m,group", [(24, 128), (20, 64), (32, 32), (33, 128), (48, 64), (64, 32), (64, 128)])
+def test_decode_17_to_64_rows(ql, m, group):
     n, k = 1100, 11008 if group != 32 else 4096
     rng = np.random.default_rng(m + group)
     w = workloads.weight(rng, n, k)
@@ -233,12 +234,13 @@ def test_gemm_closed_forms(ql, path, group):
     assert not y2.any()
 
 
-# One-hot rows through each decode kernel at 128-channel groups: the
-# single-row GEMV kernel (m = 1), the 16-row kernel, the 32-row kernel (m = 24) and
-# six-wave workgroups (9-32 rows, N above 64 channels per CU), with K split
-# into slices where the plan splits it.
+# One-hot rows through each decode kernel at 128-channel groups: the GEMV
+# kernel (m <= 3), the 16-row kernel, the 32-row kernel (m = 24), six-wave
+# workgroups (9-32 rows, N above 64 channels per CU) and the 64-row kernel
+# (33-64 rows), with K split into slices where the plan splits it.
 @pytest.mark.parametrize("m,n,k", [(1, 1100, 4224), (2, 1100, 4224), (3, 300, 11008), (3, 5120, 13824),
-                                   (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512), (32, 20000, 512)])
+                                   (16, 300, 11008), (24, 1100, 4096), (12, 20000, 512), (32, 20000, 512),
+                                   (64, 1100, 4224), (48, 5120, 13824), (40, 20000, 512)])
 def test_decode_one_hot_bit_exact_group128(ql, m, n, k):
     group = 128
     rng = np.random.default_rng(m + n + k)

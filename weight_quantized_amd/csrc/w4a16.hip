@@ -1,11 +1,11 @@
 // W4A16 kernels for gfx950 and their C-ABI entry points.
 //
 //   w4a16_dequant_kernel  -- writes the shared dequantisation routine's output
-//   w4a16_decode_kernel   -- 4 <= m <= 32: split-K GEMV on MFMA, weights
+//   w4a16_decode_kernel   -- 4 <= m <= 64: split-K GEMV on MFMA, weights
 //                            streamed from HBM once, dequantised in registers
 //   w4a16_gemv_kernel     -- m <= 3: one 16-channel tile per workgroup, K split
 //                            among its waves, activations and tables in LDS
-//   w4a16_gemm_pipe_kernel -- m > 32: LDS-ring fp16 MFMA GEMM (split-K when
+//   w4a16_gemm_pipe_kernel -- m > 64: LDS-ring fp16 MFMA GEMM (split-K when
 //                            its tiles would leave CUs idle)
 //   w4a16_gemm_kernel     -- the same for shapes the ring does not cover
 //
@@ -104,9 +104,10 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// decode: m <= MT (16 or 32)
+// decode: m <= MT (16, 32 or 64)
 //
-// Workgroup = T waves (4, or 6 where that keeps every CU at one workgroup);
+// Workgroup = T waves (4, or 6 where that keeps every CU at one workgroup; 8
+// for 64 rows, one workgroup per CU);
 // wave w owns R tiles of 16 output channels, so a workgroup covers
 // TW = 16 T R channels and one K slice of KS (a multiple of 256; one slice
 // when K is not split).  K advances in blocks of 256.  Per
@@ -163,7 +164,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t s16)
 
 // Workgroups per CU the register budget is held to: three four-wave
 // workgroups for one 16-row tile (a 1376-wave launch stays resident in one
-// round), two for 32 rows; as many T-wave workgroups as fit the same waves.
+// round), two for 32 or 64 rows; as many T-wave workgroups as fit the same
+// waves (one eight-wave workgroup for 64 rows).
 template <int MT, int R, int T = 4>
 constexpr int decode_wg_per_cu()
 {
@@ -432,15 +434,15 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     // (16 h + 4q + jj) ^ xswz(m) of row m, h = j >> 2, jj = j & 3.  Bit 4 of
     // the swizzle only flips the half h, so the second half is the first
     // shifted by hoff = +-16 chunks.
-    int arow[MTI][4], hoff[MTI];
-#pragma unroll
-    for (int i = 0; i < MTI; ++i) {
-        const int m = i * 16 + r16;
-        const int f = xswz(m);
+    // xswz depends on the row's low four bits only, so row tile i's
+    // addresses are tile 0's plus 512 chunks (16 rows of 32)
+    int arow[4], hoff;
+    {
+        const int f = xswz(r16);
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            arow[i][jj] = m * 32 + ((4 * q + jj) ^ (f & 15)) + (f & 16);
-        hoff[i] = (f & 16) ? -16 : 16;
+            arow[jj] = r16 * 32 + ((4 * q + jj) ^ (f & 15)) + (f & 16);
+        hoff = (f & 16) ? -16 : 16;
     }
     const int glane = (32 * q) >> lg;             // this lane's group offset within a block
     const int gmax = gs - 1;
@@ -459,12 +461,20 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
             const int b = b0 + p;
             // activation fragments of block b: requested first, so the LDS
             // latency passes while the weights are dequantised
-            uint4 af[8][MTI];
+            // (with four row tiles only tile 0's; the others are read as
+            // their MFMAs come up)
+            constexpr int MTA = MTI > 2 ? 1 : MTI;
+            uint4 af[8][MTA];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
 #pragma unroll
-                for (int i = 0; i < MTI; ++i)
-                    af[j][i] = xs[b & 1][arow[i][j & 3] + (j >> 2) * hoff[i]];
+                for (int i = 0; i < MTA; ++i)
+                    af[j][i] = xs[b & 1][arow[j & 3] + (j >> 2) * hoff + 512 * i];
+            auto frag = [&](int j, int i) -> uint4 {
+                if (i < MTA)
+                    return af[j][i];
+                return xs[b & 1][arow[j & 3] + (j >> 2) * hoff + 512 * i];
+            };
             // groups of the two pieces (padding blocks clamp to the last group;
             // their activations are zero)
             const int ga = min(((256 * b) >> lg) + glane, gmax);
@@ -525,8 +535,8 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
                         f4_t da = f4_t{0.f, 0.f, 0.f, 0.f}, db = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            da = mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[8 * t + j], da);
-                            db = mfma16x16x32(__builtin_bit_cast(h8_t, af[4 + j][i]), bw[8 * t + 4 + j], db);
+                            da = mfma16x16x32(__builtin_bit_cast(h8_t, frag(j, i)), bw[8 * t + j], da);
+                            db = mfma16x16x32(__builtin_bit_cast(h8_t, frag(4 + j, i)), bw[8 * t + 4 + j], db);
                         }
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
 #pragma unroll
                         for (int t = 0; t < R; ++t)
                             acc[t][i][j % NJ] =
-                                mfma16x16x32(__builtin_bit_cast(h8_t, af[j][i]), bw[8 * t + j], acc[t][i][j % NJ]);
+                                mfma16x16x32(__builtin_bit_cast(h8_t, frag(j, i)), bw[8 * t + j], acc[t][i][j % NJ]);
             }
             // block b + 1's activations -> the other slot; the barrier
             // publishes them and frees this slot for block b + 2
@@ -897,7 +907,7 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// GEMM (m > 32): block tile BM x BN, K advanced in tiles of 64, 4 waves as
+// GEMM (m > 64): block tile BM x BN, K advanced in tiles of 64, 4 waves as
 // 2 x 2 (wave tile BM/2 x BN/2), MFMA f32 16x16x32 f16.
 //
 // Per k-tile the activations (BM rows x 64 k, 128 contiguous bytes per row)
@@ -1585,7 +1595,7 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
 // ---------------------------------------------------------------------------
 struct DecodePlan {
     bool gemv;  // GEMV kernel, m <= 3 (one 16-channel tile per workgroup; else the streamed one)
-    int mt;     // 16 or 32
+    int mt;     // 16, 32 or 64
     int t;      // waves per workgroup (streamed kernel: 4 or 6)
     int r;      // 16-channel tiles per wave
     int p;      // blocks in flight per wave (GEMV kernel: most blocks per wave)
@@ -1606,6 +1616,7 @@ constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
 constexpr int kDecodeWaveMin = 1024;             // 4 streaming waves per CU (MI355X: 256 CUs)
 constexpr int kDecodeWaveTarget = 2048;          // 8 streaming waves per CU
 constexpr bool kDecodeWide = true;               // six-wave workgroups where they avoid doubled CUs
+constexpr int64_t kDecodeMaxRows = 64;           // the decode path takes m <= 64
 
 // Dynamic LDS of the decode kernel: the scale and zero-point tables.
 size_t decode_tables(int64_t sblocks, int64_t channels, int group)
@@ -1620,17 +1631,18 @@ size_t decode_tables(int64_t sblocks, int64_t channels, int group)
 DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
 {
     DecodePlan p{};
-    p.mt = m <= 16 ? 16 : 32;
+    p.mt = m <= 16 ? 16 : (m <= 32 ? 32 : 64);
     p.p = 2;
     p.r = 1;
     p.post = group == 128;
-    p.t = 4;
+    p.t = p.mt == 64 ? 8 : 4;
     const int64_t cus = ql::cu_count();
     // From 9 rows on, a launch not split along K whose four-wave column
     // blocks would put two workgroups on some CUs, while six-wave ones fit
     // one per CU, takes six-wave workgroups: the busiest CU then holds six
     // channel tiles instead of eight.
-    if (kDecodeWide && m > 8 && cus > 0 && (n + 63) / 64 > cus && (n + 95) / 96 <= cus && (n + 63) / 64 * 4 >= kDecodeWaveMin)
+    if (kDecodeWide && p.mt < 64 && m > 8 && cus > 0 && (n + 63) / 64 > cus && (n + 95) / 96 <= cus &&
+        (n + 63) / 64 * 4 >= kDecodeWaveMin)
         p.t = 6;
     const int64_t tw = 16 * p.t * p.r;
     p.nblk = (int)((n + tw - 1) / tw);
@@ -1638,6 +1650,10 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     const int64_t waves = (int64_t)p.nblk * p.t;
     const int64_t target = (m > 8 && (waves >= kDecodeWaveMin || p.t == 6)) ? waves : kDecodeWaveTarget;
     int64_t slices = std::min<int64_t>((target + waves - 1) / waves, kblocks);
+    // 64-row workgroups run one per CU: no more slices than keep the launch
+    // in one round
+    if (p.mt == 64 && cus > 0)
+        slices = std::max<int64_t>(1, std::min<int64_t>(slices, cus / p.nblk));
     const int64_t sblocks = (kblocks + slices - 1) / slices;   // the longest balanced slice
     p.ks = (int)(sblocks * 256);
     p.lds_bytes = decode_tables(sblocks, tw, group);
@@ -1844,6 +1860,7 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
         return true;                                                                             \
     }
     QL_DECODE_CASE(16, 1, 2, 4) QL_DECODE_CASE(32, 1, 2, 4) QL_DECODE_CASE(16, 1, 2, 6) QL_DECODE_CASE(32, 1, 2, 6)
+    QL_DECODE_CASE(64, 1, 2, 8) QL_DECODE_CASE(64, 1, 2, 8)
 #undef QL_DECODE_CASE
     return false;
 }
@@ -1855,7 +1872,7 @@ extern "C" size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int 
     if (m <= 0 || n <= 0 || k <= 0 || !ql::valid_group(group) || k % group)
         return 0;
     const size_t g = gemm_workspace(gemm_plan(m, n, k, group));
-    if (m > 32)
+    if (m > kDecodeMaxRows)
         return g;
     return std::max(g, decode_workspace(decode_plan_auto(m, n, k, group)));
 }
@@ -1875,9 +1892,10 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     if (path != QL_PATH_AUTO && path != QL_PATH_DECODE && path != QL_PATH_GEMM)
         QL_FAIL(QL_ERR_UNSUPPORTED, "%s: unknown path %d", who, path);
     if (path == QL_PATH_AUTO)
-        path = m <= 32 ? QL_PATH_DECODE : QL_PATH_GEMM;
-    if (path == QL_PATH_DECODE && m > 32)
-        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: decode path needs m <= 32 (m=%lld)", who, (long long)m);
+        path = m <= kDecodeMaxRows ? QL_PATH_DECODE : QL_PATH_GEMM;
+    if (path == QL_PATH_DECODE && m > kDecodeMaxRows)
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: decode path needs m <= %lld (m=%lld)", who, (long long)kDecodeMaxRows,
+                (long long)m);
     if (m == 0 || n == 0)
         return QL_OK;
     if (!x || !y)
