@@ -141,6 +141,24 @@ def test_gemm_path_mid_m(ql, m, n, k, group):
     assert rel_err(y.cpu().numpy(), ref) <= TOL
 
 
+# 128-row launches whose 128 x 192 tiles would leave CUs idle take 128 x 128
+# tiles: 200 x 1000 gives 2 x 8 tiles (a ragged last m-tile and n-tile) with K
+# split across workgroups; compared on the full output at each group size.
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_gemm_128_column_tiles(ql, group):
+    m, n, k = 200, 1000, 2048
+    rng = np.random.default_rng(m + n + group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k, outlier_channel_frac=0.01)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    y1 = ql.w4a16_gemm(dev(x), *d, group, path=2)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, path=2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    ref = oracle.w4a16_forward(x, qw, sc, qz, group)
+    assert rel_err(y1.cpu().numpy(), ref) <= TOL
+
+
 # Launches of two or more rounds of 128 x 192 tiles take the 8-wave ring
 # kernel: 1000 x 12200 gives 8 x 64 tiles with a ragged last m-tile and
 # n-tile; checked on sampled output channels at each group size.
