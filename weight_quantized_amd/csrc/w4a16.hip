@@ -1758,12 +1758,16 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, int group)
     p.bm = (p.pipe && m <= 64) ? 64 : 128;
     p.tiles = ((n + p.bn - 1) / p.bn) * ((m + p.bm - 1) / p.bm);
     const int64_t cus = ql::cu_count();
-    // 128-row tiles that leave CUs idle: 128 columns instead of 192 where
-    // that gives at least 20% more tiles and still one round (13B up M=256:
-    // 144 -> 216 tiles, 66 -> 54 us; fused QKV M=256: 61 -> 41 us)
-    if (p.pipe && p.bm == 128 && cus > 0 && p.tiles < cus) {
+    // 128 columns instead of 192 where 192-column tiles leave CUs idle and
+    // 128 gives at least 20% more tiles in one round (13B up M=256: 144 ->
+    // 216 tiles, 66 -> 54 us; fused QKV M=256: 61 -> 41 us), or, over several
+    // rounds, where whole rounds x width is smaller (13B up M=1024: 3 rounds
+    // of 192 against 4 of 128, 203 -> 197 us)
+    if (p.pipe && p.bm == 128 && cus > 0) {
         const int64_t t128 = ((n + 127) / 128) * ((m + 127) / 128);
-        if (t128 <= cus && t128 * 5 >= p.tiles * 6) {
+        const int64_t r192 = (p.tiles + cus - 1) / cus, r128 = (t128 + cus - 1) / cus;
+        const bool idle = p.tiles < cus && t128 <= cus && t128 * 5 >= p.tiles * 6;
+        if (idle || (p.tiles > cus && r128 * 128 < r192 * 192)) {
             p.bn = 128;
             p.tiles = t128;
         }
