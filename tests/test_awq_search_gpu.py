@@ -24,7 +24,7 @@ def calibration(rng, t, k):
 
 
 @pytest.mark.parametrize("t,n,k,group,grid", [
-    (1, 128, 512, 64, 5),       # single-row decode kernel
+    (1, 128, 512, 64, 5),       # GEMV decode kernel (m <= 3)
     (8, 100, 1056, 32, 6),      # streamed decode kernel, ragged N and K
     (16, 256, 512, 64, 10),
     (64, 192, 1024, 128, 8),    # prefill GEMM

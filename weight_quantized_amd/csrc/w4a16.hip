@@ -671,10 +671,11 @@ __device__ __forceinline__ void ring_wait_n(int n, u4v_t& a, u4v_t& b)
 // and [16+4q, 16+4q+4) of each 32-word block row), MFMAs, interleaved
 // dequantisation and POST scaling: as w4a16_decode_kernel, with M <= MR rows
 // (A row r reads activation row min(r, M - 1); output rows >= M are not
-// stored; MR = 1 compiles the single-row case without the other rows' work).  LDS: the scale and zero-point tables of the tile's 16 channels
-// for the slice's groups (16 x SD scale dwords from the dword holding the
-// first group, 16 x ZD zero words; both padded to whole 64-entry wave loads),
-// the slice's activation chunks of each row (reordered in place for the
+// stored; MR = 1 compiles the single-row case without the other rows' work).
+// LDS: the scale and zero-point tables of the tile's 16 channels for the
+// slice's groups (16 x SD scale dwords from the dword holding the first
+// group, 16 x ZD zero words; both padded to whole 64-entry wave loads), the
+// slice's activation chunks of each row (reordered in place for the
 // interleaved dequantiser, zero past the slice; rows 64 bytes apart in the
 // banks), and KW x MR x 16 floats for the sum.
 // ---------------------------------------------------------------------------
@@ -1973,8 +1974,9 @@ extern "C" int ql_w4a16_gemm_path(const uint16_t* x, const int32_t* qweight, con
     const unsigned grid = (unsigned)((units + kXcds - 1) / kXcds * kXcds);   // whole rounds over the XCDs
     if (gp.pipe) {
         if (gp.eight && gp.bn == 128)
-            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8N>), dim3(grid), dim3(Pipe8N::NW * 64), (size_t)Pipe8N::kLds,
-                               st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb, gp.nsl);
+            hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8N>), dim3(grid), dim3(Pipe8N::NW * 64),
+                               (size_t)Pipe8N::kLds, st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb,
+                               gp.nsl);
         else if (gp.eight)
             hipLaunchKernelGGL((w4a16_gemm_pipe_kernel<Pipe8>), dim3(grid), dim3(Pipe8::NW * 64), (size_t)Pipe8::kLds,
                                st, xw, qw, scales, qz, y, mi, ni, ki, lg, part, cnt, gp.kb, gp.nsl);

@@ -161,13 +161,15 @@ template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v)
 {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    return __builtin_bit_cast(double, (uint64_t)dpp<CTRL>((uint32_t)b) | ((uint64_t)dpp<CTRL>((uint32_t)(b >> 32)) << 32));
+    const uint64_t lo = dpp<CTRL>((uint32_t)b), hi = dpp<CTRL>((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
 }
 __device__ __forceinline__ double readlane_f64(double v, int l)
 {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    return __builtin_bit_cast(double, (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l) |
-                                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l) << 32));
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __builtin_bit_cast(double, lo | (hi << 32));
 }
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -175,7 +177,9 @@ __device__ __forceinline__ float wave_max(float v)
     v = fmaxf(v, __builtin_bit_cast(float, dpp<0x4E>(__builtin_bit_cast(uint32_t, v))));
     v = fmaxf(v, __builtin_bit_cast(float, dpp<0x141>(__builtin_bit_cast(uint32_t, v))));
     v = fmaxf(v, __builtin_bit_cast(float, dpp<0x140>(__builtin_bit_cast(uint32_t, v))));
-    const auto rl = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+    const auto rl = [&](int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    };
     return fmaxf(fmaxf(rl(0), rl(16)), fmaxf(rl(32), rl(48)));
 }
 __device__ __forceinline__ double wave_sum_f64(double v)
