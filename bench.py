@@ -391,6 +391,20 @@ def measure_extra(torch, ql, workloads, dev, log):
                 "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
                 "frac_mfma_fp16": round(flops / (us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)})
     del gph, ds
+    # context, not part of the path: the vendor library's plain fp16 GEMM
+    # (torch.mm on hipBLASLt) at the same shape with dense fp16 weights (4x the
+    # weight bytes, no dequantisation), timed the same way
+    w16 = torch.from_numpy(workloads.config_weight("qkv")).to(dev).half()
+    w16s = [w16.clone() for _ in range(cold_copies(w16.numel() * 2))]
+    del w16
+    torch.mm(x, w16s[0].t(), out=y)
+    torch.cuda.synchronize()
+    gl = capture(torch, [(lambda w=w: torch.mm(x, w.t(), out=y)) for w in w16s])
+    us_l = time_graph(torch, gl, reps) * 1e3 / len(w16s)
+    out.append({"name": "library_fp16_gemm_qkv", "kind": "reference: torch.mm (hipBLASLt), dense fp16 weights",
+                "m": 512, "n": n, "k": k, "us": round(us_l, 2), "TFLOP/s": round(flops / (us_l * 1e-6) / 1e12, 1),
+                "frac_mfma_fp16": round(flops / (us_l * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)})
+    del gl, w16s
     # W8A8 SmoothQuant: QRMSNorm + int8 GEMM, M=2048, K=4096, N=11008
     xh, gamma, wf = workloads.smoothquant_inputs()
     s, gs, wsm = ql.smooth(xh, gamma, wf)
@@ -422,6 +436,17 @@ def measure_extra(torch, ql, workloads, dev, log):
     out.append({"name": "w8a8_gemm", "m": m, "n": nn, "k": kk, "us": round(us_g, 2),
                 "TOP/s": round(ops / (us_g * 1e-6) / 1e12, 1),
                 "frac_mfma_int8": round(ops / (us_g * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)})
+    # context: the vendor library's int8 GEMM (torch._int_mm on hipBLASLt) on
+    # the same codes, int32 output (no scales, no fp16 epilogue)
+    acc32 = torch.empty((m, nn), dtype=torch.int32, device=dev)
+    torch._int_mm(xq, wqs[0].t(), out=acc32)
+    torch.cuda.synchronize()
+    gi = capture(torch, [(lambda wqd=wqd: torch._int_mm(xq, wqd.t(), out=acc32)) for wqd in wqs])
+    us_i = time_graph(torch, gi, reps) * 1e3 / copies
+    out.append({"name": "library_int8_gemm", "kind": "reference: torch._int_mm (hipBLASLt), int32 output",
+                "m": m, "n": nn, "k": kk, "us": round(us_i, 2), "TOP/s": round(ops / (us_i * 1e-6) / 1e12, 1),
+                "frac_mfma_int8": round(ops / (us_i * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4)})
+    del gi, acc32
 
     # the steps beside the path: residual-fused QRMSNorm, per-token
     # quantisation of a plain activation, the GEMM with bias and residual

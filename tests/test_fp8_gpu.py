@@ -66,10 +66,11 @@ def _codes(rng, shape):
     return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)   # no NaN codes
 
 
-# whole 256 x 128 tiles (LDS-staged epilogue), ragged tiles, n % 4 != 0,
-# and a shape whose 256 x 256 tiles fill whole rounds of the CUs
+# whole 256 x 128 tiles (LDS-staged epilogue), ragged tiles, n % 4 != 0, a
+# shape whose 256 x 256 tiles fill whole rounds of the CUs, and one that runs
+# a single partial round of 256 x 256 tiles with ragged m and n
 @pytest.mark.parametrize("m,n,k", [(256, 128, 4096), (300, 260, 1024), (257, 33, 512), (64, 128, 448),
-                                   (2048, 8192, 512)])
+                                   (2048, 8192, 512), (1000, 11000, 256)])
 def test_fp8_gemm_parity(ql, m, n, k):
     if k % 64:
         k += 64 - k % 64

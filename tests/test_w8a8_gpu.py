@@ -145,17 +145,15 @@ def test_gemm_fp16_epilogue_rounding(ql, m, n, k):
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
 
 
-# Shapes whose 256 x 256 tiles fill whole rounds of the CUs take the 8-wave
-# 256 x 256 ring with 128-byte k-tiles: whole tiles, ragged m and n inside it,
-# n % 8 != 0 (no LDS-staged epilogue) and n % 4 != 0 (element stores).  The
-# int32 accumulator and the fp16 epilogue (with bias and residual) are checked
-# bit for bit on every output.
-@pytest.mark.parametrize("m,n,k", [(2048, 8192, 512), (2000, 8100, 384), (2048, 8098, 256)])
+# Shapes that take the 8-wave 256 x 256 ring with 128-byte k-tiles on 256 CUs:
+# whole rounds with whole tiles, ragged m and n inside them, n % 8 != 0 (no
+# LDS-staged epilogue) and n % 4 != 0 (element stores), 688 tiles (two full
+# rounds and a partial one, ragged last column) and 172 tiles (one partial
+# round).  The int32 accumulator and the fp16 epilogue (with bias and
+# residual) are checked bit for bit on every output.
+@pytest.mark.parametrize("m,n,k", [(2048, 8192, 512), (2000, 8100, 384), (2048, 8098, 256), (4096, 11000, 128),
+                                   (1024, 11008, 256)])
 def test_gemm_big_tiles(ql, m, n, k):
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tiles = -(-m // 256) * -(-n // 256)
-    if tiles % cus:
-        pytest.skip(f"{tiles} tiles do not fill whole rounds of {cus} CUs")
     rng = np.random.default_rng(m + n + k)
     xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
     wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)

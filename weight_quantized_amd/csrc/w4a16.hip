@@ -1875,7 +1875,7 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
         return true;                                                                             \
     }
     QL_DECODE_CASE(16, 1, 2, 4) QL_DECODE_CASE(32, 1, 2, 4) QL_DECODE_CASE(16, 1, 2, 6) QL_DECODE_CASE(32, 1, 2, 6)
-    QL_DECODE_CASE(64, 1, 2, 8) QL_DECODE_CASE(64, 1, 2, 8)
+    QL_DECODE_CASE(64, 1, 2, 8)
 #undef QL_DECODE_CASE
     return false;
 }

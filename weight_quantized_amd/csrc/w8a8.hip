@@ -1122,14 +1122,17 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
 //              workgroups per CU, so a partial last round of tiles costs little
 //   PipeBig -- 256 x 256 tiles, 128-byte k-tiles, 2 stages (128 KiB), 8 waves:
 //              a third fewer L2 -> LDS bytes per MFMA, read as whole 128-byte
-//              lines; 13% faster when its tiles fill whole rounds of the CUs
-//              (2048 x 8192: 69 vs 80 us), slower with a partial last round
-//              (2048 x 11008, 344 tiles on 256 CUs: 124 vs 114 us)
+//              lines, one workgroup per CU
 using Pipe = PipeCfg<kQBM, kQBN, 64, 3, true>;
 using PipeBig = PipeCfg<256, 256, 128, 2, true, 8>;
 
-// PipeBig when its tiles fill whole rounds of the CUs, or at least four
-// rounds (the partial round is then a small share)
+// PipeBig where its estimated time is lower.  Measured per-round costs at
+// K = 4096 (all scale with K alike): a full round of PipeBig tiles (one per
+// CU) 69 us, a partial one ~50-56 us; a full round of Pipe tiles (two per CU)
+// 80 us, a partial one of at most one tile per CU ~35 us, a fuller one ~71 us.
+// 2048 x 8192: 69 against 80 us; 2048 x 11008 (344 big tiles): 120 against
+// 112 us, so Pipe; 4096 x 11008 (688): 192 against 228 us; 1024 x 11008
+// (172): 56.5 against 70 us; 3072 x 11008 and 2048 x 16640: equal.
 bool use_big_tiles(int64_t m, int64_t n, int64_t k)
 {
     if (k % PipeBig::BK || !ql::lds_fits(PipeBig::kLds))
@@ -1137,8 +1140,12 @@ bool use_big_tiles(int64_t m, int64_t n, int64_t k)
     const int64_t cus = ql::cu_count();
     if (cus <= 0)
         return false;
-    const int64_t tiles = ((m + PipeBig::BM - 1) / PipeBig::BM) * ((n + PipeBig::BN - 1) / PipeBig::BN);
-    return tiles >= cus && (tiles % cus == 0 || tiles >= 4 * cus);
+    const int64_t tb = ((m + PipeBig::BM - 1) / PipeBig::BM) * ((n + PipeBig::BN - 1) / PipeBig::BN);
+    const int64_t ts = ((m + Pipe::BM - 1) / Pipe::BM) * ((n + Pipe::BN - 1) / Pipe::BN);
+    const int64_t big = (tb / cus) * 69 + (tb % cus ? 54 : 0);
+    const int64_t rs = ts % (2 * cus);
+    const int64_t small = (ts / (2 * cus)) * 80 + (rs == 0 ? 0 : (rs <= cus ? 35 : 75));
+    return big < small;
 }
 
 template <bool kRaw, bool kF8 = false>
