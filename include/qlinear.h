@@ -383,7 +383,7 @@ int ql_fp8_quant_per_token(const uint16_t* x, uint8_t* xq, float* x_scale,
  *   [n], bias fp16 [n] or NULL, residual fp16 [m, n] or NULL (device); y fp16
  *   [m, n] (device, written; may be residual).  k % 64 == 0.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED
- * (k % 64, or k above 131072), QL_ERR_HIP.
+ * (k % 64, k above 131072, or xq or wq of 4 GiB or more), QL_ERR_HIP.
  */
 int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale,
                 const uint16_t* bias, const uint16_t* residual, uint16_t* y,

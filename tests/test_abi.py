@@ -172,6 +172,7 @@ def test_fp8_validation():
     g = LIB.ql_fp8_gemm
     assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 64, 100, DEF) == E["QL_ERR_SHAPE"]       # k % 16
     assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 64, 96, DEF) == E["QL_ERR_UNSUPPORTED"]  # k % 64
+    assert g(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, 64, 4096, DEF) == E["QL_ERR_UNSUPPORTED"]  # 4 GiB
     assert g(FAKE, None, FAKE, FAKE, None, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_NULL"]
     assert g(FAKE, FAKE, FAKE, FAKE, MIS, None, FAKE, 4, 64, 128, DEF) == E["QL_ERR_ALIGN"]
     assert g(None, None, None, None, None, None, None, 0, 64, 128, DEF) == E["QL_OK"]

@@ -881,9 +881,11 @@ struct PipeCfg {
     static constexpr int kStageBytes = (BM + BN) * BK;
     static constexpr int kLds = S * kStageBytes;
     static constexpr int D = (BM + BN) / RPB / NW;  // direct loads per wave per stage
+    static constexpr int DA = BM / RPB / NW;        // ... of them activation rows
     static constexpr int kWgPerCu = kLds <= 80 * 1024 ? 2 : 1;   // workgroups that fit one CU's LDS
     static_assert(BK == 64 || BK == 128, "k-tile of 64 or 128 bytes");
-    static_assert((BM + BN) % (NW * RPB) == 0 && BM % RPB == 0, "whole 1 KiB blocks, X/W split on a block");
+    static_assert((BM + BN) % (NW * RPB) == 0 && BM % (NW * RPB) == 0,
+                  "whole 1 KiB blocks, every wave's loads split alike between X and W");
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static_assert(S >= 2 && D * (S - 1) < 64, "ring depth within vmcnt");
 };
@@ -913,30 +915,37 @@ __global__ __launch_bounds__(C::NW * 64, C::kWgPerCu) void w8a8_gemm_pipe_kernel
     const uint32_t lds0 = (uint32_t)(uintptr_t)pl;
 
     // This wave's direct loads: the stage is (BM + BN) rows of BK bytes in
-    // blocks of RPB rows (1 KiB); wave w fills blocks w, w+NW, ...  Lane l of a
-    // block writes physical chunk l % CH of row l / CH, i.e. it reads logical
-    // chunk (l % CH) ^ f(row).  Rows past M or N re-read the last row.
-    const uint8_t* src[D];
-    uint32_t dst[D];
+    // blocks of RPB rows (1 KiB); wave w fills blocks w, w+NW, ...: its first
+    // DA loads are activation rows, the rest weight rows.  Lane l of a block
+    // writes physical chunk l % CH of row l / CH, i.e. it reads logical chunk
+    // (l % CH) ^ f(row).  Rows past M or N re-read the last row.  Each load is
+    // a wave-uniform base (the operand advanced to k-tile kt, in scalar
+    // registers) plus a fixed 32-bit per-lane offset (the host sends operands
+    // of 4 GiB or more to the register-staged kernel), and its LDS
+    // destination is wave-uniform too, so issuing a load costs no vector
+    // instruction.
+    constexpr int DA = C::DA;
+    uint32_t soff[D];
 #pragma unroll
     for (int u = 0; u < D; ++u) {
         const int blk = wave + NW * u;
         const int row = blk * C::RPB + lane / C::CH;
         const int c = (lane % C::CH) ^ swz<BK>(row);
-        if (row < BM) {
+        if (u < DA) {
             const int m = min(m0 + row, M - 1);
-            src[u] = reinterpret_cast<const uint8_t*>(xq) + (int64_t)m * K + 16 * c;
+            soff[u] = (uint32_t)m * (uint32_t)K + 16u * (uint32_t)c;
         } else {
             const int n = min(n0 + row - BM, N - 1);
-            src[u] = reinterpret_cast<const uint8_t*>(wq) + (int64_t)n * K + 16 * c;
+            soff[u] = (uint32_t)n * (uint32_t)K + 16u * (uint32_t)c;
         }
-        dst[u] = (uint32_t)(blk * 1024);
     }
+    const uint32_t wdst = (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)wave * 1024u);
     auto issue = [&](int kt, int slot) {
+        const uint8_t* xb = reinterpret_cast<const uint8_t*>(xq) + (int64_t)kt * BK;
+        const uint8_t* wb = reinterpret_cast<const uint8_t*>(wq) + (int64_t)kt * BK;
 #pragma unroll
         for (int u = 0; u < D; ++u)
-            ql::dma16(src[u] + (int64_t)kt * BK,
-                  (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + slot * C::kStageBytes + dst[u]));
+            ql::dma16s(u < DA ? xb : wb, soff[u], wdst + (uint32_t)(slot * C::kStageBytes + NW * u * 1024));
     };
 
     using AccT = std::conditional_t<kF8, f16v_t, i16_t>;
@@ -1157,11 +1166,13 @@ void launch_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const
         const int64_t tiles = ((n + bn - 1) / bn) * ((m + bm - 1) / bm);
         return (unsigned)((tiles + kXcds - 1) / kXcds * kXcds);
     };
-    if (use_big_tiles(m, n, k))
+    // the ring kernels address each operand with 32-bit per-lane offsets
+    const bool fits32 = m * k < (1LL << 32) && n * k < (1LL << 32);
+    if (fits32 && use_big_tiles(m, n, k))
         hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<PipeBig, kRaw, kF8>), dim3(grid_for(PipeBig::BM, PipeBig::BN)),
                            dim3(PipeBig::NW * 64), (size_t)PipeBig::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n,
                            (int)k);
-    else if (kF8 || (k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds)))   // FP8: the host checks k % 64 and LDS
+    else if (kF8 || (fits32 && k % Pipe::BK == 0 && ql::lds_fits(Pipe::kLds)))   // FP8: checked by the host
         hipLaunchKernelGGL((w8a8_gemm_pipe_kernel<Pipe, kRaw, kF8>), dim3(grid_for(Pipe::BM, Pipe::BN)), dim3(Pipe::NW * 64),
                            (size_t)Pipe::kLds, st, xq, xs, wq, ws, et, out, (int)m, (int)n, (int)k);
     else
@@ -1332,6 +1343,9 @@ extern "C" int ql_fp8_gemm(const uint8_t* xq, const float* x_scale, const uint8_
         return rc;
     if (k % Pipe::BK)
         QL_FAIL(QL_ERR_UNSUPPORTED, "%s: k=%lld (the FP8 GEMM needs a multiple of 64)", who, (long long)k);
+    if (m * k >= (1LL << 32) || n * k >= (1LL << 32))
+        QL_FAIL(QL_ERR_UNSUPPORTED, "%s: operands of 4 GiB or more (m=%lld n=%lld k=%lld)", who, (long long)m,
+                (long long)n, (long long)k);
     if (m == 0 || n == 0)
         return QL_OK;
     if (!x_scale || !w_scale)
