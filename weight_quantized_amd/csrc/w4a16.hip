@@ -1286,7 +1286,9 @@ __global__ __launch_bounds__(C::NW * 64) void w4a16_gemm_pipe_kernel(const uint1
     uint32_t soff[D];
     uint32_t tdst[D - DA - DB];                        // LDS offsets of the table loads
     bool tscale[D - DA - DB];                          // scale dwords (else zero words)
-    const int lw = wave & 3;                           // loading wave
+    // loading wave, in a scalar register: every ring load's LDS destination
+    // is then formed by scalar instructions
+    const int lw = __builtin_amdgcn_readfirstlane(wave & 3);
 #pragma unroll
     for (int u = 0; u < D; ++u) {
         if (u < DA) {
