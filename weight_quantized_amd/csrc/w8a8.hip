@@ -155,7 +155,9 @@ __device__ __forceinline__ U128 block_sum128(U128 v, U128* sh)
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    // every lane enabled and every source lane within its row: the old value
+    // is never used, and bound_ctrl lets the compiler leave it unset
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v)
