@@ -479,26 +479,48 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             pk[h] = __builtin_amdgcn_perm(qv[4 * h + 1], qv[4 * h], 0x0C0C0400u) |
                     __builtin_amdgcn_perm(qv[4 * h + 3], qv[4 * h + 2], 0x04000C0Cu);
     };
-    // FP8: fp32(y / scale), whose e4m3 cast is the code (0 for a zero scale).
-    // q0 = y * RN(1/scale) lies within 4 ulp of fp32(y / scale).  The cast
-    // rounds at the midpoints between codes: fp32 patterns with fraction bits
-    // [19:0] = 0x80000 in the normal range, half-integers of |q| * 2^9 below
-    // 2^-6.  Unless q0 lies within 4 ulp of one, both give the same code; only
-    // those take the correctly rounded division.
-    auto quot8 = [&](float yv) -> float {
-        if (!(scale > 0.0f))
-            return 0.0f;
-        const float q0 = yv * rcp;
-        const float a0 = fabsf(q0);
-        bool near;
-        if (a0 < 0x1p-6f) {
-            const float t = a0 * 512.0f;                     // ulp <= 2^-21
-            near = fabsf(t - floorf(t) - 0.5f) <= 0x1p-19f;
-        } else {
-            const int m20 = (int)(__builtin_bit_cast(uint32_t, q0) & 0xFFFFFu);
-            near = abs(m20 - 0x80000) <= 4;
+    // FP8 codes of eight y: e4m3(fp32(y / scale)), 0 for a zero scale.  q0 = y
+    // * RN(1/scale) differs from fp32(y / scale) by less than 3 * 2^-24 of its
+    // magnitude, fewer than 8 fp32 steps either way.  The cast is monotone and
+    // rounds q and -q alike, so when |q0| eight steps down and eight steps up
+    // cast to the same code, so does fp32(y / scale), and q0 gives the code;
+    // otherwise (rare) that quotient is formed by the correctly rounded
+    // division.  Casts take two values per instruction (nearest, ties to even;
+    // no quotient exceeds 448 by more than rounding).
+    auto cvt4 = [](float a, float b, float c, float d) -> uint32_t {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+    };
+    auto codes_f8 = [&](const float (&yv)[8], uint32_t (&pk)[2]) {
+        if (!(scale > 0.0f)) {
+            pk[0] = pk[1] = 0u;
+            return;
         }
-        return __builtin_expect(near, 0) ? __fdiv_rn(yv, scale) : q0;
+        float qf[8], lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qf[e] = yv[e] * rcp;
+            const uint32_t a = __builtin_bit_cast(uint32_t, qf[e]) & 0x7FFFFFFFu;
+            lo[e] = __builtin_bit_cast(float, __builtin_elementwise_sub_sat(a, 8u));
+            hi[e] = __builtin_bit_cast(float, a + 8u);
+        }
+        uint32_t dif[2];
+        bool near = false;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            dif[h] = cvt4(lo[4 * h], lo[4 * h + 1], lo[4 * h + 2], lo[4 * h + 3]) ^
+                     cvt4(hi[4 * h], hi[4 * h + 1], hi[4 * h + 2], hi[4 * h + 3]);
+            near |= dif[h] != 0u;
+        }
+        if (__builtin_expect(near, 0)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((dif[e >> 2] >> (8 * (e & 3))) & 0xFFu)
+                    qf[e] = __fdiv_rn(yv[e], scale);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            pk[h] = cvt4(qf[4 * h], qf[4 * h + 1], qf[4 * h + 2], qf[4 * h + 3]);
     };
     uint2* qr = reinterpret_cast<uint2*>(xq + (int64_t)row * K);
 #pragma unroll R
@@ -515,18 +537,10 @@ __global__ __launch_bounds__(kNormThreads) void quant_rmsnorm_kernel(const uint1
             y_of(v, g, yo);
         }
         uint32_t packed[2] = {0u, 0u};
-        if constexpr (kF8) {
-            // e4m3 casts of two quotients per instruction (nearest, ties to
-            // even; no quotient exceeds 448 by more than rounding)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot8(yo[4 * h]), quot8(yo[4 * h + 1]), 0, false);
-                w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot8(yo[4 * h + 2]), quot8(yo[4 * h + 3]), (int)w, true);
-                packed[h] = w;
-            }
-        } else {
+        if constexpr (kF8)
+            codes_f8(yo, packed);
+        else
             codes8(yo, packed);
-        }
         if (c < nch)
             qr[c] = make_uint2(packed[0], packed[1]);
     }
