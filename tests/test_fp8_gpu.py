@@ -54,6 +54,18 @@ def test_fp8_quant_per_token_bit_exact_and_edges(ql):
     x[3] = np.float16(2.0 ** -24)                         # smallest subnormal
     x[4] = np.linspace(-448, 448, k).astype(np.float16)  # quotients on the code grid and between
     x[5, ::2] = np.float16(1e-4)                          # codes in the subnormal range
+    # scale 3 (max 1344): quotients at the midpoints between e4m3 codes and one
+    # fp16 step either side of them, where x * RN(1/3) and the correctly
+    # rounded x / 3 can fall on different sides of a rounding boundary
+    codes = np.arange(0, 127, dtype=np.uint8)                # every finite positive code
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mids = np.float16(3.0 * (vals[:-1] + vals[1:]) / 2)
+    near = np.concatenate([mids, np.nextafter(mids, np.float16(np.inf)), np.nextafter(mids, np.float16(0))])
+    row = np.zeros(k, np.float16)
+    row[0] = 1344
+    row[1:1 + near.size] = near
+    row[1 + near.size:1 + 2 * near.size] = -near
+    x[6] = row
     xq, xs = ql.fp8_quant_per_token(dev(x))
     torch.cuda.synchronize()
     oq, osc = oracle.quant_fp8(x)
