@@ -33,7 +33,8 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got.astype(np.float64) - ref)) / (den if den > 0 else 1.0))
 
 
-@pytest.mark.parametrize("m,k", [(1, 8), (3, 4096), (17, 1000), (64, 4096), (5, 16392), (2, 65536)])
+@pytest.mark.parametrize("m,k", [(1, 8), (3, 4096), (17, 1000), (64, 4096), (5, 16392), (2, 65536), (9, 2056),
+                                 (4, 4088)])
 def test_fp8_quant_rmsnorm_bit_exact(ql, m, k):
     x, gamma, _ = workloads.smoothquant_inputs(m=m, k=k, n=1, seed=m + 5 * k)
     xq, xs = ql.fp8_quant_rmsnorm(dev(x), dev(gamma), 1e-6)
