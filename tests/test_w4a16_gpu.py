@@ -290,6 +290,31 @@ def test_gemm_empty(ql):
     assert y.shape == (0, 64)
 
 
+# K ending inside a 256-k block, so a slice's last block holds groups past K.
+# The scales are read four bytes at a time, so the last channel's last dword
+# reaches two bytes past the scale tensor; here those bytes (and the rest of the
+# buffer the tensor sits at the front of) hold NaN.  Groups past the slice's
+# valid k must never be used: every output stays finite and within the bar.
+# (Found by the random shape sweep: M = 16, N = 1471, K = 1504, group 32 put NaN
+# in the last column.)
+@pytest.mark.parametrize("group,k", [(32, 1504), (64, 1472), (128, 1408)])
+@pytest.mark.parametrize("m,path", [(1, 1), (2, 1), (5, 1), (16, 1), (24, 1), (40, 1), (16, 2)])
+def test_ragged_k_groups_past_k_unused(ql, m, path, group, k):
+    n = 1471
+    rng = np.random.default_rng(m + k + group)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), (dq, _, dz) = pack_dev(ql, w, group)
+    ng = k // group
+    buf = torch.full((n * ng + 64,), float("nan"), dtype=torch.float16, device="cuda:0")
+    buf[: n * ng] = dev(sc).reshape(-1)
+    ds = buf[: n * ng].view(n, ng)
+    y = ql.w4a16_gemm(dev(x), dq, ds, dz, group, path=path).cpu().numpy()
+    assert np.isfinite(y).all()
+    ref = oracle_all_channels(x, qw, sc, qz, group)
+    assert rel_err(y, ref) <= TOL
+
+
 # Launches of 1-3 rows take the GEMV kernel (one 16-channel tile per
 # workgroup, K split among its waves and, where the plan says so, across
 # workgroups): a ragged last 256-block (4224 = 16 x 256 + 128; 4160 = 16 x 256

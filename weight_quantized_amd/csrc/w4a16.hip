@@ -445,7 +445,10 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
         hoff = (f & 16) ? -16 : 16;
     }
     const int glane = (32 * q) >> lg;             // this lane's group offset within a block
-    const int gmax = gs - 1;
+    // the slice's last group holding valid k: blocks past the slice and k
+    // past K (zero activations) reuse it, so no group index reaches past the
+    // tensor's groups (whose padding, for the last channel, lies beyond it)
+    const int gmax = (kend - k0 - 1) >> lg;
     // table row of each of this lane's channels, and the element offset of
     // its first group within its scale dwords
     int trow[R], spar[R];
@@ -796,7 +799,10 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     // 4. this wave's blocks
     const uint4* xs = gv_lds + act_off / 16 + min(r16, M - 1) * CRS;   // this lane's A row
     const int glane = (32 * q) >> lg;
-    const int gmax = gs - 1;
+    // the slice's last group holding valid k: blocks past the slice and k
+    // past K (zero activations) reuse it, so no group index reaches past the
+    // tensor's groups (whose padding, for the last channel, lies beyond it)
+    const int gmax = (kend - k0 - 1) >> lg;
     const int spar = (int)(((uint32_t)nrow * (uint32_t)NG + (uint32_t)g0) & 1u);
     const uint16_t* srow = reinterpret_cast<const uint16_t*>(tab + r16 * SD);
     const uint32_t* zrow = tab + spad + r16 * ZD;
