@@ -38,7 +38,7 @@ def rel_err(got, ref):
     return float(np.max(np.abs(got.astype(np.float64) - ref)) / (den if den > 0 else 1.0))
 
 
-def _w4_shapes(count=30, seed=2024):
+def _w4_shapes(count=80, seed=2024):
     rng = np.random.default_rng(seed)
     buckets = [(1, 3), (4, 16), (17, 32), (33, 64), (65, 320)]
     out = []
@@ -75,7 +75,7 @@ def test_w4a16_random_shapes(ql, m, n, k, g):
         assert err <= TOL, (path, err)
 
 
-def _w8_shapes(count=12, seed=77):
+def _w8_shapes(count=20, seed=77):
     rng = np.random.default_rng(seed)
     return [(int(rng.integers(1, 700)), int(rng.integers(1, 1300)), 16 * int(rng.integers(1, 128)))
             for _ in range(count)]
@@ -133,3 +133,92 @@ def test_fp8_gemm_random_shapes(ql, m, n, k):
     ref = oracle.fp8_forward(xq, xs, wq, ws)
     assert np.isfinite(y).all()
     assert rel_err(y, ref) <= TOL
+
+
+def _w4_wide_shapes(count=20, seed=99):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m = int(rng.integers(1, 65))
+        g = int(rng.choice([32, 64, 128]))
+        k = g * int(rng.integers(2, 1024 // g + 1))
+        n = int(rng.integers(12000, 30000))
+        out.append((m, n, k, g))
+    return out
+
+
+# Wide launches (the decode plans' six-wave workgroups, many column blocks,
+# split-K at small k) through the ordinary and the allocation-free entry
+# points, which must agree bit for bit.
+@pytest.mark.parametrize("m,n,k,g", _w4_wide_shapes())
+def test_w4a16_wide_random_shapes(ql, m, n, k, g):
+    rng = np.random.default_rng(m + 3 * n + k + g)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    qw, sc, qz = ql.awq_pack(w, g)
+    d = [dev(a) for a in (qw, sc, qz)]
+    q, z = oracle.awq_unpack(qw, qz, g)
+    _, wd16 = oracle.awq_dequant(q, z, sc, g)
+    ref = x.astype(np.float64) @ wd16.astype(np.float64).T
+    xd = dev(x)
+    y = ql.w4a16_gemm(xd, *d, g)
+    y2 = torch.empty_like(y)
+    ql.w4a16_gemm_noalloc(xd, *d, g, out=y2)
+    yn = y.cpu().numpy()
+    assert np.isfinite(yn).all()
+    assert rel_err(yn, ref) <= TOL
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("m,k", _tok_shapes(count=8, seed=21))
+def test_residual_quantiser_random_shapes(ql, m, k):
+    x, gamma, _ = workloads.smoothquant_inputs(m=m, k=k, n=1, seed=2 * m + k)
+    rng = np.random.default_rng(m * k)
+    r = workloads.activations(rng, m, k)
+    h, xq, xs = ql.w8a8_add_quant_rmsnorm(dev(x), dev(r), dev(gamma), 1e-6)
+    oh, oq, osc = oracle.add_quant_rmsnorm(x, r, gamma, 1e-6)
+    assert np.array_equal(h.cpu().numpy().view(np.uint16), oh)
+    assert np.array_equal(xq.cpu().numpy(), oq)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    fq, fs = ql.fp8_quant_per_token(dev(x))
+    oq8, os8 = oracle.quant_fp8(x)
+    assert np.array_equal(fq.cpu().numpy(), oq8)
+    assert np.array_equal(fs.cpu().numpy().view(np.uint32), os8.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", _w8_shapes(count=6, seed=303))
+def test_w8a8_epilogue_random_shapes(ql, m, n, k):
+    rng = np.random.default_rng(m + n + 5 * k)
+    xq = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    xs = rng.uniform(1e-3, 1e-1, m).astype(np.float32)
+    ws = rng.uniform(1e-4, 1e-2, n).astype(np.float32)
+    bias = (rng.standard_normal(n) * 4).astype(np.float16)
+    res = (rng.standard_normal((m, n)) * 4).astype(np.float16)
+    y = ql.w8a8_gemm_ex(dev(xq), dev(xs), dev(wq), dev(ws), bias=dev(bias), residual=dev(res)).cpu().numpy()
+    oacc = oracle.int8_gemm(xq, wq)
+    f = (oacc.astype(np.float32) * xs[:, None]).astype(np.float32) * ws[None, :]
+    f = (f + bias.astype(np.float32)[None, :]).astype(np.float32)
+    f = (f + res.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(y.view(np.uint16), f.astype(np.float16).view(np.uint16))
+
+
+def _kv_shapes(count=8, seed=8):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        g = int(rng.choice([32, 64, 128]))
+        out.append((int(rng.integers(1, 5000)), g))
+    return out
+
+
+@pytest.mark.parametrize("groups,g", _kv_shapes())
+def test_kv_int8_random_shapes(ql, groups, g):
+    rng = np.random.default_rng(groups * g)
+    x = (rng.standard_normal(groups * g) * rng.uniform(0.01, 10.0)).astype(np.float16)
+    q, s = ql.kv_quant_int8(dev(x), g)
+    oq, osc = oracle.kv_quant_int8(x, g)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    back = ql.kv_dequant_int8(q, s, g).cpu().numpy()
+    assert np.array_equal(back.view(np.uint16), oracle.kv_dequant_int8(oq, osc, g))
