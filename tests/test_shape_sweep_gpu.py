@@ -222,3 +222,23 @@ def test_kv_int8_random_shapes(ql, groups, g):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), osc.view(np.uint32))
     back = ql.kv_dequant_int8(q, s, g).cpu().numpy()
     assert np.array_equal(back.view(np.uint16), oracle.kv_dequant_int8(oq, osc, g))
+
+
+# Degenerate sizes: one or a few output channels, k of a single group, rows on
+# both sides of each kernel boundary (3 | 4, 16 | 17, 32 | 33, 64 | 65).
+@pytest.mark.parametrize("n", [1, 2, 17])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("m", [1, 3, 4, 16, 17, 33, 64, 65])
+def test_w4a16_tiny_shapes(ql, m, n, g):
+    k = g
+    rng = np.random.default_rng(m * 100 + n * 10 + g)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    qw, sc, qz = ql.awq_pack(w, g)
+    d = [dev(a) for a in (qw, sc, qz)]
+    ref = oracle.w4a16_forward(x, qw, sc, qz, g)
+    paths = [ql.PATH_AUTO] + ([ql.PATH_DECODE, ql.PATH_GEMM] if m <= 64 else [])
+    for path in paths:
+        y = ql.w4a16_gemm(dev(x), *d, g, path=path).cpu().numpy()
+        assert np.isfinite(y).all(), (path,)
+        assert rel_err(y, ref) <= TOL, (path, rel_err(y, ref))
