@@ -115,3 +115,27 @@ def test_fp8_weight_quant_full_workload_matches_oracle():
     wq, wsc = ql.fp8_quant_weight(ws)
     oq, osc = oracle.fp8_quant_weight(ws)
     assert np.array_equal(wq, oq) and np.array_equal(wsc.view(np.uint32), osc.view(np.uint32))
+
+
+def _pack_shapes(count, seed=20261):
+    """Seeded (n, k, group) draws: ragged channel counts, odd and even group
+    counts (padded zero words or none), k of one group up to a few hundred."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        group = int(rng.choice([32, 64, 128]))
+        n = int(rng.integers(1, 300))
+        groups = int(rng.integers(1, 40))
+        out.append((n, groups * group, group, int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("n,k,group,seed", _pack_shapes(24))
+def test_awq_pack_random_shapes_match_oracle(n, k, group, seed):
+    rng = np.random.default_rng(seed)
+    w = workloads.weight(rng, n, k, outliers="normal0.3", outlier_frac=0.02)
+    qw, sc, qz = ql.awq_pack(w, group)
+    oq, os_, oz = _oracle_pack(w, group)
+    assert np.array_equal(qw, oq)
+    assert np.array_equal(sc.view(np.uint16), os_)
+    assert np.array_equal(qz, oz)
