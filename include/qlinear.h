@@ -96,11 +96,16 @@ int ql_awq_pack(const float* w, int64_t n, int64_t k, int group,
 /*
  * Bytes of device workspace ql_w4a16_gemm needs for this shape (0 if none),
  * enough for every kernel path ql_w4a16_gemm_path may take.  The workspace
- * holds per-tile split-K arrival counters and fp32 partial sums: the decode
- * kernels (m <= 64) split K when their column blocks alone would leave CUs
- * idle, and so does the MFMA GEMM when its tiles would.
+ * holds what split-K launches exchange: the decode kernels (m <= 64) split K
+ * when their column blocks alone would leave CUs idle, and so does the MFMA
+ * GEMM when its tiles would.  Launches split in two meet in exchange slots;
+ * launches split further use per-tile arrival counters and fp32 partial sums.
  */
 size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
+
+/* Leading bytes of a W4A16 workspace that must be zero before its first use
+ * and that every completed call leaves zero. */
+#define QL_W4A16_WS_ZERO_BYTES (32768u + (4u << 20))
 
 /*
  * ql_w4a16_gemm (device).  The W4A16 linear layer of the LMDeploy
@@ -129,12 +134,14 @@ size_t ql_w4a16_workspace_bytes(int64_t m, int64_t n, int64_t k, int group);
  *   qweight, scales, qzeros         as written by ql_awq_pack (device)
  *   y        fp16 [m, n]            (device, written)
  *   workspace, workspace_bytes      device scratch of at least
- *            ql_w4a16_workspace_bytes(m, n, k, group) bytes: a fixed 32 KiB
- *            region of split-K arrival counters followed by fp32 partial sums.
- *            Its first use must find the counter region zero-filled; every
- *            completed call leaves it zero again, so one zeroed buffer serves
- *            any number of calls of any shape on one stream.  Calls that may
- *            run concurrently need separate workspaces.  May be NULL when the
+ *            ql_w4a16_workspace_bytes(m, n, k, group) bytes: a fixed region
+ *            of 32 KiB + 4 MiB (QL_W4A16_WS_ZERO_BYTES: split-K arrival
+ *            counters, then the slots in which two-slice launches exchange
+ *            their partial sums) followed by fp32 partial sums.  Its first
+ *            use must find the fixed region zero-filled; every completed call
+ *            leaves it zero again, so one zeroed buffer serves any number of
+ *            calls of any shape on one stream.  Calls that may run
+ *            concurrently need separate workspaces.  May be NULL when the
  *            size is 0.
  * Errors: QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_GROUP, QL_ERR_ALIGN,
  * QL_ERR_WORKSPACE, QL_ERR_HIP.
@@ -150,10 +157,11 @@ int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* sca
  * bit-identical to ql_w4a16_gemm, with the split-K workspace taken from a
  * scratch array the library holds in device memory instead of an argument.
  *   Arguments as ql_w4a16_gemm, without the workspace.
- *   Scratch: 32 MiB per device (a 32 KiB counter region plus partial sums),
- *   placed when the library's code loads on that device and held until the
- *   process ends; the first call on a device clears its counters with a
- *   small kernel on `stream`, and every completed call leaves them zero.
+ *   Scratch: 32 MiB per device (the QL_W4A16_WS_ZERO_BYTES region of
+ *   counters and exchange slots, then partial sums), placed when the
+ *   library's code loads on that device and held until the process ends;
+ *   the first call on a device clears that region with a small kernel on
+ *   `stream`, and every completed call leaves it zero.
  *   The call itself allocates nothing (no hipMalloc, no library allocator).
  *   Every call on a device shares that device's scratch: calls that may
  *   overlap on one device (other streams, other threads) race and must be

@@ -97,6 +97,21 @@ def test_workspace_sizes():
     assert LIB.ql_w4a16_workspace_bytes(16, 4096, 4096, 128) > 0
 
 
+def test_workspace_zero_region():
+    """The header's zero-region size, the binding's copy of it, and every
+    split shape's workspace covering it (two-slice launches keep their
+    exchange slots there)."""
+    with open(HEADER) as f:
+        m = re.search(r"#define QL_W4A16_WS_ZERO_BYTES \((\d+)u \+ \((\d+)u << (\d+)\)\)", f.read())
+    assert m, "QL_W4A16_WS_ZERO_BYTES not found"
+    zero = int(m.group(1)) + (int(m.group(2)) << int(m.group(3)))
+    assert zero == ql.W4A16_WS_ZERO_BYTES
+    for shape in [(8, 22016, 4096, 128), (4, 16400, 512, 128), (16, 13824, 5120, 128), (1, 5120, 13824, 128),
+                  (1, 4096, 11008, 128), (16, 4096, 11008, 128)]:
+        need = LIB.ql_w4a16_workspace_bytes(*shape)
+        assert need >= zero, shape
+
+
 def test_dequant_validation():
     d = LIB.ql_w4a16_dequant
     E = CODES

@@ -124,4 +124,4 @@ def test_decode_on_two_streams(ql):
     keys = [k for k in ql._workspaces if k[2] in (streams[0].cuda_stream, streams[1].cuda_stream)]
     assert len(keys) == 2
     for key in keys:
-        assert not ql._workspaces[key][:32768].cpu().numpy().any()
+        assert not ql._workspaces[key][:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()

@@ -199,7 +199,7 @@ def test_gemm_split_k(ql, m, n, k, group):
     y2 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=2)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    assert not ws[:32768].cpu().numpy().any()
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
     got = y1.cpu().numpy()
     assert np.isfinite(got).all()
     full, sampled = full_and_sampled(got, x, qw, sc, qz, group, sample_rows(n, 5))
@@ -360,6 +360,63 @@ def test_decode_six_wave_workgroups(ql, m, k, group, n):
     assert full <= TOL and sampled <= TOL
 
 
+# K split in exactly two slices (4 to 8 rows, 16K-32K channels): the slices
+# meet in exchange slots (one atomic swap per pair of output rows) instead of
+# arrival counters and partial tiles.  Ragged m (odd rows leave half a pair),
+# ragged n (the last 16-channel tile and column block partly outside), ragged
+# k (the second slice one block shorter) and every group size; the launch is
+# repeated on one workspace (the slots must be back at zero for the second
+# call's first arrivals) and all channels are compared with the oracle.
+@pytest.mark.parametrize("m,n,k,group", [(4, 16400, 512, 128), (5, 17001, 1024, 64), (7, 20000, 768, 32),
+                                         (8, 32700, 1280, 128), (6, 22016, 4096, 128), (8, 22016, 4096, 64)])
+def test_decode_two_slice_exchange(ql, m, n, k, group):
+    rng = np.random.default_rng(m * 7 + n + k)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    need = ql.w4a16_workspace_bytes(m, n, k, group)
+    assert need >= ql.W4A16_WS_ZERO_BYTES
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    y1 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=1).clone()
+    y2 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
+    got = y1.cpu().numpy()
+    assert np.isfinite(got).all()
+    rows = np.unique(np.concatenate([sample_rows(n, 5), np.arange(n - 20, n)]))
+    full, sampled = full_and_sampled(got, x, qw, sc, qz, group, rows)
+    assert full <= TOL and sampled <= TOL, (full, sampled)
+
+
+def test_decode_two_slice_exchange_nan_and_zero(ql):
+    """Partials that are NaN in one slice only, or zero in both (an all-zero
+    activation row): the exchange still tells the first arrival from the
+    second, the NaN reaches every output of its row, zero rows give zeros,
+    and the slots end at zero."""
+    m, n, k, group = 8, 17000, 1024, 128
+    rng = np.random.default_rng(77)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    x[2, k - 5] = np.nan          # the second slice's partial of row 2
+    x[3, 7] = np.nan              # the first slice's partial of row 3
+    x[5] = 0                      # both partials +0
+    x[6] = -0.0                   # both partials zero (the products' signs follow the weights)
+    (qw, sc, qz), d = pack_dev(ql, w, group)
+    ws = torch.zeros(ql.w4a16_workspace_bytes(m, n, k, group), dtype=torch.uint8, device="cuda:0")
+    y = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=1)
+    y2 = ql.w4a16_gemm(dev(x), *d, group, workspace=ws, path=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
+    got = y.cpu().numpy()
+    assert np.isnan(got[2]).all() and np.isnan(got[3]).all()
+    assert (got[5] == 0).all() and (got[6] == 0).all()
+    ok = [0, 1, 4, 7]
+    ref = oracle_all_channels(x[ok], qw, sc, qz, group)
+    assert rel_err(got[ok], ref) <= TOL
+
+
 def test_decode_deterministic_and_workspace_left_zero(ql):
     m, n, k, group = 16, 4096, 4096, 128
     rng = np.random.default_rng(4)
@@ -372,7 +429,7 @@ def test_decode_deterministic_and_workspace_left_zero(ql):
     y2 = ql.w4a16_gemm(x, *d, group, workspace=ws, path=1)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
-    counters = ws[:32768].cpu().numpy()
+    counters = ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy()
     assert not counters.any()
 
 
@@ -381,7 +438,8 @@ def test_decode_shared_workspace_across_shapes(ql):
     and partial sums of one call never alias another call's)."""
     group = 128
     rng = np.random.default_rng(6)
-    cases = [(16, 4096, 4096), (1, 22016, 4096), (8, 1000, 11008), (16, 22016, 4096), (32, 4096, 11008)]
+    cases = [(16, 4096, 4096), (1, 22016, 4096), (8, 1000, 11008), (8, 22016, 4096), (16, 22016, 4096),
+             (32, 4096, 11008), (5, 17001, 1024)]
     need = max(ql.w4a16_workspace_bytes(m, n, k, group) for m, n, k in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
     for m, n, k in cases + cases[::-1]:
@@ -395,7 +453,7 @@ def test_decode_shared_workspace_across_shapes(ql):
         got = y.cpu().numpy()
         assert np.isfinite(got).all()
         assert rel_err(got[:, rows], ref) <= TOL, (m, n, k)
-    assert not ws[:32768].cpu().numpy().any()
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
 
 
 def test_decode_graph_replays_match_eager(ql):
@@ -404,7 +462,7 @@ def test_decode_graph_replays_match_eager(ql):
     (the arrival counters reset themselves; no memset nodes are involved)."""
     group = 128
     rng = np.random.default_rng(8)
-    cases = [(1, 4096, 4096), (16, 4096, 11008)]
+    cases = [(1, 4096, 4096), (16, 4096, 11008), (6, 17001, 1024)]
     need = max(ql.w4a16_workspace_bytes(m, n, k, group) for m, n, k in cases)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
     data = []
@@ -429,7 +487,7 @@ def test_decode_graph_replays_match_eager(ql):
         torch.cuda.synchronize()
         for e, (_, _, y) in zip(eager, data):
             assert torch.equal(e, y), rep
-    assert not ws[:32768].cpu().numpy().any()
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
 
 
 # ------------------------------------------------------------------ full-size configurations

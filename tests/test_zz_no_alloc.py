@@ -60,10 +60,11 @@ def _with_workspace(lib, d, m, n, k, group, y):
 
 
 # pairs of calls, the second smaller: split-K decode (16-row, single-row and
-# 32-row kernels, four- and six-wave workgroups), an unsplit launch and the
-# MFMA GEMM (no scratch)
+# 32-row kernels, four- and six-wave workgroups, two slices meeting in exchange
+# slots), an unsplit launch and the MFMA GEMM (no scratch)
 PAIRS = [
     ((16, 4096, 11008, 128), (4, 1100, 4096, 128)),
+    ((8, 22016, 4096, 128), (5, 17001, 1024, 64)),
     ((1, 22016, 4096, 128), (1, 4096, 4096, 64)),
     ((32, 4096, 11008, 128), (8, 1000, 2048, 32)),
     ((24, 20000, 2176, 64), (12, 4096, 1024, 128)),

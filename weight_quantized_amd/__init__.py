@@ -19,13 +19,17 @@ __all__ = [
     "QLError", "lib_path", "awq_pack", "smooth", "w8a8_quant_weight",
     "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant", "w8a8_quant_rmsnorm",
     "w8a8_gemm", "w8a8_gemm_i32", "status_string", "version",
-    "PATH_AUTO", "PATH_DECODE", "PATH_GEMM", "EXPORTS",
+    "PATH_AUTO", "PATH_DECODE", "PATH_GEMM", "W4A16_WS_ZERO_BYTES", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libqlinear.so")
 
 PATH_AUTO, PATH_DECODE, PATH_GEMM = 0, 1, 2
+
+# Leading bytes of a W4A16 workspace that are zero between calls (split-K
+# arrival counters, then two-slice exchange slots); mirrors include/qlinear.h
+W4A16_WS_ZERO_BYTES = 32768 + (4 << 20)
 
 _p, _i64, _sz, _i = C.c_void_p, C.c_int64, C.c_size_t, C.c_int
 
@@ -261,8 +265,8 @@ _workspaces = {}
 
 def _workspace(device, nbytes):
     """A zero-filled split-K workspace per (device, stream), grown on demand.
-    The kernels leave its counter area zero after every call, so it is reused
-    as is.  Calls on one stream run in order and may share it; calls on
+    The kernels leave its leading W4A16_WS_ZERO_BYTES (counters and exchange
+    slots) zero after every call, so it is reused as is.  Calls on one stream run in order and may share it; calls on
     different streams may run concurrently and so each stream has its own.
     It is allocated while its stream is current, so when a larger one
     replaces it the caching allocator hands the old memory out again only to

@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 // arrival counter; the last arrival reads the partials back with agent-scope
 // loads and sums them in slice order (deterministic).  No cache-wide fence is
 // needed because every cross-workgroup value travels through agent-scope
-// accesses.
+// accesses.  With exactly two slices the partials meet in exchange slots
+// instead (pair_finish below: one atomic round trip instead of three).
 // ---------------------------------------------------------------------------
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format
 
@@ -309,11 +310,103 @@ __device__ __forceinline__ void splitk_finish(float* __restrict__ part, uint32_t
         __hip_atomic_store(&cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Two-slice completion.  With K split in exactly two slices every output is
+// the sum of two partials, one per slice, added in slice order (slice 0's
+// first, which fixes the bits even for NaN payloads).  Each pair of adjacent
+// output rows of a lane meets in one 8-byte slot of a region that is zero
+// between calls: each slice swaps its two partials into the slot with one
+// relaxed agent-scope atomic exchange (the values travel in the atomic
+// itself, so nothing else needs ordering, and there is no arrival counter,
+// no wait for store acknowledgements and no re-read of partial tiles).  The
+// exchange that returns zero came first and is done; the other receives the
+// first slice's partials, adds them to its own, stores the fp16 outputs and
+// puts zero back.  Slots hold the partials' bits XOR kPairKey, so a zero
+// slot cannot be mistaken for stored partials: that would need both partials
+// to be 0x7F8A5A5A, a signalling NaN with nonzero low 13 mantissa bits,
+// which neither fp32 arithmetic (its NaNs are quiet) nor a value widened
+// from fp16 (low 13 bits zero) produces.
+//
+// NF fragments per lane: fragment f holds output rows row0[f] + 0..3 of
+// column col[f]; its slots are slot[(f * 64 + lane) * 2 + h], h = 0 for rows
+// 0-1 and 1 for rows 2-3.  Pairs starting at or past M (the padding of the
+// row tiles) are skipped by both slices alike: the exchanges' cost grows with
+// their number (exchanging the padding too made gate/up M = 4 / 8 0.4 us
+// slower).
+constexpr uint64_t kPairKey = 0x7F8A5A5A7F8A5A5Aull;
+
+template <int NF>
+__device__ __forceinline__ void pair_finish(uint64_t* __restrict__ slot, const f4_t (&v)[NF], const int (&row0)[NF],
+                                            const int (&col)[NF], uint16_t* __restrict__ y, int M, int N)
+{
+    const int lane = threadIdx.x & 63;
+    const bool first_slice = blockIdx.y == 0;
+    // every exchange's address and operand in registers of its own before
+    // the first is issued (computed inside each lane-predicated exchange,
+    // they shared registers, and each exchange waited for the one before)
+    typedef __attribute__((address_space(1))) uint64_t gu64_t;   // global memory: global, not flat, atomics
+    gu64_t* addr[NF][2];
+    uint64_t val[NF][2], old[NF][2];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // (each element copied out first: a bit cast of a vector element
+            // in place reads element 0)
+            const float lo = v[f][2 * h], hi = v[f][2 * h + 1];
+            val[f][h] = ((uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                         ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32)) ^ kPairKey;
+            addr[f][h] = (gu64_t*)&slot[(f * 64 + lane) * 2 + h];
+            asm volatile("" : "+v"(val[f][h]), "+v"(addr[f][h]));
+        }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            old[f][h] = row0[f] + 2 * h < M ? __hip_atomic_exchange(addr[f][h], val[f][h], __ATOMIC_RELAXED,
+                                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                            : 0ull;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (old[f][h] == 0ull)
+                continue;
+            const uint64_t o = old[f][h] ^ kPairKey;
+            const float other[2] = {__builtin_bit_cast(float, (uint32_t)o), __builtin_bit_cast(float, (uint32_t)(o >> 32))};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float mine = v[f][2 * h + e];
+                const float sum = first_slice ? mine + other[e] : other[e] + mine;
+                const int m = row0[f] + 2 * h + e;
+                if (m < M && col[f] < N)
+                    y[(int64_t)m * N + col[f]] = f32_to_f16_bits(sum);
+            }
+            __hip_atomic_store(&slot[(f * 64 + lane) * 2 + h], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+}
+
+// The same exchange for one output per thread: a 4-byte slot holding the
+// partial's bits XOR the low half of kPairKey.
+__device__ __forceinline__ void pair_finish_one(uint32_t* __restrict__ slot, float v, uint16_t* __restrict__ y, int m,
+                                                int col, int N)
+{
+    constexpr uint32_t kKey = (uint32_t)kPairKey;
+    const uint32_t old = __hip_atomic_exchange(slot, __builtin_bit_cast(uint32_t, v) ^ kKey, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    if (old == 0u)
+        return;
+    const float other = __builtin_bit_cast(float, old ^ kKey);
+    const float sum = blockIdx.y == 0 ? v + other : other + v;
+    if (col < N)
+        y[(int64_t)m * N + col] = f32_to_f16_bits(sum);
+    __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int MT, int R, int P, bool POST, int T = 4>
 __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS)
+    uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS, int pair)
 {
     constexpr int NT = 64 * T;                     // threads
     constexpr int TW = 16 * T * R;                 // channels per workgroup
@@ -591,6 +684,24 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
         return;
     }
 
+    if (pair) {
+        // two slices: this wave's fragments meet the other slice's in the
+        // column block's slots
+        f4_t v[R * MTI];
+        int row0[R * MTI], col[R * MTI];
+#pragma unroll
+        for (int t = 0; t < R; ++t)
+#pragma unroll
+            for (int i = 0; i < MTI; ++i) {
+                v[t * MTI + i] = res[t][i];
+                row0[t * MTI + i] = i * 16 + 4 * q;
+                col[t * MTI + i] = n0 + (wave * R + t) * 16 + r16;
+            }
+        pair_finish<R * MTI>(reinterpret_cast<uint64_t*>(part) + ((int64_t)blockIdx.x * T + wave) * (R * MTI * 128),
+                             v, row0, col, y, M, N);
+        return;
+    }
+
     // 6. split-K: this slice's partial tile with agent-scope stores, then
     //    the arrival and the last arrival's reduction
     float* tile = part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)M * TW;
@@ -686,7 +797,7 @@ template <int NB, int P, bool POST, int MR, int KW = 4, int P0 = P>
 __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
-    uint32_t* __restrict__ cnt, int m_rows, int N, int K, int lg, int KS)
+    uint32_t* __restrict__ cnt, int m_rows, int N, int K, int lg, int KS, int pair)
 {
     static_assert(NB >= 1 && NB <= 16 && P >= 1 && P <= NB, "the ring waits cover up to 16 blocks");
     static_assert(MR >= 1 && MR <= 4, "up to four rows (lanes 0-15 hold output rows 0-3)");
@@ -903,6 +1014,14 @@ __global__ __launch_bounds__(64 * KW) void w4a16_gemv_kernel(
     if (gridDim.y == 1) {
         if (rr < M && ncol < N)
             y[(int64_t)rr * N + ncol] = f32_to_f16_bits(sum);
+        return;
+    }
+    if (pair) {
+        // two slices: each output meets the other slice's partial in one
+        // 4-byte slot, [column block][MR rows][16 channels]
+        if (rr < M)
+            pair_finish_one(reinterpret_cast<uint32_t*>(part) + ((int64_t)blockIdx.x * MR + rr) * TW + cc, sum,
+                            y, rr, ncol, N);
         return;
     }
     // 6. split-K across workgroups: this slice's M x 16 partial tile, then
@@ -1612,15 +1731,19 @@ struct DecodePlan {
     int ks;     // k per slice (multiple of 256)
     int slices; // split-K factor
     int nblk;   // column blocks
+    bool pair;  // two slices that meet in exchange slots (no counters, no partial tiles)
     size_t lds_bytes;   // dynamic LDS bytes
     size_t part_offset, part_bytes;
 };
 
-// The workspace starts with a fixed counter region that only ever holds
-// arrival counters (zero between calls); partial sums follow it.  A fixed
-// region keeps calls of different shapes from reading each other's partial
-// sums as counters when they share one workspace.
+// The workspace starts with a fixed region that is zero between calls: the
+// arrival counters, then the two-slice exchange slots; partial sums follow
+// it.  A fixed region keeps calls of different shapes from reading each
+// other's partial sums as counters or slots when they share one workspace.
 constexpr size_t kCounterBytes = 32768;
+constexpr size_t kPairBytes = (size_t)4 << 20;
+constexpr size_t kFixedBytes = kCounterBytes + kPairBytes;
+static_assert(kFixedBytes == QL_W4A16_WS_ZERO_BYTES, "the header states the fixed region's size");
 constexpr int kMaxDecodeBlocks = (int)(kCounterBytes / sizeof(uint32_t));
 constexpr int kDecodeWaveMin = 1024;             // 4 streaming waves per CU (MI355X: 256 CUs)
 constexpr int kDecodeWaveTarget = 2048;          // 8 streaming waves per CU
@@ -1659,6 +1782,17 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     const int64_t waves = (int64_t)p.nblk * p.t;
     const int64_t target = (m > 8 && (waves >= kDecodeWaveMin || p.t == 6)) ? waves : kDecodeWaveTarget;
     int64_t slices = std::min<int64_t>((target + waves - 1) / waves, kblocks);
+    // Two slices meet in exchange slots (one atomic round trip) where more
+    // need the counter protocol (three dependent round trips, about 1 us
+    // more): where that balance asks for three or four slices, two are as
+    // fast or faster (measured at M = 4-32, N = 8192-14336 and the 13B up
+    // projection: 1.1-4.4 us less at three slices, even at four).  Not for
+    // the 64-row kernel, whose eight exchanges per lane cost more than the
+    // counter protocol (13B up M = 64: 29.6 against 26.0 us).
+    const size_t pair_slots = (size_t)p.nblk * (size_t)(tw / 16) * (size_t)(p.mt / 16) * 1024;
+    const bool pair_ok = p.mt <= 32 && pair_slots <= kPairBytes;
+    if ((slices == 3 || slices == 4) && pair_ok)
+        slices = 2;
     // 64-row workgroups run one per CU: no more slices than keep the launch
     // in one round
     if (p.mt == 64 && cus > 0)
@@ -1667,21 +1801,28 @@ DecodePlan decode_plan(int64_t m, int64_t n, int64_t k, int group)
     p.ks = (int)(sblocks * 256);
     p.lds_bytes = decode_tables(sblocks, tw, group);
     p.slices = (int)slices;
-    p.part_offset = kCounterBytes;
-    // partial tiles [slices][nblk][m][64 r] fp32
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)tw * sizeof(float) : 0;
+    p.part_offset = kFixedBytes;
+    // two slices: 8-byte slots for pairs of output rows, [nblk][tw / 16][mt / 16][64 lanes][2]
+    p.pair = p.slices == 2 && pair_ok;
+    // else partial tiles [slices][nblk][m][tw] fp32
+    p.part_bytes = p.slices > 1 && !p.pair ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * (size_t)tw * sizeof(float) : 0;
     return p;
 }
 
 // GEMV plan (m <= kGemvMaxRows): one workgroup of kGemvWaves waves per
 // 16-channel tile; K split across workgroups (sg slices) only where that
-// evens out the load per CU by more than the cross-workgroup sum costs (taken
-// as 15%), or where the slice's activation rows would not fit their budget.
+// evens out the load per CU by more than the cross-workgroup sum costs, or
+// where the slice's activation rows would not fit their budget.  The costs
+// are fitted to the LLaMA-7B and 13B shapes: with 128-channel groups 5% for
+// two slices, which meet in exchange slots, and 30% for more (13B down M = 1
+// 12.9 us at two slices against 13.7 us at four); with smaller groups 10% and
+// 15% (13B down M = 1 at G = 32: 17.2 us at two slices, 15.8 at four).
 constexpr int kGemvWaves = 4;
 constexpr int kGemvEarlyBlocks = 2;              // weight blocks requested before the tables and activations land
 constexpr int kGemvMaxWaveBlocks = 16;
 constexpr int64_t kGemvMaxActBytes = 98304;
 constexpr int kGemvMaxRows = 3;
+constexpr int kGemvResidentWgs = 8;              // four-wave workgroups per CU at most (32 waves)
 
 DecodePlan decode_plan_gemv(int64_t m, int64_t n, int64_t k, int group)
 {
@@ -1700,7 +1841,13 @@ DecodePlan decode_plan_gemv(int64_t m, int64_t n, int64_t k, int group)
     if (cus > 0) {
         double best = 1e30;
         for (int64_t s2 = sg_min; s2 <= std::min<int64_t>(4 * sg_min, kblocks); ++s2) {
-            const double load = (double)((p.nblk * s2 + cus - 1) / cus) / (double)s2 * (s2 > 1 ? 1.15 : 1.0);
+            // two slices meet in exchange slots, more through the counter
+            // protocol; two are not taken where their workgroups would
+            // not all be resident at once
+            if (s2 == 2 && p.nblk * 2 > kGemvResidentWgs * cus)
+                continue;
+            const double cost = s2 == 1 ? 1.0 : (p.post ? (s2 == 2 ? 1.05 : 1.3) : (s2 == 2 ? 1.1 : 1.15));
+            const double load = (double)((p.nblk * s2 + cus - 1) / cus) / (double)s2 * cost;
             if (load < best - 1e-9) {
                 best = load;
                 sg = s2;
@@ -1721,8 +1868,10 @@ DecodePlan decode_plan_gemv(int64_t m, int64_t n, int64_t k, int group)
     const int64_t cpad = (p.ks / 8 + nt - 1) / nt * nt;
     const int64_t mr = m > 1 ? kGemvMaxRows : 1;
     p.lds_bytes = (size_t)((spad + zpad) * 4 + m * (cpad + (m > 1 ? 4 : 0)) * 16 + kGemvWaves * mr * 16 * 4);
-    p.part_offset = kCounterBytes;
-    p.part_bytes = p.slices > 1 ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * 16 * sizeof(float) : 0;
+    p.part_offset = kFixedBytes;
+    // two slices: 4-byte slots [nblk][rows][16]; else partial tiles [slices][nblk][m][16] fp32
+    p.pair = p.slices == 2 && (size_t)p.nblk * (size_t)kGemvMaxRows * 16 * sizeof(float) <= kPairBytes;
+    p.part_bytes = p.slices > 1 && !p.pair ? (size_t)p.slices * (size_t)p.nblk * (size_t)m * 16 * sizeof(float) : 0;
     return p;
 }
 
@@ -1795,7 +1944,7 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, int group)
             p.nsl = (int)((nk + p.kb - 1) / p.kb);
         }
     }
-    p.part_offset = kCounterBytes;
+    p.part_offset = kFixedBytes;
     p.part_bytes = p.nsl > 1 ? (size_t)p.nsl * (size_t)p.tiles * (size_t)std::min<int64_t>(m, p.bm) * (size_t)p.bn *
                                    sizeof(float)
                              : 0;
@@ -1834,9 +1983,11 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
                      const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
-    float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
+    float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                          (p.pair ? kCounterBytes : p.part_offset))
+                               : nullptr;
     hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST, T>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes,
-                       st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+                       st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks, p.pair ? 1 : 0);
 }
 
 template <int NB, int P, bool POST>
@@ -1844,17 +1995,20 @@ void launch_gemv_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
                    const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
     uint32_t* cnt = p.slices > 1 ? static_cast<uint32_t*>(ws) : nullptr;
-    float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_offset) : nullptr;
+    float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                          (p.pair ? kCounterBytes : p.part_offset))
+                               : nullptr;
+    const int pair = p.pair ? 1 : 0;
     constexpr int P0 = kGemvEarlyBlocks < P ? kGemvEarlyBlocks : P;
     if (m > 1) {
         hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, kGemvMaxRows, kGemvWaves, P0>),
                            dim3(p.nblk, p.slices), dim3(64 * kGemvWaves),
-                           p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+                           p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks, pair);
         return;
     }
     hipLaunchKernelGGL((w4a16_gemv_kernel<NB, P, POST, 1, kGemvWaves, P0>),
                        dim3(p.nblk, p.slices), dim3(64 * kGemvWaves),
-                       p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks);
+                       p.lds_bytes, st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks, pair);
 }
 
 bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
@@ -2022,7 +2176,7 @@ extern "C" int ql_w4a16_gemm(const uint16_t* x, const int32_t* qweight, const ui
 // stand-in, not device memory): the device address comes from
 // hipGetSymbolAddress, once per device, and is kept in g_scratch.
 // ---------------------------------------------------------------------------
-constexpr size_t kScratchBytes = (size_t)32 << 20;  // 32 KiB of counters + partial sums
+constexpr size_t kScratchBytes = (size_t)32 << 20;  // the fixed zero region + partial sums
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
@@ -2060,8 +2214,8 @@ int scratch_for_current_device(hipStream_t st, void** out, const char* who)
         if (e != hipSuccess || !p)
             QL_FAIL(QL_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who, dev,
                     hipGetErrorString(e));
-        hipLaunchKernelGGL(zero_words_kernel, dim3(8), dim3(256), 0, st, static_cast<uint32_t*>(p),
-                           (int)(kCounterBytes / sizeof(uint32_t)));
+        hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, st, static_cast<uint32_t*>(p),
+                           (int)(kFixedBytes / sizeof(uint32_t)));
         if (int rc = launch_status(who))
             return rc;
         g_scratch[dev].store(p, std::memory_order_release);
