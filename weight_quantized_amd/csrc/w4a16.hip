@@ -327,8 +327,9 @@ __device__ __forceinline__ void splitk_finish(float* __restrict__ part, uint32_t
 // from fp16 (low 13 bits zero) produces.
 //
 // NF fragments per lane: fragment f holds output rows row0[f] + 0..3 of
-// column col[f]; its slots are slot[(f * 64 + lane) * 2 + h], h = 0 for rows
-// 0-1 and 1 for rows 2-3.  Pairs starting at or past M (the padding of the
+// column col[f]; its slots are slot[(f * 2 + h) * 64 + lane], h = 0 for rows
+// 0-1 and 1 for rows 2-3, so each exchange instruction covers 512 contiguous
+// bytes (interleaving h, 0.1-0.3 us slower).  Pairs starting at or past M (the padding of the
 // row tiles) are skipped by both slices alike: the exchanges' cost grows with
 // their number (exchanging the padding too made gate/up M = 4 / 8 0.4 us
 // slower).
@@ -355,7 +356,7 @@ __device__ __forceinline__ void pair_finish(uint64_t* __restrict__ slot, const f
             const float lo = v[f][2 * h], hi = v[f][2 * h + 1];
             val[f][h] = ((uint64_t)__builtin_bit_cast(uint32_t, lo) |
                          ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32)) ^ kPairKey;
-            addr[f][h] = (gu64_t*)&slot[(f * 64 + lane) * 2 + h];
+            addr[f][h] = (gu64_t*)&slot[(f * 2 + h) * 64 + lane];
             asm volatile("" : "+v"(val[f][h]), "+v"(addr[f][h]));
         }
 #pragma unroll
@@ -381,7 +382,7 @@ __device__ __forceinline__ void pair_finish(uint64_t* __restrict__ slot, const f
                 if (m < M && col[f] < N)
                     y[(int64_t)m * N + col[f]] = f32_to_f16_bits(sum);
             }
-            __hip_atomic_store(&slot[(f * 64 + lane) * 2 + h], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&slot[(f * 2 + h) * 64 + lane], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 }
 
