@@ -82,8 +82,10 @@ def traffic_records():
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps before the timed ones (the default, ~55 ms of GPU work, lets the clocks "
+                         "come up after the host-side phases, as WARM_MS does for the per-launch graphs)")
     ap.add_argument("--copies", type=int, default=12, help="cold-cache weight copies per shape")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
