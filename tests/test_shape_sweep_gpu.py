@@ -170,6 +170,54 @@ def test_w4a16_wide_random_shapes(ql, m, n, k, g):
     assert torch.equal(y, y2)
 
 
+def _w4_split_shapes(count=18, seed=4242):
+    """Shapes whose decode plans split K in two and meet in exchange slots:
+    the streamed kernel at 4-8 rows and 16K-32K channels, plans that would
+    split in three or four (4-32 rows, 6K-16K channels, k up to 6144), and
+    the GEMV kernel (1-3 rows, 5K-14K channels, k 5K-14K)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        g = int(rng.choice([32, 64, 128]))
+        kind = i % 3
+        if kind == 0:
+            m, n, k = int(rng.integers(4, 9)), int(rng.integers(16400, 32700)), int(rng.integers(512, 4097))
+        elif kind == 1:
+            m, n, k = int(rng.integers(4, 33)), int(rng.integers(6000, 16000)), int(rng.integers(1024, 6145))
+        else:
+            m, n, k = int(rng.integers(1, 4)), int(rng.integers(5000, 14000)), int(rng.integers(5120, 14337))
+        out.append((m, n, k // g * g, g))
+    return out
+
+
+# Split-in-two launches at larger k than the wide sweep: every call twice on
+# one workspace (bit-identical, the exchange slots back at zero), the
+# allocation-free entry point bit for bit, and sampled channels (the tail
+# included) against the oracle's own loop.
+@pytest.mark.parametrize("m,n,k,g", _w4_split_shapes())
+def test_w4a16_split_in_two_random_shapes(ql, m, n, k, g):
+    rng = np.random.default_rng(m + 5 * n + k + g)
+    w = workloads.weight(rng, n, k)
+    x = workloads.activations(rng, m, k)
+    qw, sc, qz = ql.awq_pack(w, g)
+    d = [dev(a) for a in (qw, sc, qz)]
+    xd = dev(x)
+    ws = torch.zeros(max(ql.w4a16_workspace_bytes(m, n, k, g), 16), dtype=torch.uint8, device="cuda:0")
+    y1 = ql.w4a16_gemm(xd, *d, g, workspace=ws).clone()
+    y2 = ql.w4a16_gemm(xd, *d, g, workspace=ws)
+    y3 = torch.empty_like(y1)
+    ql.w4a16_gemm_noalloc(xd, *d, g, out=y3)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
+    assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any()
+    yn = y1.cpu().numpy()
+    assert np.isfinite(yn).all()
+    rows = np.unique(np.concatenate([np.linspace(0, n - 1, 12).astype(np.int64), np.arange(n - 4, n)]))
+    ref = oracle.w4a16_forward(x, qw, sc, qz, g, rows=rows)
+    assert rel_err(yn[:, rows], ref) <= TOL
+
+
 @pytest.mark.parametrize("m,k", _tok_shapes(count=8, seed=21))
 def test_residual_quantiser_random_shapes(ql, m, k):
     x, gamma, _ = workloads.smoothquant_inputs(m=m, k=k, n=1, seed=2 * m + k)
