@@ -343,9 +343,12 @@ def test_decode_gemv(ql, m, n, k, group):
 # 9-32 rows on a wide N take six-wave workgroups (96 channels) when that keeps
 # every CU at one workgroup: a ragged last workgroup (20000 = 208 x 96 + 32;
 # 20001 also ends inside a 16-channel tile) and a ragged K, compared on sampled
-# output channels including the tail.
+# output channels including the tail.  The 16-row ones publish activations
+# every second block through a four-slot ring, so block counts that are not a
+# multiple of four (1, 5, 7, 9, 13 blocks) run padding blocks.
 @pytest.mark.parametrize("m,k,group,n", [(12, 2176, 128, 20000), (24, 2080, 32, 20000), (32, 2176, 64, 20000),
-                                         (20, 2176, 128, 20001)])
+                                         (20, 2176, 128, 20001), (9, 1280, 64, 17000), (16, 3328, 32, 20001),
+                                         (13, 256, 128, 16500), (10, 1792, 128, 24577)])
 def test_decode_six_wave_workgroups(ql, m, k, group, n):
     rng = np.random.default_rng(m * 3 + k)
     w = workloads.weight(rng, n, k)

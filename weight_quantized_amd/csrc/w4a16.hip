@@ -166,12 +166,14 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t s16)
 // Workgroups per CU the register budget is held to: three four-wave
 // workgroups for one 16-row tile (a 1376-wave launch stays resident in one
 // round), two for 32 or 64 rows; as many T-wave workgroups as fit the same
-// waves (one eight-wave workgroup for 64 rows).
-template <int MT, int R, int T = 4>
+// waves (one eight-wave workgroup for 64 rows).  A launch that publishes
+// activations every second block (XB = 2: the six-wave, one-workgroup-per-CU
+// plans) is held to one workgroup per CU.
+template <int MT, int R, int T = 4, int XB = 1>
 constexpr int decode_wg_per_cu()
 {
     constexpr int waves = 4 * (R > 1 ? 1 : (MT == 16 ? 3 : 2));
-    return waves / T > 0 ? waves / T : 1;
+    return XB > 1 ? 1 : (waves / T > 0 ? waves / T : 1);
 }
 
 // Scale and zero-point tables of TW channels [n0, n0 + TW) for the groups
@@ -403,8 +405,8 @@ __device__ __forceinline__ void pair_finish_one(uint32_t* __restrict__ slot, flo
     __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int R, int P, bool POST, int T = 4>
-__global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_decode_kernel(
+template <int MT, int R, int P, bool POST, int T = 4, int XB = 1>
+__global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T, XB>())) void w4a16_decode_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
     const uint32_t* __restrict__ qz, uint16_t* __restrict__ y, float* __restrict__ part,
     uint32_t* __restrict__ cnt, int M, int N, int K, int lg, int KS, int pair)
@@ -416,7 +418,14 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     constexpr int XPT = (XC + NT - 1) / NT;        // ... per thread
     constexpr int NJ = POST ? 1 : (R * MTI >= 4 ? 1 : 4 / (R * MTI));   // accumulator chains
     constexpr int NW = 8 * R;                      // words per lane and block
-    __shared__ uint4 xs[2][MT * 32];               // activation ring: two 256-k blocks
+    // activations: published every XB blocks, so XR blocks are held in
+    // registers (requested XR blocks ahead) and XSL in the LDS ring; the loop
+    // is unrolled over U blocks (a multiple of both rings)
+    static_assert(XB == 1 || (XB == 2 && P == 2), "barrier every block, or every second with a 2-deep ring");
+    constexpr int XR = XB == 1 ? P : 4;
+    constexpr int XSL = XB == 1 ? 2 : 4;
+    constexpr int U = XB == 1 ? P : 4;
+    __shared__ uint4 xs[XSL][MT * 32];             // activation ring: XSL 256-k blocks
     extern __shared__ uint32_t tab[];              // scale and zero-point tables
     __shared__ int s_last;
 
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     const int kend = min(K, (int)(((int64_t)(blockIdx.y + 1) * nkb) / S) << 8);
     const int nch = (kend - k0) >> 3;             // valid chunks of the slice
     const int nb = (kend - k0 + 255) >> 8;        // blocks of this slice
-    const int nbp = (nb + P - 1) / P * P;         // blocks streamed, padded to the ring
+    const int nbp = (nb + U - 1) / U * U;         // blocks streamed, padded to the unrolled step
     const int mrows = M < MT ? M : MT;
     const int gs = KS >> lg;                      // groups per slice
 
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
         for (int u = 0; u < XPT; ++u) {
             const bool ok = j * 32 + xcc[u] < xlim[u];
             if (XC % NT == 0 || xhas[u])
-                xs[j & 1][xdst[u]] =
+                xs[j % XSL][xdst[u]] =
                     ql::permute_x8_sel(v[u], ok ? ql::kPermLo : ql::kPermZero, ok ? ql::kPermHi : ql::kPermZero);
         }
     };
@@ -503,16 +512,20 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
     //    stream has a static count)
     tb.load(0, 0);
     uint4 ring[P][R][2];
-    uint4 xr[P][XPT];
+    uint4 xr[XR][XPT];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        x_load(p, xr[p]);
-        load_block(p < nb ? p : nb - 1, ring[p]);
+    for (int p = 0; p < (XR > P ? XR : P); ++p) {
+        if (p < XR)
+            x_load(p, xr[p]);
+        if (p < P)
+            load_block(p < nb ? p : nb - 1, ring[p]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // 2. tables and block 0's activations -> LDS
+    // 2. tables and the first XB blocks' activations -> LDS
     tb.store_all(tab);
-    x_store(0, xr[0]);
+#pragma unroll
+    for (int j = 0; j < XB; ++j)
+        x_store(j, xr[j]);
     __syncthreads();
 
     // 3. stream the slice
@@ -552,10 +565,11 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
         spar[t] = tb.parity(trow[t]);
     }
 
-    for (int b0 = 0; b0 < nbp; b0 += P) {
+    for (int b0 = 0; b0 < nbp; b0 += U) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
+        for (int p = 0; p < U; ++p) {
             const int b = b0 + p;
+            const int pw = p % P;                 // this block's weight ring slot
             // activation fragments of block b: requested first, so the LDS
             // latency passes while the weights are dequantised
             // (with four row tiles only tile 0's; the others are read as
@@ -566,11 +580,11 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
             for (int j = 0; j < 8; ++j)
 #pragma unroll
                 for (int i = 0; i < MTA; ++i)
-                    af[j][i] = xs[b & 1][arow[j & 3] + (j >> 2) * hoff + 512 * i];
+                    af[j][i] = xs[b % XSL][arow[j & 3] + (j >> 2) * hoff + 512 * i];
             auto frag = [&](int j, int i) -> uint4 {
                 if (i < MTA)
                     return af[j][i];
-                return xs[b & 1][arow[j & 3] + (j >> 2) * hoff + 512 * i];
+                return xs[b % XSL][arow[j & 3] + (j >> 2) * hoff + 512 * i];
             };
             // groups of the two pieces (padding blocks clamp to the last group;
             // their activations are zero)
@@ -588,7 +602,7 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
                 s16[t][0] = srow[spar[t] + ga];
                 s16[t][1] = srow[spar[t] + gb];
                 const ql::zb_t za = ql::make_zb(za_), zc = ql::make_zb(zb_);
-                const uint4 w0 = ring[p][t][0], w1 = ring[p][t][1];
+                const uint4 w0 = ring[pw][t][0], w1 = ring[pw][t][1];
                 const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -620,8 +634,8 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
             // the whole ring.
             const int nxt = b + P < nb ? b + P : nb - 1;
             __builtin_amdgcn_sched_barrier(0);
-            x_load(b + P, xr[p]);
-            load_block(nxt, ring[p]);
+            x_load(b + XR, xr[p % XR]);
+            load_block(nxt, ring[pw]);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (POST) {
 #pragma unroll
@@ -651,9 +665,18 @@ __global__ __launch_bounds__(64 * T, (decode_wg_per_cu<MT, R, T>())) void w4a16_
                                 mfma16x16x32(__builtin_bit_cast(h8_t, frag(j, i)), bw[8 * t + j], acc[t][i][j % NJ]);
             }
             // block b + 1's activations -> the other slot; the barrier
-            // publishes them and frees this slot for block b + 2
-            x_store(b + 1, xr[(p + 1) % P]);
-            __syncthreads();
+            // publishes them and frees this slot for block b + 2.  Every
+            // second block instead (XB = 2): blocks b + 1 and b + 2 into
+            // slots last read by blocks b - 3 and b - 2, both before the
+            // previous barrier.
+            if constexpr (XB == 1) {
+                x_store(b + 1, xr[(p + 1) % XR]);
+                __syncthreads();
+            } else if (p & 1) {
+                x_store(b + 1, xr[(p + 1) % XR]);
+                x_store(b + 2, xr[(p + 2) % XR]);
+                __syncthreads();
+            }
         }
     }
     f4_t res[R][MTI];
@@ -1979,7 +2002,7 @@ int launch_status(const char* who)
     return QL_OK;
 }
 
-template <int MT, int R, int P, bool POST, int T>
+template <int MT, int R, int P, bool POST, int T, int XB = 1>
 void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, const uint16_t* sc,
                      const uint32_t* qz, uint16_t* y, void* ws, int m, int n, int k, int lg, hipStream_t st)
 {
@@ -1987,7 +2010,7 @@ void launch_decode_t(const DecodePlan& p, const uint16_t* x, const uint32_t* qw,
     float* part = p.slices > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
                                                           (p.pair ? kCounterBytes : p.part_offset))
                                : nullptr;
-    hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST, T>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes,
+    hipLaunchKernelGGL((w4a16_decode_kernel<MT, R, P, POST, T, XB>), dim3(p.nblk, p.slices), dim3(64 * T), p.lds_bytes,
                        st, x, qw, sc, qz, y, part, cnt, m, n, k, lg, p.ks, p.pair ? 1 : 0);
 }
 
@@ -2029,16 +2052,17 @@ bool launch_decode(const DecodePlan& p, const uint16_t* x, const uint32_t* qw, c
         return false;
     }
 
-#define QL_DECODE_CASE(MT_, R_, P_, T_)                                                          \
-    if (p.mt == MT_ && p.r == R_ && p.p == P_ && p.t == T_) {                                    \
-        if (p.post)                                                                              \
-            launch_decode_t<MT_, R_, P_, true, T_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
-        else                                                                                     \
-            launch_decode_t<MT_, R_, P_, false, T_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
-        return true;                                                                             \
+#define QL_DECODE_CASE(MT_, R_, P_, T_, XB_)                                                          \
+    if (p.mt == MT_ && p.r == R_ && p.p == P_ && p.t == T_) {                                         \
+        if (p.post)                                                                                   \
+            launch_decode_t<MT_, R_, P_, true, T_, XB_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);    \
+        else                                                                                          \
+            launch_decode_t<MT_, R_, P_, false, T_, XB_>(p, x, qw, sc, qz, y, ws, m, n, k, lg, st);   \
+        return true;                                                                                  \
     }
-    QL_DECODE_CASE(16, 1, 2, 4) QL_DECODE_CASE(32, 1, 2, 4) QL_DECODE_CASE(16, 1, 2, 6) QL_DECODE_CASE(32, 1, 2, 6)
-    QL_DECODE_CASE(64, 1, 2, 8)
+    // six-wave 16-row launches (one workgroup per CU) publish activations every second block
+    QL_DECODE_CASE(16, 1, 2, 4, 1) QL_DECODE_CASE(32, 1, 2, 4, 1) QL_DECODE_CASE(16, 1, 2, 6, 2)
+    QL_DECODE_CASE(32, 1, 2, 6, 1) QL_DECODE_CASE(64, 1, 2, 8, 1)
 #undef QL_DECODE_CASE
     return false;
 }
