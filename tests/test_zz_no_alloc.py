@@ -99,6 +99,41 @@ def test_noalloc_repeated_calls_are_identical(lib):
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
 
 
+def test_noalloc_graph_replays_match_eager(lib):
+    """The allocation-free entry point captured in a HIP graph (the callers it
+    is for): a counter-protocol split launch and a two-slice exchange launch,
+    replayed four times with eager work and synchronisation in between; every
+    replay equals the eager result bit for bit.  The first call on the device
+    (which clears the scratch with a small kernel) runs eagerly, before the
+    capture."""
+    cases = [(16, 4096, 11008, 128), (8, 17001, 1024, 64)]
+    data = []
+    for i, (m, n, k, group) in enumerate(cases):
+        _, _, d = _problem(m, n, k, group, seed=40 + i)
+        y = torch.empty((m, n), dtype=torch.float16, device="cuda:0")
+        data.append(((m, n, k, group), d, y))
+    eager = []
+    for (m, n, k, group), d, y in data:
+        assert _noalloc(lib, d, m, n, k, group, y) == 0, lib.ql_last_error().decode()
+        torch.cuda.synchronize()
+        eager.append(y.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (m, n, k, group), d, y in data:
+            assert _noalloc(lib, d, m, n, k, group, y) == 0
+    for rep in range(4):
+        for _, _, y in data:
+            y.fill_(float("nan"))
+        (m, n, k, group), d, _ = data[0]
+        other = torch.empty((m, n), dtype=torch.float16, device="cuda:0")
+        assert _noalloc(lib, d, m, n, k, group, other) == 0        # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, (_, _, y) in zip(eager, data):
+            assert torch.equal(e.view(torch.int16), y.view(torch.int16)), rep
+
+
 def test_noalloc_validation(lib):
     E_NULL, E_GROUP, E_SHAPE = -1, -3, -2
     x = torch.zeros((4, 256), dtype=torch.float16, device="cuda:0")
