@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -64,10 +65,15 @@ def w4a16_bytes(m, n, k, g):
 
 
 def kernel_source_hash():
+    """Hash of the W4A16 kernel sources with comments and blank space removed,
+    so that a traffic record stays valid across edits that change no code."""
     h = hashlib.sha256()
     for f in ("w4a16.hip", "dequant.hpp", "lds_dma.hpp"):
-        with open(os.path.join(ROOT, "weight_quantized_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "weight_quantized_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)     # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                   # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -116,8 +116,11 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(const uint32_t* __re
 // two-slot LDS ring: the threads load block b + P's activations together with
 // the weights of block b + P, reorder each 16-byte chunk for the dequantiser
 // in registers and write it to LDS one block ahead of its use; one barrier per
-// block publishes it.  Every load is an ordinary (compiler-tracked) load, so
-// each wait names exactly the block it needs.
+// block publishes it.  With XB = 2 (the six-wave 16-row launches, one
+// workgroup per CU) the activations are requested four blocks ahead and
+// published two at a time into a four-slot ring, one barrier per two blocks.
+// Every load is an ordinary (compiler-tracked) load, so each wait names
+// exactly the block it needs.
 //
 // In a block, lane l (row l%16, quarter q = l/16) loads two 16-byte pieces of
 // its row: words [4q, 4q+4) and [16+4q, 16+4q+4), so 4 lanes read 64
