@@ -99,7 +99,8 @@ def parse():
                     help="output channels per launch for the oracle sample (0 = all of them)")
     ap.add_argument("--profile-launch", metavar="SHAPE,M",
                     help="run one workload for counter collection and exit: gate_up,M or down,M or q_proj,1 "
-                         "(decode, cold weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM); "
+                         "(decode, cold weights), qkv,512 (prefill GEMM), w8a8,2048 (QRMSNorm + int8 GEMM), "
+                         "fp8,2048 (FP8 QRMSNorm + FP8 GEMM), kv,4096 (KV cache INT8 quantise + dequantise); "
                          "then a plain "
                          f"{COPY_BYTES >> 20} MiB device copy of known size that calibrates the byte counters")
     ap.add_argument("--profile-reps", type=int, default=12)
@@ -632,6 +633,32 @@ def profile_launch(args):
             ql.w8a8_quant_rmsnorm(xd, gd, 1e-6, xq=xq, x_scale=xsc)
             ql.w8a8_gemm(xq, xsc, wqd, wsd, out=yy)
         desc = {"shape": f"w8a8_m{m}", "ops_per_launch": 2 * m * wq.shape[0] * xh.shape[1]}
+    elif shape == "fp8":
+        xh, gamma, wf = workloads.smoothquant_inputs(m=m)
+        s_, gs, wsm = ql.smooth(xh, gamma, wf)
+        wq8, wsc8 = ql.fp8_quant_weight(wsm)
+        del wf, wsm
+        xd, gd = torch.from_numpy(xh).to(dev), torch.from_numpy(gs).to(dev)
+        wqd, wsd = torch.from_numpy(wq8).to(dev), torch.from_numpy(wsc8).to(dev)
+        xq = torch.empty(xh.shape, dtype=torch.uint8, device=dev)
+        xsc = torch.empty((m,), dtype=torch.float32, device=dev)
+        yy = torch.empty((m, wq8.shape[0]), dtype=torch.float16, device=dev)
+        for _ in range(args.profile_reps):
+            ql.fp8_quant_rmsnorm(xd, gd, 1e-6, xq=xq, x_scale=xsc)
+            ql.fp8_gemm(xq, xsc, wqd, wsd, out=yy)
+        desc = {"shape": f"fp8_m{m}", "flops_per_launch": 2 * m * wq8.shape[0] * xh.shape[1]}
+    elif shape == "kv":
+        # KV cache INT8 codec on m tokens of one LLaMA-7B layer's K and V (2 x m x 32 heads x 128)
+        rng = np.random.default_rng(5)
+        kv = torch.from_numpy((rng.standard_normal((2 * m * 32, 128)) *
+                               rng.uniform(0.1, 10, (2 * m * 32, 1))).astype(np.float16)).to(dev)
+        kq = torch.empty(kv.shape, dtype=torch.int8, device=dev)
+        ksc = torch.empty((kv.shape[0],), dtype=torch.float32, device=dev)
+        kout = torch.empty_like(kv)
+        for _ in range(args.profile_reps):
+            ql.kv_quant_int8(kv, 128, q=kq, scale=ksc)
+            ql.kv_dequant_int8(kq, ksc, 128, out=kout)
+        desc = {"shape": f"kv_m{m}", "values": kv.numel(), "bytes_per_launch": kv.numel() * 3 + kv.shape[0] * 4}
     else:
         raise SystemExit(f"unknown workload {shape!r}")
     torch.cuda.synchronize()
