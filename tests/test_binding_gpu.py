@@ -98,10 +98,11 @@ def test_w8a8_rejects_mismatched_operands(ql):
 def test_decode_on_two_streams(ql):
     """Split-K decode launches on two streams without explicit workspaces:
     each stream gets its own cached workspace, so concurrent launches do not
-    share arrival counters or partial sums."""
+    share arrival counters, partial sums or exchange slots (one launch split
+    eight ways through counters, one split in two that exchanges)."""
     group = 128
     rng = np.random.default_rng(11)
-    cases = [(8, 4096, 11008), (16, 4096, 11008)]
+    cases = [(8, 4096, 11008), (5, 17001, 1024)]
     data = []
     for m, n, k in cases:
         w = workloads.weight(rng, n, k)
