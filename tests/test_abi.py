@@ -258,3 +258,35 @@ def test_binding_shape_helpers():
         ql._w4_operands(qw, sc, qz, n, 500, g)
     with pytest.raises(ValueError):
         ql._shape(torch.zeros(3), (4,), "t")
+
+
+def test_header_is_c99_and_links_from_c(tmp_path):
+    """include/qlinear.h is a plain C header: a C99 program (-pedantic,
+    warnings as errors) includes it, links against libqlinear and calls the
+    entry points that touch no device (version, status strings, workspace
+    sizes, argument checks)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include "qlinear.h"
+int main(void)
+{
+    size_t ws = ql_w4a16_workspace_bytes(8, 22016, 4096, 128);
+    int rc = ql_w4a16_gemm(0, 0, 0, 0, 0, 1, 64, 128, 128, 0, 0, 0);
+    printf("%d|%s|%d|%d\n", ql_version(), ql_status_string(QL_ERR_NULL), (int)(ws >= QL_W4A16_WS_ZERO_BYTES), rc);
+    return 0;
+}
+""")
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(ql.lib_path)
+    subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lqlinear", "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.strip().split("|")
+    assert int(out[0]) == LIB.ql_version()
+    assert out[1] == LIB.ql_status_string(CODES["QL_ERR_NULL"]).decode()
+    assert out[2] == "1" and int(out[3]) == CODES["QL_ERR_NULL"]
