@@ -392,6 +392,25 @@ def test_decode_two_slice_exchange(ql, m, n, k, group):
     assert full <= TOL and sampled <= TOL, (full, sampled)
 
 
+def test_decode_two_slice_exchange_many_calls(ql):
+    """Forty back-to-back calls of each two-slice launch (the streamed kernel
+    at gate/up M = 4 and 8, the GEMV kernel at 13B down M = 1) on one
+    workspace, without synchronisation between them: arrival orders vary from
+    call to call, the outputs must not, and the slots end at zero."""
+    group = 128
+    for m, n, k in [(4, 22016, 4096), (8, 22016, 4096), (1, 5120, 13824)]:
+        rng = np.random.default_rng(m + n)
+        w = workloads.weight(rng, n, k)
+        _, d = pack_dev(ql, w, group)
+        x = dev(workloads.activations(rng, m, k))
+        ws = torch.zeros(ql.w4a16_workspace_bytes(m, n, k, group), dtype=torch.uint8, device="cuda:0")
+        outs = [ql.w4a16_gemm(x, *d, group, workspace=ws, path=1) for _ in range(40)]
+        torch.cuda.synchronize()
+        for y in outs[1:]:
+            assert torch.equal(y.view(torch.int16), outs[0].view(torch.int16)), (m, n, k)
+        assert not ws[:ql.W4A16_WS_ZERO_BYTES].cpu().numpy().any(), (m, n, k)
+
+
 def test_decode_two_slice_exchange_nan_and_zero(ql):
     """Partials that are NaN in one slice only, or zero in both (an all-zero
     activation row): the exchange still tells the first arrival from the
