@@ -363,15 +363,17 @@ def test_decode_six_wave_workgroups(ql, m, k, group, n):
     assert full <= TOL and sampled <= TOL
 
 
-# K split in exactly two slices (4 to 8 rows, 16K-32K channels): the slices
-# meet in exchange slots (one atomic swap per pair of output rows) instead of
-# arrival counters and partial tiles.  Ragged m (odd rows leave half a pair),
+# K split in exactly two slices (2 to 8 rows, 13K-32K channels; two and three
+# rows take the streamed kernel instead of the GEMV on such wide layers): the
+# slices meet in exchange slots (one atomic swap per pair of output rows)
+# instead of arrival counters and partial tiles.  Ragged m (odd rows leave half a pair),
 # ragged n (the last 16-channel tile and column block partly outside), ragged
 # k (the second slice one block shorter) and every group size; the launch is
 # repeated on one workspace (the slots must be back at zero for the second
 # call's first arrivals) and all channels are compared with the oracle.
 @pytest.mark.parametrize("m,n,k,group", [(4, 16400, 512, 128), (5, 17001, 1024, 64), (7, 20000, 768, 32),
-                                         (8, 32700, 1280, 128), (6, 22016, 4096, 128), (8, 22016, 4096, 64)])
+                                         (8, 32700, 1280, 128), (6, 22016, 4096, 128), (8, 22016, 4096, 64),
+                                         (2, 17001, 1024, 64), (3, 22016, 4096, 128), (3, 13824, 5120, 32)])
 def test_decode_two_slice_exchange(ql, m, n, k, group):
     rng = np.random.default_rng(m * 7 + n + k)
     w = workloads.weight(rng, n, k)

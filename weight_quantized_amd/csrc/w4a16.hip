@@ -1902,10 +1902,20 @@ DecodePlan decode_plan_gemv(int64_t m, int64_t n, int64_t k, int group)
     return p;
 }
 
-// Kernel choice by m (measured on the MLP decode shapes).
+// Kernel choice by m (measured on the MLP decode shapes).  Two or three rows
+// on a wide layer, where the streamed kernel splits K in two exchanging
+// slices, take the streamed kernel (gate/up M = 2 / 3 13.7 / 14.1 us against
+// 13.8 / 14.8 for the GEMV, 13B up 12.9 / 13.0 against 13.9 / 14.7); on
+// narrow layers, where it would split K eight ways, the GEMV stays (down
+// M = 2 / 3 10.3 / 10.9 against 11.2, q_proj 5.2 / 5.4 against 8.4).
 DecodePlan decode_plan_auto(int64_t m, int64_t n, int64_t k, int group)
 {
     if (m <= kGemvMaxRows) {
+        if (m >= 2) {
+            DecodePlan s = decode_plan(m, n, k, group);
+            if (s.pair)
+                return s;
+        }
         DecodePlan p = decode_plan_gemv(m, n, k, group);
         if (ql::lds_fits(p.lds_bytes))
             return p;
